@@ -1,0 +1,30 @@
+"""CPU oracle for the redundant-expert MoE dispatch path -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the package's ``smoke()`` check and the benchmark's CPU
+baseline leg may import this package.  It shares no code with the HIP
+library or its binding and imports neither.
+
+Parity pins (what checks the oracle against something other than itself)
+are listed per function in the tests:
+
+* ``maxvio``, ``plan``, ``layout``: hand-worked golden examples
+  (tests/golden), invariants on random and adversarial routings, brute-force
+  optimal replica counts on tiny inputs, and special cases that reduce to a
+  stable argsort / bincount (one rank) or to plain expert parallelism
+  (balanced routing).
+* ``permute``, ``group_gemm``, ``combine``, ``replica_grad_fold``: a
+  simulation of every rank that must reproduce the dense MoE definition and
+  its per-expert weight gradients exactly on small-integer inputs.
+* ``bf16``: torch's CPU cast on sampled bit patterns.
+
+Parity unpinned: any specific plan versus the original library's planner
+(the pages print none).
+"""
+from .moe_ref import (  # noqa: F401
+    STATUS_BAD_EXPERT_ID, STATUS_SLOT_OVERFLOW, HEADER_WORDS, Plan, Replica, maxvio, histogram,
+    plan, plan_words, layout, layout_loops, permute, group_gemm, group_gemm_rows, wgrad_entries,
+    combine, replica_grad_fold, prefetch,
+)
+from .bf16 import (  # noqa: F401
+    bf16_bits_to_f32, bf16_bits_to_f64, f32_to_bf16_bits, f64_to_bf16_bits,
+)

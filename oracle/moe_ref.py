@@ -1,0 +1,526 @@
+"""CPU oracle for the redundant-expert MoE dispatch path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package's smoke entry
+and the benchmark's CPU-baseline leg may import this module.  The product
+path (the HIP library and its Python binding) never imports, calls or
+falls back to it, and this module imports nothing from the product path.
+
+Plain, slow, obviously correct numpy code: integer work is exact, floating
+point is done in float64 from exactly widened inputs and rounded once to
+the output type.  Every function names the passage it follows.  Pages
+cited (title, then the section or paragraph):
+
+  [ainovat]  "Moonshot AI Open-Sources MoonEP: A Perfectly Balanced Expert
+             Parallelism Library for MoE Training" (ainovat.com)
+  [repocard] "MoonEP" repository card (findrepo.work): "Why it is worth
+             attention", "Strengths", "Considerations"
+  [blog]     "MoonEP" walkthrough (moses-y.github.io): "The Problem",
+             "What This Does", "How It Is Wired", "How To Use It",
+             "Real-World Use"
+  [wtf]      "wtf is moonep?" (gitwtfhub.com)
+
+The pages fix the skew metric, the exact S*K-per-rank invariant, the
+mechanism (a few redundant experts planned online from the router outputs,
+weights prefetched, replica gradients returned home), and the contract (one
+contiguous [E+B, H, H'] weight tensor per projection addressed by row index,
+plus a planner-produced cu_seqlens).  They do not print the planning
+algorithm, its tie-breaks, the token-to-replica assignment, the row order
+in the buffer, the activation or the numerics.  Where they are silent this
+module takes the plainest reading that meets what they do fix; each such
+reading is marked READING.
+
+Notation: R ranks, S tokens per rank, K routed experts per token, E experts,
+E_loc = E / R home experts per rank, B replica slots per rank, SK = S*K.
+A token copy is (p, s, k); its copy id is (p*S + s)*K + k.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, f32_to_bf16_bits, bf16_bits_to_f32
+
+STATUS_BAD_EXPERT_ID = 1
+STATUS_SLOT_OVERFLOW = 2
+HEADER_WORDS = 8
+
+
+# --------------------------------------------------------------------------------------------
+# Skew metric
+# --------------------------------------------------------------------------------------------
+
+def maxvio(T, R: int, S: int, K: int, E: int) -> float:
+    """max_e T_e / T_bar - 1, with T_bar the per-expert count under perfect balance.
+
+    [ainovat] paragraph defining maxvio.  READING: "tokens" are token-expert
+    copies, so perfect balance puts T_bar = R*S*K / E copies on every expert.
+    """
+    T = np.asarray(T, dtype=np.float64)
+    t_bar = R * S * K / E
+    return float(T.max() / t_bar - 1.0)
+
+
+# --------------------------------------------------------------------------------------------
+# Planner
+# --------------------------------------------------------------------------------------------
+
+def histogram(topk_idx: np.ndarray, E: int):
+    """C[p, e] = number of copies (p, s, k) routed to expert e.
+
+    The per-expert token count T_e of [ainovat] (skew-metric paragraph) is
+    the column sum of C.  READING: an id outside [0, E) is not counted and
+    raises STATUS_BAD_EXPERT_ID; a repeated id within one token counts once
+    per copy.
+    """
+    R = topk_idx.shape[0]
+    flat = topk_idx.reshape(R, -1).astype(np.int64)
+    valid = (flat >= 0) & (flat < E)
+    C = np.zeros((R, E), dtype=np.int64)
+    for p in range(R):
+        C[p] = np.bincount(flat[p][valid[p]], minlength=E)
+    status = 0 if bool(valid.all()) else STATUS_BAD_EXPERT_ID
+    return C, status
+
+
+@dataclass
+class Replica:
+    expert: int     # expert e being duplicated
+    rank: int       # receiving rank q (never home(e))
+    start: int      # first position, in e's copy order, that this replica takes
+    count: int      # number of copies it takes
+    slot: int = -1  # slot j on rank q (weight row E + j); -1 if dropped for lack of slots
+
+
+@dataclass
+class Plan:
+    R: int
+    S: int
+    K: int
+    E: int
+    B: int
+    status: int
+    counts: np.ndarray          # C [R, E]
+    T: np.ndarray               # [E]
+    keep: np.ndarray            # copies of e that stay on its home rank, [E]
+    replicas: list              # Replica, in emission order
+    n_donors: int
+    n_receivers: int
+    n_pieces: int
+    max_needed: int             # most replicas any one rank was asked to host
+    rep_first: np.ndarray = field(default=None)
+    rep_n: np.ndarray = field(default=None)
+
+    @property
+    def E_loc(self):
+        return self.E // self.R
+
+    @property
+    def SK(self):
+        return self.S * self.K
+
+    def home(self, e):
+        return e // self.E_loc
+
+    def slot_table(self):
+        """(slot_expert, slot_start, slot_count), each [R, B]; empty slots are (-1, 0, 0)."""
+        se = np.full((self.R, self.B), -1, np.int64)
+        ss = np.zeros((self.R, self.B), np.int64)
+        sc = np.zeros((self.R, self.B), np.int64)
+        for m in self.replicas:
+            if m.slot >= 0:
+                se[m.rank, m.slot] = m.expert
+                ss[m.rank, m.slot] = m.start
+                sc[m.rank, m.slot] = m.count
+        return se, ss, sc
+
+    def rows_per_rank(self):
+        """n[q, rho]: copies that rank q processes with weight row rho, rho in [0, E+B)."""
+        R, E, B = self.R, self.E, self.B
+        n = np.zeros((R, E + B), np.int64)
+        for e in range(E):
+            n[self.home(e), e] = self.keep[e]
+        _, _, sc = self.slot_table()
+        n[:, E:] = sc
+        return n
+
+    def cu_seqlens(self):
+        """cu[q] = [0, n[q,0], n[q,0]+n[q,1], ...], E+B+1 entries per rank."""
+        n = self.rows_per_rank()
+        cu = np.zeros((self.R, self.E + self.B + 1), np.int64)
+        cu[:, 1:] = np.cumsum(n, axis=1)
+        return cu
+
+    def to_blob(self) -> np.ndarray:
+        """int32 words: header, T, keep, rep_first, rep_n, replica list, slot tables.
+
+        header = [status, n_replicas, max_needed, n_donors, n_receivers,
+        n_pieces, 0, 0]; the replica list holds E+R entries of each of
+        (expert, rank, slot, start, count), unused entries (-1, -1, -1, 0, 0);
+        the slot tables are [R*B] each of (expert, start, count).
+        """
+        R, E, B = self.R, self.E, self.B
+        L = E + R
+        re = np.full(L, -1, np.int64); rq = np.full(L, -1, np.int64)
+        rs = np.full(L, -1, np.int64); rst = np.zeros(L, np.int64); rc = np.zeros(L, np.int64)
+        for i, m in enumerate(self.replicas):
+            re[i], rq[i], rs[i], rst[i], rc[i] = m.expert, m.rank, m.slot, m.start, m.count
+        se, ss, sc = self.slot_table()
+        hdr = np.array([self.status, len(self.replicas), self.max_needed, self.n_donors,
+                        self.n_receivers, self.n_pieces, 0, 0], np.int64)
+        blob = np.concatenate([hdr, self.T, self.keep, self.rep_first, self.rep_n,
+                               re, rq, rs, rst, rc, se.ravel(), ss.ravel(), sc.ravel()])
+        assert blob.size == plan_words(R, E, B)
+        return blob.astype(np.int32)
+
+
+def plan_words(R: int, E: int, B: int) -> int:
+    return HEADER_WORDS + 4 * E + 5 * (E + R) + 3 * R * B
+
+
+def plan(topk_idx: np.ndarray, E: int, B: int) -> Plan:
+    """Online redundant-expert plan from the current router outputs.
+
+    [ainovat] invariant and mechanism paragraphs: every rank must receive
+    exactly S*K copies, whatever the skew, by duplicating a few experts onto
+    other ranks, planned from this step's routing alone.  [repocard]
+    "Strengths" asks for few replicas chosen near-optimally with negligible
+    cost.  READING (the pages give no algorithm): a greedy donor-to-receiver
+    placement that minimises the replica count in the common cases:
+
+      1. histogram, T_e = sum_p C[p, e]
+      2. home(e) = e // E_loc; rank load L_r = sum of T_e over its home
+         experts; excess d_r = L_r - S*K
+      3. donors (d_r > 0) ordered by (d_r desc, r asc); receivers (d_r < 0)
+         by (-d_r desc, r asc)
+      4. each donor, taking its home experts by (T_e desc, e asc), cuts one
+         piece of a = min(T_e, remaining excess) from each until its excess
+         is gone; keep_e = T_e - a
+      5. the piece list and the receiver list are walked together; each step
+         emits a replica of the current piece's expert on the current
+         receiver carrying x = min(piece left, deficit left) copies, taken
+         from e's copy order starting at keep_e + (part of the piece already
+         emitted); whichever runs out advances
+      6. replicas on a receiver take slots 0, 1, ... in emission order; a
+         replica beyond slot B-1 is dropped and STATUS_SLOT_OVERFLOW is set
+    """
+    R, S, K = topk_idx.shape
+    SK = S * K
+    E_loc = E // R
+    C, status = histogram(topk_idx, E)
+    T = C.sum(axis=0)
+
+    # step 2: home loads and excess
+    L = np.array([int(T[r * E_loc:(r + 1) * E_loc].sum()) for r in range(R)], np.int64)
+    d = L - SK
+
+    # step 3: order donors and receivers
+    donors = sorted([r for r in range(R) if d[r] > 0], key=lambda r: (-int(d[r]), r))
+    receivers = sorted([r for r in range(R) if d[r] < 0], key=lambda r: (int(d[r]), r))
+
+    # step 4: pieces
+    keep = T.copy()
+    pieces = []          # (expert, amount)
+    for r in donors:
+        experts = sorted(range(r * E_loc, (r + 1) * E_loc), key=lambda e: (-int(T[e]), e))
+        rem = int(d[r])
+        for e in experts:
+            if rem == 0:
+                break
+            a = min(int(T[e]), rem)
+            if a == 0:
+                continue
+            pieces.append((e, a))
+            keep[e] -= a
+            rem -= a
+
+    # step 5: walk pieces against receivers
+    replicas = []
+    i = j = 0
+    used_piece = used_recv = 0
+    while i < len(pieces) and j < len(receivers):
+        e, a = pieces[i]
+        q = receivers[j]
+        need = -int(d[q])
+        x = min(a - used_piece, need - used_recv)
+        replicas.append(Replica(expert=e, rank=q, start=int(keep[e]) + used_piece, count=x))
+        used_piece += x
+        used_recv += x
+        if used_piece == a:
+            i += 1
+            used_piece = 0
+        if used_recv == need:
+            j += 1
+            used_recv = 0
+
+    # step 6: slots
+    hosted = [0] * R
+    for m in replicas:
+        m.slot = hosted[m.rank] if hosted[m.rank] < B else -1
+        hosted[m.rank] += 1
+    max_needed = max(hosted) if R else 0
+    if max_needed > B:
+        status |= STATUS_SLOT_OVERFLOW
+
+    rep_first = np.zeros(E, np.int64)
+    rep_n = np.zeros(E, np.int64)
+    for idx, m in enumerate(replicas):
+        if rep_n[m.expert] == 0:
+            rep_first[m.expert] = idx
+        rep_n[m.expert] += 1
+
+    return Plan(R=R, S=S, K=K, E=E, B=B, status=status, counts=C, T=T, keep=keep,
+                replicas=replicas, n_donors=len(donors), n_receivers=len(receivers),
+                n_pieces=len(pieces), max_needed=max_needed, rep_first=rep_first, rep_n=rep_n)
+
+
+# --------------------------------------------------------------------------------------------
+# Dispatch layout
+# --------------------------------------------------------------------------------------------
+
+def layout(topk_idx: np.ndarray, pl: Plan, rank: int):
+    """cu_seqlens of ``rank``, the global destination of every copy, and ``rank``'s receive map.
+
+    [ainovat] contract paragraph: dispatch returns cu_seqlens over the E+B
+    weight rows and those counts select the active rows.  [blog] "What This
+    Does": tokens land directly in their final expert-grouped positions.
+    READING:
+      * rank q's buffer holds S*K rows grouped by weight row rho = 0..E+B-1
+        in ascending rho (home experts at their global id, slot j at E+j);
+        cu_seqlens has E+B+1 entries with a leading 0;
+      * inside expert e, copies are taken in copy-id order; the first keep_e
+        stay home, replica m takes positions [start_m, start_m + count_m);
+        each segment keeps that order;
+      * dest_pos[c] = q*S*K + row position on q, or -1 when the copy has no
+        destination (bad id, or its replica was dropped);
+      * src_flat[i] = copy id landing at row i of ``rank``, or -1 if none.
+    A stable sort by expert id groups the copies of each expert in copy-id
+    order (library sort used as one step).
+    """
+    R, S, K = topk_idx.shape
+    SK = S * K
+    E, B = pl.E, pl.B
+    E_loc = E // R
+    flat = topk_idx.reshape(-1).astype(np.int64)
+    key = np.where((flat >= 0) & (flat < E), flat, E)
+    order = np.argsort(key, kind="stable")
+    first = np.concatenate([[0], np.cumsum(np.bincount(key, minlength=E + 1))])
+    cu = pl.cu_seqlens()
+    dest = np.full(R * SK, -1, np.int64)
+    for e in range(E):
+        group = order[first[e]:first[e + 1]]
+        h = e // E_loc
+        k_e = int(pl.keep[e])
+        dest[group[:k_e]] = h * SK + cu[h, e] + np.arange(k_e)
+        for m in pl.replicas:
+            if m.expert != e or m.slot < 0:
+                continue
+            dest[group[m.start:m.start + m.count]] = (m.rank * SK + cu[m.rank, E + m.slot]
+                                                      + np.arange(m.count))
+    src = np.full(SK, -1, np.int64)
+    mine = np.nonzero((dest >= rank * SK) & (dest < (rank + 1) * SK))[0]
+    src[dest[mine] - rank * SK] = mine
+    return cu[rank].astype(np.int32), dest.astype(np.int32), src.astype(np.int32)
+
+
+def layout_loops(topk_idx: np.ndarray, pl: Plan, rank: int):
+    """Per-copy pure-Python version of ``layout`` (same reading), for small inputs.
+
+    Walks the copies in copy-id order with one running counter per expert,
+    so it needs no sort; used to cross-check the vectorised version.
+    """
+    R, S, K = topk_idx.shape
+    SK = S * K
+    E = pl.E
+    E_loc = E // R
+    cu = pl.cu_seqlens()
+    seen = [0] * E
+    dest = [-1] * (R * SK)
+    flat = topk_idx.reshape(-1).tolist()
+    for c, e in enumerate(flat):
+        if not (0 <= e < E):
+            continue
+        g = seen[e]
+        seen[e] += 1
+        if g < pl.keep[e]:
+            h = e // E_loc
+            dest[c] = h * SK + int(cu[h, e]) + g
+            continue
+        for m in pl.replicas:
+            if m.expert == e and m.start <= g < m.start + m.count:
+                if m.slot >= 0:
+                    dest[c] = m.rank * SK + int(cu[m.rank, E + m.slot]) + (g - m.start)
+                break
+    src = [-1] * SK
+    for c, dpos in enumerate(dest):
+        if rank * SK <= dpos < (rank + 1) * SK:
+            src[dpos - rank * SK] = c
+    return (cu[rank].astype(np.int32), np.array(dest, np.int32), np.array(src, np.int32))
+
+
+# --------------------------------------------------------------------------------------------
+# Permute, grouped GEMM, combine, fold
+# --------------------------------------------------------------------------------------------
+
+def permute(x_all: np.ndarray, src_flat: np.ndarray, K: int, row_scale=None, dtype="bf16"):
+    """xp[i] = x_all[src_flat[i] // K]: a row gather into expert-grouped order.
+
+    [blog] "What This Does" and [repocard] "Strengths" (the permute is fused
+    into dispatch, no extra copy).  Without ``row_scale`` it is a bitwise
+    copy; rows with src_flat < 0 are zero.  With ``row_scale`` (indexed by
+    copy id) it is the backward of the weighted combine: READING, one IEEE
+    fp32 multiply w * x then one rounding to the row type.
+    ``x_all`` is uint16 bf16 bits or float32.
+    """
+    SK = src_flat.shape[0]
+    out = np.zeros((SK, x_all.shape[1]), dtype=x_all.dtype)
+    for i in range(SK):
+        c = int(src_flat[i])
+        if c < 0:
+            continue
+        row = x_all[c // K]
+        if row_scale is None:
+            out[i] = row
+        else:
+            w = np.float32(row_scale[c])
+            if dtype == "bf16":
+                out[i] = f32_to_bf16_bits(w * bf16_bits_to_f32(row))
+            else:
+                out[i] = w * row.astype(np.float32)
+    return out
+
+
+def _widen(a, dtype):
+    return bf16_bits_to_f64(a) if dtype == "bf16" else np.asarray(a, np.float64)
+
+
+def _narrow(a64, dtype):
+    return f64_to_bf16_bits(a64) if dtype == "bf16" else a64.astype(np.float32)
+
+
+def group_gemm(op: str, a, b, cu, dtype="bf16", out=None):
+    """Grouped GEMM over one contiguous weight tensor addressed by row index.
+
+    [ainovat] contract and contiguity paragraphs: segment rho of the rows
+    (cu[rho] .. cu[rho+1]) is multiplied by weight row rho of a single
+    [E+B, H, H'] tensor; rows with an empty segment are not touched.
+    Float64 products from exactly widened inputs, rounded once.
+
+      "fwd":   out[seg] = a[seg] @ W[rho]          a [M, Kd], W [G, Kd, N] -> [M, N]
+      "dgrad": out[seg] = a[seg] @ W[rho]^T        a [M, N],  W [G, Kd, N] -> [M, Kd]
+      "wgrad": out[rho] += a[seg]^T @ b[seg]       a [M, Kd], b [M, N]     -> fp32 [G, Kd, N]
+
+    READING: output rows outside every segment keep the value of ``out``
+    (zeros if not given); wgrad accumulates into fp32 ``out``, one rounding
+    per call.
+    """
+    cu = np.asarray(cu, np.int64)
+    G = cu.shape[0] - 1
+    if op == "wgrad":
+        res = np.array(out, dtype=np.float32, copy=True)
+        for rho in range(G):
+            lo, hi = int(cu[rho]), int(cu[rho + 1])
+            if hi <= lo:
+                continue
+            acc = _widen(a[lo:hi], dtype).T @ _widen(b[lo:hi], dtype)
+            res[rho] = (res[rho].astype(np.float64) + acc).astype(np.float32)
+        return res
+    M = a.shape[0]
+    ncols = b.shape[2] if op == "fwd" else b.shape[1]
+    odt = np.uint16 if dtype == "bf16" else np.float32
+    res = np.zeros((M, ncols), odt) if out is None else np.array(out, dtype=odt, copy=True)
+    for rho in range(G):
+        lo, hi = int(cu[rho]), int(cu[rho + 1])
+        if hi <= lo:
+            continue
+        w = _widen(b[rho], dtype)
+        prod = _widen(a[lo:hi], dtype) @ (w if op == "fwd" else w.T)
+        res[lo:hi] = _narrow(prod, dtype)
+    return res
+
+
+def group_gemm_rows(op: str, a, b, cu, rows, dtype="bf16"):
+    """Selected output rows of ``group_gemm`` ("fwd"/"dgrad"), computed one row at a time.
+
+    For large shapes: each row needs only its own input row and its
+    segment's weight row.  Returns (segment of each row, output rows).
+    """
+    cu = np.asarray(cu, np.int64)
+    rows = np.asarray(rows, np.int64)
+    seg = np.searchsorted(cu, rows, side="right") - 1
+    outs = []
+    for r, rho in zip(rows, seg):
+        w = _widen(b[rho], dtype)
+        x = _widen(a[r:r + 1], dtype)
+        outs.append(_narrow(x @ (w if op == "fwd" else w.T), dtype)[0])
+    return seg, np.stack(outs) if outs else np.zeros((0,), np.float32)
+
+
+def wgrad_entries(a, b, cu, rho: int, ii, jj, dtype="bf16", init=None):
+    """Selected entries (ii, jj) of a[seg]^T @ b[seg] (+ init) for one weight row rho, fp32."""
+    lo, hi = int(cu[rho]), int(cu[rho + 1])
+    A = _widen(a[lo:hi][:, ii], dtype)          # [n, len]
+    Bm = _widen(b[lo:hi][:, jj], dtype)
+    acc = (A * Bm).sum(axis=0)
+    if init is not None:
+        acc = acc + np.asarray(init, np.float64)
+    return acc.astype(np.float32)
+
+
+def combine(y_all, dest_pos, topk_w, rank: int, S: int, K: int, dtype="bf16", tokens=None):
+    """out[s] = sum over k of w[rank, s, k] * y_all[dest_pos of copy (rank, s, k)].
+
+    [blog] "What This Does" / "Real-World Use": combine gathers each token's
+    expert outputs back from their expert-grouped positions.  READING: pull
+    form, weights are the router's top-K weights, sum in ascending k
+    (float64 here), one rounding; copies with dest_pos < 0 add nothing.
+    ``tokens`` restricts the computation to those token indices.
+    """
+    toks = np.arange(S) if tokens is None else np.asarray(tokens, np.int64)
+    width = y_all.shape[1]
+    acc = np.zeros((toks.size, width), np.float64)
+    w = np.asarray(topk_w, np.float32).reshape(-1)
+    dp = np.asarray(dest_pos).reshape(-1)
+    for t, s in enumerate(toks):
+        for k in range(K):
+            c = (rank * S + int(s)) * K + k
+            d = int(dp[c])
+            if d < 0:
+                continue
+            acc[t] += np.float64(w[c]) * _widen(y_all[d], dtype)
+    return _narrow(acc, dtype)
+
+
+def replica_grad_fold(dw: np.ndarray, pl: Plan, rank: int) -> np.ndarray:
+    """Fold replica weight-gradient rows of ``rank`` into their home expert rows.
+
+    [ainovat] mechanism paragraph and [blog] "Real-World Use": in backward,
+    the gradients of duplicated experts go back to their home experts.
+    READING (one GPU holds the whole [E+B, ...] tensor): for each used slot j
+    of ``rank`` in ascending j, dw[e] = fp32(dw[e] + dw[E+j]) and then
+    dw[E+j] = 0, so the slot starts the next step clean.
+    """
+    out = np.array(dw, dtype=np.float32, copy=True)
+    se, _, _ = pl.slot_table()
+    for j in range(pl.B):
+        e = int(se[rank, j])
+        if e < 0:
+            continue
+        out[e] = out[e] + out[pl.E + j]
+        out[pl.E + j] = 0.0
+    return out
+
+
+def prefetch(w: np.ndarray, pl: Plan, rank: int) -> np.ndarray:
+    """Slot rows of ``rank`` receive a copy of the expert they duplicate.
+
+    [ainovat] mechanism paragraph: duplicated experts' weights are fetched
+    before expert compute.  Empty slots are left as they were.
+    """
+    out = np.array(w, copy=True)
+    se, _, _ = pl.slot_table()
+    for j in range(pl.B):
+        e = int(se[rank, j])
+        if e >= 0:
+            out[pl.E + j] = out[e]
+    return out

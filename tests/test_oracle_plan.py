@@ -1,0 +1,290 @@
+"""Oracle planner and layout vs what the pages and the mathematics fix.
+
+* Invariants (ainovat article, invariant and mechanism paragraphs): every
+  rank receives exactly S*K copies; every copy lands on a replica of its own
+  expert; a replica never sits on its expert's home rank; at most one
+  replica per (expert, rank); at most B replicas per rank or the overflow
+  status is set; cu_seqlens sums to S*K.
+* Quality: brute-force minimum replica count on tiny inputs (max-flow
+  feasibility of every replica support, smallest first) and the proven
+  bounds max(P, U) <= opt <= greedy <= P + U - 1, with greedy == opt when
+  min(P, U) <= 1 (P = pieces, U = receivers).
+* Special cases: one rank (layout = stable argsort, cu = prefix of
+  bincount), exactly balanced routing (no replica, plain expert
+  parallelism), B = 0 with imbalance (overflow), adversarial counts.
+"""
+from itertools import combinations
+
+import numpy as np
+import pytest
+from scipy.sparse import csr_matrix
+from scipy.sparse.csgraph import maximum_flow
+
+import oracle
+import synth
+
+
+def check_plan_invariants(idx, pl, B):
+    R, S, K = idx.shape
+    E = pl.E
+    SK = S * K
+    E_loc = E // R
+    valid = (idx >= 0) & (idx < E)
+    assert pl.counts.sum() == valid.sum()
+    assert (pl.T == pl.counts.sum(axis=0)).all()
+    # replica bookkeeping
+    per_expert = np.zeros(E, np.int64)
+    pairs = set()
+    hosted = np.zeros(R, np.int64)
+    for m in pl.replicas:
+        assert m.rank != m.expert // E_loc
+        assert (m.expert, m.rank) not in pairs
+        pairs.add((m.expert, m.rank))
+        assert m.count > 0
+        assert m.start >= pl.keep[m.expert]
+        per_expert[m.expert] += m.count
+        if m.slot >= 0:
+            assert 0 <= m.slot < B
+            hosted[m.rank] += 1
+    assert (hosted <= B).all()
+    # replicas of one expert tile [keep_e, T_e) contiguously, in order
+    for e in range(E):
+        ms = [m for m in pl.replicas if m.expert == e]
+        pos = int(pl.keep[e])
+        for m in ms:
+            assert m.start == pos
+            pos += m.count
+        if pl.status == 0:
+            assert pos == pl.T[e]
+    if pl.status == 0:
+        assert (pl.keep + per_expert == pl.T).all()
+    else:
+        assert pl.max_needed > B or pl.status & oracle.STATUS_BAD_EXPERT_ID
+    cu_all = pl.cu_seqlens()
+    assert (cu_all[:, -1] <= SK).all()
+    if pl.status == 0:
+        assert (cu_all[:, -1] == SK).all(), "every rank receives exactly S*K copies"
+    return cu_all
+
+
+def check_layout(idx, pl, rank_list=None):
+    R, S, K = idx.shape
+    SK = S * K
+    E, B = pl.E, pl.B
+    E_loc = E // R
+    flat = idx.reshape(-1)
+    se, _, _ = pl.slot_table()
+    cu_all = pl.cu_seqlens()
+    dest_ref = None
+    for r in (range(R) if rank_list is None else rank_list):
+        cu, dest, src = oracle.layout(idx, pl, r)
+        if dest_ref is None:
+            dest_ref = dest
+            good = dest >= 0
+            assert len(np.unique(dest[good])) == good.sum(), "dest_pos injective"
+            if pl.status == 0:
+                assert good.all()
+        assert (dest == dest_ref).all()
+        assert (cu == cu_all[r]).all()
+        # src_flat is exactly the inverse of dest_pos restricted to rank r
+        mine = np.nonzero((dest >= r * SK) & (dest < (r + 1) * SK))[0]
+        assert sorted(src[src >= 0].tolist()) == sorted(mine.tolist())
+        for i in range(SK):
+            c = src[i]
+            if c < 0:
+                assert i >= cu[-1]
+                continue
+            assert dest[c] == r * SK + i
+            # the weight row holding position i serves the copy's own expert
+            rho = int(np.searchsorted(cu, i, side="right") - 1)
+            e = int(flat[c])
+            if rho < E:
+                assert rho == e and e // E_loc == r
+            else:
+                assert se[r, rho - E] == e
+    return dest_ref
+
+
+def random_routing(rng, R, S, K, E, skew):
+    """Routing with a random skew: experts drawn from a random Dirichlet popularity."""
+    pop = rng.dirichlet(np.full(E, skew))
+    idx = np.empty((R, S, K), np.int32)
+    for p in range(R):
+        for s in range(S):
+            idx[p, s] = rng.choice(E, size=K, replace=False, p=pop)
+    return idx
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_invariants_random(seed):
+    rng = np.random.default_rng(seed)
+    R = int(rng.integers(1, 7))
+    E_loc = int(rng.integers(1, 5))
+    E = R * E_loc
+    K = int(rng.integers(1, min(E, 4) + 1))
+    S = int(rng.integers(1, 24))
+    B = int(rng.integers(0, 5))
+    idx = random_routing(rng, R, S, K, E, skew=float(rng.choice([0.1, 0.5, 2.0, 50.0])))
+    pl = oracle.plan(idx, E, B)
+    check_plan_invariants(idx, pl, B)
+    check_layout(idx, pl)
+    for r in range(R):
+        a = oracle.layout(idx, pl, r)
+        b = oracle.layout_loops(idx, pl, r)
+        for x, y in zip(a, b):
+            assert (x == y).all()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_invariants_zipf_generator(seed):
+    dims = synth.Dims(R=8, S=64, K=4, E=32, B=4, H=8, Hp=8)
+    idx, w = synth.routing(dims, zipf_s=0.4 * seed, base_seed=seed)
+    assert idx.shape == (8, 64, 4)
+    assert np.allclose(w.sum(-1), 1.0, atol=1e-6)
+    pl = oracle.plan(idx, dims.E, dims.B)
+    check_plan_invariants(idx, pl, dims.B)
+    check_layout(idx, pl, rank_list=[0, 3, 7])
+
+
+def test_bad_ids_are_safe():
+    rng = np.random.default_rng(7)
+    idx = rng.integers(0, 16, size=(4, 32, 2)).astype(np.int32)
+    idx[1, 3, 0] = -1
+    idx[2, 5, 1] = 16
+    pl = oracle.plan(idx, 16, 3)
+    assert pl.status & oracle.STATUS_BAD_EXPERT_ID
+    dest = check_layout(idx, pl)
+    assert dest[(1 * 32 + 3) * 2 + 0] == -1 and dest[(2 * 32 + 5) * 2 + 1] == -1
+
+
+# ------------------------------------------------------------------------------------------
+# brute force
+# ------------------------------------------------------------------------------------------
+
+def _feasible(T, R, E, SK, support):
+    """Integral max-flow: source -> expert e [T_e] -> home(e) or a replica rank -> sink [SK]."""
+    E_loc = E // R
+    n = E + R + 2
+    src, snk = 0, n - 1
+    rows, cols, caps = [], [], []
+    for e in range(E):
+        rows.append(src); cols.append(1 + e); caps.append(int(T[e]))
+        rows.append(1 + e); cols.append(1 + E + e // E_loc); caps.append(int(T[e]))
+    for (e, q) in support:
+        rows.append(1 + e); cols.append(1 + E + q); caps.append(int(T[e]))
+    for q in range(R):
+        rows.append(1 + E + q); cols.append(snk); caps.append(SK)
+    g = csr_matrix((np.array(caps, np.int32), (rows, cols)), shape=(n, n))
+    return maximum_flow(g, src, snk).flow_value == int(np.sum(T))
+
+
+def brute_force_opt(T, R, E, SK, B=None):
+    E_loc = E // R
+    pairs = [(e, q) for e in range(E) for q in range(R) if q != e // E_loc and T[e] > 0]
+    for size in range(len(pairs) + 1):
+        for sub in combinations(pairs, size):
+            if B is not None:
+                per = np.bincount([q for _, q in sub], minlength=R)
+                if (per > B).any():
+                    continue
+            if _feasible(T, R, E, SK, sub):
+                return size
+    return None
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_bruteforce_bounds(seed):
+    rng = np.random.default_rng(1000 + seed)
+    R = int(rng.integers(2, 4))
+    E_loc = int(rng.integers(1, 3))
+    E = R * E_loc
+    K = int(rng.integers(1, min(E, 2) + 1))
+    S = int(rng.integers(1, 8 // K + 1))
+    idx = random_routing(rng, R, S, K, E, skew=float(rng.choice([0.2, 1.0, 5.0])))
+    SK = S * K
+    pl = oracle.plan(idx, E, B=64)
+    assert pl.status == 0
+    P, U = pl.n_pieces, pl.n_receivers
+    greedy = len(pl.replicas)
+    opt = brute_force_opt(pl.T, R, E, SK)
+    assert opt is not None
+    assert max(P, U) <= opt <= greedy
+    if P + U > 0:
+        assert greedy <= P + U - 1
+    if min(P, U) <= 1:
+        assert greedy == opt
+    assert greedy <= 2 * max(opt, 1) - 1 or greedy == 0
+    # with the slot cap, the greedy plan is never better than the capped optimum
+    for B in (1, 2):
+        plB = oracle.plan(idx, E, B)
+        optB = brute_force_opt(pl.T, R, E, SK, B=B)
+        if plB.status == 0:
+            assert optB is not None and optB <= len(plB.replicas)
+
+
+# ------------------------------------------------------------------------------------------
+# special cases
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(5))
+def test_single_rank_is_stable_sort(seed):
+    rng = np.random.default_rng(seed)
+    E, S, K = 12, 50, 3
+    idx = random_routing(rng, 1, S, K, E, skew=1.0)
+    pl = oracle.plan(idx, E, B=2)
+    assert pl.replicas == [] and pl.status == 0
+    cu, dest, src = oracle.layout(idx, pl, 0)
+    flat = idx.reshape(-1)
+    assert (src == np.argsort(flat, kind="stable")).all()
+    assert (cu[:E + 1] == np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))])).all()
+    assert (cu[E:] == S * K).all()
+
+
+def test_balanced_routing_is_plain_ep():
+    dims = synth.Dims(R=8, S=64, K=6, E=64, B=4, H=8, Hp=8)
+    idx, _ = synth.balanced_routing(dims)
+    pl = oracle.plan(idx, dims.E, dims.B)
+    assert pl.status == 0 and pl.replicas == [] and pl.n_donors == 0
+    assert oracle.maxvio(pl.T, dims.R, dims.S, dims.K, dims.E) == 0.0
+    for r in range(dims.R):
+        cu, dest, src = oracle.layout(idx, pl, r)
+        n = np.diff(cu)
+        assert (n[r * dims.E_loc:(r + 1) * dims.E_loc] == dims.SK // dims.E_loc).all()
+        assert n.sum() == dims.SK and (n[dims.E:] == 0).all()
+
+
+def test_zero_slots_with_imbalance_overflows():
+    idx = np.zeros((2, 4, 1), np.int32)          # everything on expert 0 (rank 0)
+    pl = oracle.plan(idx, 2, B=0)
+    assert pl.status == oracle.STATUS_SLOT_OVERFLOW
+    assert all(m.slot == -1 for m in pl.replicas)
+    cu, dest, src = oracle.layout(idx, pl, 1)
+    assert cu[-1] == 0 and (src == -1).all()
+
+
+def test_adversarial_many_donors_one_receiver():
+    """R-1 donors with excess 1 each and one receiver with deficit R-1 needs R-1 slots."""
+    R, K = 6, 1
+    S = R - 1                      # rank 0's deficit S equals R-1 donors' excess 1
+    E = R
+    flat = []
+    for r in range(1, R):          # ranks 1..R-1 own S+1 copies each of their one expert
+        flat += [r] * (S + 1)
+    assert len(flat) == R * S
+    idx = np.array(flat, np.int32).reshape(R, S, K)
+    pl = oracle.plan(idx, E, B=R - 1)
+    assert pl.status == 0 and pl.max_needed == R - 1
+    pl2 = oracle.plan(idx, E, B=2)
+    assert pl2.status == oracle.STATUS_SLOT_OVERFLOW
+    check_plan_invariants(idx, pl2, 2)
+    check_layout(idx, pl2)
+
+
+def test_plan_blob_size_and_header():
+    rng = np.random.default_rng(3)
+    idx = random_routing(rng, 4, 16, 2, 16, skew=0.5)
+    pl = oracle.plan(idx, 16, 3)
+    blob = pl.to_blob()
+    assert blob.dtype == np.int32 and blob.size == oracle.plan_words(4, 16, 3)
+    assert blob[0] == pl.status and blob[1] == len(pl.replicas)
+    assert (blob[8:8 + 16] == pl.T).all()
