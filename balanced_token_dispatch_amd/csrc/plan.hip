@@ -1,0 +1,368 @@
+// moe_plan: per-expert histogram of all ranks' router outputs and the
+// greedy redundant-expert placement that gives every rank exactly S*K copies.
+//
+// Pages: ainovat.com "Moonshot AI Open-Sources MoonEP", paragraphs on the
+// skew metric (per-expert token counts), the exact S*K-per-rank invariant and
+// the mechanism (a few redundant experts planned online from the current
+// router outputs); findrepo.work "MoonEP" card, "Strengths" (near-optimal
+// choice, negligible planning cost).  The placement rule itself is this
+// library's reading; it is spelled out at moe_plan in moe.h.
+//
+// Three launches, no atomics on global memory, so the result is
+// deterministic:
+//   k_plan_hist    grid (chunks, R): LDS histogram of 4096 ids -> partials
+//   k_plan_reduce  grid R: sum the partials of one rank -> counts[p][*]
+//   k_plan_solve   one 1024-thread workgroup: loads, donor/receiver order,
+//                  pieces, the piece/receiver walk and slots, all as
+//                  counting ranks and block scans in LDS (no serial loop
+//                  over ranks or experts).
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kPlanChunk = 4096;
+constexpr int kHistThreads = 256;
+constexpr int kSolveThreads = 1024;
+constexpr int kMaxE = 1024;
+constexpr int kMaxR = 512;
+constexpr int kMaxL = kMaxE + kMaxR;
+
+// ids of rank p, chunk c -> partial[(p*nchunk + c)*(E+1) + e]; bin E counts bad ids.
+__global__ __launch_bounds__(kHistThreads) void k_plan_hist(const int32_t *__restrict__ topk,
+                                                            int32_t *__restrict__ partial, int SK,
+                                                            int E, int nchunk) {
+  __shared__ int hist[kMaxE + 1];
+  const int c = blockIdx.x, p = blockIdx.y;
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int lo = c * kPlanChunk;
+  const int hi = min(SK, lo + kPlanChunk);
+  const int32_t *ids = topk + (size_t)p * SK;
+  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
+    const int e = ids[i];
+    const int key = (e >= 0 && e < E) ? e : E;
+    atomicAdd(&hist[key], 1);
+  }
+  __syncthreads();
+  int32_t *dst = partial + (size_t)(p * nchunk + c) * (E + 1);
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) dst[e] = hist[e];
+}
+
+// counts[p][e] = sum over chunks; bad[p] = number of bad ids of rank p.
+__global__ __launch_bounds__(kHistThreads) void k_plan_reduce(const int32_t *__restrict__ partial,
+                                                              int32_t *__restrict__ counts,
+                                                              int32_t *__restrict__ bad, int E,
+                                                              int nchunk) {
+  const int p = blockIdx.x;
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+    int s = 0;
+    for (int c = 0; c < nchunk; ++c) s += partial[(size_t)(p * nchunk + c) * (E + 1) + e];
+    if (e < E)
+      counts[(size_t)p * E + e] = s;
+    else
+      bad[p] = s;
+  }
+}
+
+// Exclusive scan of one int per thread across a 1024-thread workgroup.
+__device__ int block_scan_excl(int v, int *tmp /* >= 17 ints */, int *total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    const int nw = blockDim.x >> 6;
+    int w = lane < nw ? tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(w, off, 64);
+      if (lane >= off) w += y;
+    }
+    if (lane < nw) tmp[lane] = w;  // inclusive per-wave totals
+  }
+  __syncthreads();
+  const int base = wid ? tmp[wid - 1] : 0;
+  *total = tmp[(blockDim.x >> 6) - 1];
+  __syncthreads();
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__restrict__ counts,
+                                                              const int32_t *__restrict__ bad,
+                                                              int32_t *__restrict__ plan,
+                                                              uint32_t *__restrict__ dev_status,
+                                                              int R, int S, int K, int E, int B) {
+  // per expert
+  __shared__ int sT[kMaxE], sKeep[kMaxE], sSrank[kMaxE], sPre[kMaxE], sA[kMaxE];
+  __shared__ int sRepFirst[kMaxE], sRepN[kMaxE];
+  // per piece (indexed by global piece order, at most E pieces)
+  __shared__ int sPieceE[kMaxE], sPieceP[kMaxE], sPieceJlo[kMaxE], sPieceCnt[kMaxE];
+  // per rank
+  __shared__ int sD[kMaxR], sDonorPos[kMaxR], sDonorAt[kMaxR], sRecvAt[kMaxR], sNP[kMaxR];
+  __shared__ int sDonorBase[kMaxR], sPieceBase0[kMaxR], sRecvBase[kMaxR + 1];
+  __shared__ int sRecvFirst[kMaxR], sRecvN[kMaxR];
+  // replica list
+  __shared__ int sRexp[kMaxL], sRrank[kMaxL], sRstart[kMaxL], sRcount[kMaxL], sRslot[kMaxL];
+  __shared__ int sTmp[32];
+  __shared__ int sNDonor, sNRecv, sMaxNeeded, sOverflow, sBad;
+
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int E_loc = E / R;
+  const int SK = S * K;
+  const PlanLayout L(E, R, B);
+
+  if (tid == 0) {
+    sNDonor = 0;
+    sNRecv = 0;
+    sMaxNeeded = 0;
+    sOverflow = 0;
+    sBad = 0;
+  }
+  __syncthreads();
+  // T_e and the bad-id flag
+  for (int e = tid; e < E; e += nt) {
+    int s = 0;
+    for (int p = 0; p < R; ++p) s += counts[(size_t)p * E + e];
+    sT[e] = s;
+    sRepFirst[e] = 0;
+    sRepN[e] = 0;
+  }
+  for (int p = tid; p < R; p += nt) {
+    if (bad[p] != 0) atomicOr(&sBad, 1);
+    sNP[p] = 0;
+    sRecvFirst[p] = -1;
+    sRecvN[p] = 0;
+  }
+  __syncthreads();
+  // home loads and excess
+  for (int r = tid; r < R; r += nt) {
+    int l = 0;
+    for (int e = r * E_loc; e < (r + 1) * E_loc; ++e) l += sT[e];
+    sD[r] = l - SK;
+  }
+  __syncthreads();
+  // donor order (d desc, r asc) and receiver order (-d desc, r asc) by counting ranks
+  for (int r = tid; r < R; r += nt) {
+    const int d = sD[r];
+    sDonorPos[r] = -1;
+    if (d > 0) {
+      int pos = 0;
+      for (int q = 0; q < R; ++q) {
+        const int dq = sD[q];
+        pos += (dq > d) || (dq == d && q < r);
+      }
+      sDonorPos[r] = pos;
+      sDonorAt[pos] = r;
+      atomicAdd(&sNDonor, 1);
+    } else if (d < 0) {
+      int pos = 0;
+      for (int q = 0; q < R; ++q) {
+        const int dq = sD[q];
+        pos += (dq < d) || (dq == d && q < r);
+      }
+      sRecvAt[pos] = r;
+      atomicAdd(&sNRecv, 1);
+    }
+  }
+  __syncthreads();
+  const int nDonor = sNDonor, nRecv = sNRecv;
+  // pieces: rank of e inside its home group by (T desc, e asc), the load before
+  // it in that order, and the piece it gives up
+  for (int e = tid; e < E; e += nt) {
+    const int r = e / E_loc, t = sT[e];
+    int srank = 0, pre = 0;
+    for (int f = r * E_loc; f < (r + 1) * E_loc; ++f) {
+      const int tf = sT[f];
+      if (tf > t || (tf == t && f < e)) {
+        ++srank;
+        pre += tf;
+      }
+    }
+    const int d = sD[r];
+    int a = 0;
+    if (d > 0) a = min(t, max(0, d - pre));
+    sSrank[e] = srank;
+    sPre[e] = pre;
+    sA[e] = a;
+    sKeep[e] = t - a;
+    if (a > 0) atomicAdd(&sNP[r], 1);
+  }
+  __syncthreads();
+  // scans in donor order: piece index base and position in the donated-copy stream
+  {
+    int total;
+    const int i = tid;
+    const int r = (i < nDonor) ? sDonorAt[i] : 0;
+    const int np = (i < nDonor) ? sNP[r] : 0;
+    const int dd = (i < nDonor) ? sD[r] : 0;
+    const int pbase = block_scan_excl(np, sTmp, &total);
+    const int dbase = block_scan_excl(dd, sTmp, &total);
+    if (i < nDonor) {
+      sPieceBase0[i] = pbase;
+      sDonorBase[i] = dbase;
+    }
+    // receiver stream positions
+    const int q = (i < nRecv) ? sRecvAt[i] : 0;
+    const int need = (i < nRecv) ? -sD[q] : 0;
+    const int qbase = block_scan_excl(need, sTmp, &total);
+    if (i < nRecv) sRecvBase[i] = qbase;
+    if (i == 0) sRecvBase[nRecv] = total;
+  }
+  __syncthreads();
+  const int qTot = sRecvBase[nRecv];
+  // each piece: its place in the piece order, stream start, receivers it spans
+  for (int e = tid; e < E; e += nt) {
+    const int a = sA[e];
+    if (a == 0) continue;
+    const int r = e / E_loc;
+    const int dpos = sDonorPos[r];
+    const int pidx = sPieceBase0[dpos] + sSrank[e];
+    const int P = sDonorBase[dpos] + sPre[e];
+    const int hiPos = min(P + a, qTot);
+    int jlo = 0, cnt = 0;
+    if (P < hiPos) {
+      // last receiver j with start <= x: binary search over sRecvBase[0..nRecv)
+      int lo = 0, hi = nRecv;  // invariant: answer in [lo, hi)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sRecvBase[mid] <= P) lo = mid; else hi = mid;
+      }
+      jlo = lo;
+      lo = jlo;
+      hi = nRecv;
+      const int last = hiPos - 1;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sRecvBase[mid] <= last) lo = mid; else hi = mid;
+      }
+      cnt = lo - jlo + 1;
+    }
+    sPieceE[pidx] = e;
+    sPieceP[pidx] = P;
+    sPieceJlo[pidx] = jlo;
+    sPieceCnt[pidx] = cnt;
+  }
+  __syncthreads();
+  int nPieces;
+  {
+    int total;
+    // number of pieces = sum over donors
+    const int v = (tid < nDonor) ? sNP[sDonorAt[tid]] : 0;
+    block_scan_excl(v, sTmp, &total);
+    nPieces = total;
+  }
+  int nRep;
+  {
+    int total;
+    const int v = (tid < nPieces) ? sPieceCnt[tid] : 0;
+    const int base = block_scan_excl(v, sTmp, &total);
+    nRep = total;
+    if (tid < nPieces) {
+      const int e = sPieceE[tid], P = sPieceP[tid], a = sA[e], jlo = sPieceJlo[tid];
+      const int cnt = sPieceCnt[tid];
+      if (cnt > 0) {
+        sRepFirst[e] = base;
+        sRepN[e] = cnt;
+      }
+      for (int u = 0; u < cnt; ++u) {
+        const int j = jlo + u;
+        const int lo = max(P, sRecvBase[j]);
+        const int hi = min(P + a, sRecvBase[j + 1]);
+        const int m = base + u;
+        sRexp[m] = e;
+        sRrank[m] = sRecvAt[j];
+        sRstart[m] = sKeep[e] + (lo - P);
+        sRcount[m] = hi - lo;
+      }
+    }
+  }
+  __syncthreads();
+  // slots: a receiver's replicas are consecutive in emission order
+  for (int m = tid; m < nRep; m += nt) {
+    const int q = sRrank[m];
+    int s = m;
+    while (s > 0 && sRrank[s - 1] == q) --s;
+    const int slot = m - s;
+    sRslot[m] = slot < B ? slot : -1;
+    if (slot >= B) atomicOr(&sOverflow, 1);
+    if (m == s) sRecvFirst[q] = m;
+    if (m == nRep - 1 || sRrank[m + 1] != q) {
+      sRecvN[q] = slot + 1;
+      atomicMax(&sMaxNeeded, slot + 1);
+    }
+  }
+  __syncthreads();
+  // write the blob, each word exactly once
+  const int status = (sBad ? MOE_DEV_BAD_EXPERT_ID : 0) | (sOverflow ? MOE_DEV_SLOT_OVERFLOW : 0);
+  if (tid == 0) {
+    plan[0] = status;
+    plan[1] = nRep;
+    plan[2] = sMaxNeeded;
+    plan[3] = nDonor;
+    plan[4] = nRecv;
+    plan[5] = nPieces;
+    plan[6] = 0;
+    plan[7] = 0;
+    if (dev_status) *dev_status = (uint32_t)status;
+  }
+  for (int e = tid; e < E; e += nt) {
+    plan[L.off_T + e] = sT[e];
+    plan[L.off_keep + e] = sKeep[e];
+    plan[L.off_rep_first + e] = sRepFirst[e];
+    plan[L.off_rep_n + e] = sRepN[e];
+  }
+  for (int m = tid; m < E + R; m += nt) {
+    const bool used = m < nRep;
+    plan[L.off_rexp + m] = used ? sRexp[m] : -1;
+    plan[L.off_rrank + m] = used ? sRrank[m] : -1;
+    plan[L.off_rslot + m] = used ? sRslot[m] : -1;
+    plan[L.off_rstart + m] = used ? sRstart[m] : 0;
+    plan[L.off_rcount + m] = used ? sRcount[m] : 0;
+  }
+  for (int w = tid; w < R * B; w += nt) {
+    const int q = w / B, j = w % B;
+    const int f = sRecvFirst[q];
+    const bool used = f >= 0 && j < min(sRecvN[q], B);
+    plan[L.off_sexp + w] = used ? sRexp[f + j] : -1;
+    plan[L.off_sstart + w] = used ? sRstart[f + j] : 0;
+    plan[L.off_scount + w] = used ? sRcount[f + j] : 0;
+  }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_plan_words(const moe_dims *d) {
+  if (!dims_ok(d)) return 0;
+  return (size_t)PlanLayout(d->E, d->R, d->B).words;
+}
+
+extern "C" size_t moe_plan_workspace_bytes(const moe_dims *d) {
+  if (!dims_ok(d)) return 0;
+  const int nchunk = ceil_div((long long)d->S * d->K, kPlanChunk);
+  return (size_t)d->R * nchunk * (d->E + 1) * sizeof(int32_t) + (size_t)d->R * sizeof(int32_t);
+}
+
+extern "C" moe_status_t moe_plan(const moe_dims *d, const int32_t *topk_idx, int32_t *counts,
+                                 int32_t *plan, uint32_t *dev_status, void *ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  if (!dims_ok(d) || !topk_idx || !counts || !plan || !ws) return MOE_EINVAL;
+  if (ws_bytes < moe_plan_workspace_bytes(d)) return MOE_ENOSPACE;
+  const int SK = d->S * d->K;
+  const int nchunk = ceil_div(SK, kPlanChunk);
+  int32_t *partial = (int32_t *)ws;
+  int32_t *bad = partial + (size_t)d->R * nchunk * (d->E + 1);
+  hipLaunchKernelGGL(k_plan_hist, dim3(nchunk, d->R), dim3(kHistThreads), 0, stream, topk_idx,
+                     partial, SK, d->E, nchunk);
+  hipLaunchKernelGGL(k_plan_reduce, dim3(d->R), dim3(kHistThreads), 0, stream, partial, counts,
+                     bad, d->E, nchunk);
+  hipLaunchKernelGGL(k_plan_solve, dim3(1), dim3(kSolveThreads), 0, stream, counts, bad, plan,
+                     dev_status, d->R, d->S, d->K, d->E, d->B);
+  return launch_status();
+}

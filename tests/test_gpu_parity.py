@@ -1,0 +1,360 @@
+"""HIP path vs the CPU oracle, through the C ABI, at sizes the oracle finishes in seconds.
+
+Plan, layout, permute, fold and prefetch must match bit for bit; GEMM and combine match
+bit for bit on small-integer inputs (every fp32 partial sum exact) and within the stated
+tolerance on random inputs (normwise max relative error 2e-2 in bf16, 1e-5 in fp32).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_common import (GpuPlan, bits, check_close, check_plan_layout, from_bits, log, mod,
+                        poisoned)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mod()  # fails loudly if the library is missing
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# ------------------------------------------------------------------------------------------
+# plan + dispatch layout (bit-exact)
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["plan_g1_single_donor.json", "plan_g2_split_piece.json",
+                                  "plan_g3_ties_overflow.json", "plan_g4_bad_id.json"])
+def test_plan_layout_golden(name):
+    g = json.load(open(os.path.join(GOLDEN, name)))
+    idx = np.array(g["topk_idx"], np.int32)
+    Bs = [c["B"] for c in g["cases"]] if "cases" in g else [g["B"]]
+    for B in Bs:
+        gp = GpuPlan(g["R"], g["S"], g["K"], g["E"], B)
+        for r in range(g["R"]):
+            log(f"golden {name} B={B} rank={r}")
+            gp.run(_dev(idx), r)
+            check_plan_layout(gp, idx, r)
+
+
+def _random_routing(rng, R, S, K, E, skew):
+    pop = rng.dirichlet(np.full(E, skew))
+    out = np.empty((R, S, K), np.int32)
+    for p in range(R):
+        # K distinct experts per token via Gumbel top-K on log-popularity
+        g = np.log(pop)[None, :] + rng.gumbel(size=(S, E))
+        out[p] = np.argsort(-g, axis=1)[:, :K]
+    return out
+
+
+CASES = [
+    # R, S, K, E, B, skew
+    (1, 300, 3, 12, 2, 1.0),
+    (2, 5000, 2, 8, 2, 0.5),         # several chunks + ragged tail
+    (4, 128, 2, 16, 2, 0.3),
+    (8, 1000, 6, 64, 4, 5.0),
+    (8, 3000, 4, 64, 1, 0.2),        # likely slot overflow
+    (16, 257, 8, 128, 8, 0.5),
+    (32, 512, 8, 256, 8, 1.0),
+    (64, 130, 8, 384, 8, 0.3),
+    (5, 999, 3, 20, 0, 0.5),         # B = 0
+    (512, 16, 2, 1024, 4, 0.5),      # maximum R and E
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_plan_layout_random(case):
+    R, S, K, E, B, skew = case
+    rng = np.random.default_rng(R * 1000 + S)
+    idx = _random_routing(rng, R, S, K, E, skew)
+    gp = GpuPlan(R, S, K, E, B)
+    pl = oracle.plan(idx, E, B)
+    for r in sorted({0, R // 2, R - 1}):
+        log(f"random plan case={case} rank={r} status={pl.status} replicas={len(pl.replicas)}")
+        gp.run(_dev(idx), r)
+        check_plan_layout(gp, idx, r, pl)
+
+
+def test_plan_layout_bad_ids():
+    rng = np.random.default_rng(11)
+    R, S, K, E, B = 4, 700, 3, 16, 3
+    idx = _random_routing(rng, R, S, K, E, 0.5)
+    idx[0, 5, 1] = -7
+    idx[3, 699, 2] = E
+    idx[2, 100, 0] = 1 << 30
+    gp = GpuPlan(R, S, K, E, B)
+    for r in range(R):
+        gp.run(_dev(idx), r)
+        pl = check_plan_layout(gp, idx, r)
+        assert pl.status & oracle.STATUS_BAD_EXPERT_ID
+
+
+@pytest.mark.parametrize("wl", ["tiny_f32", "balanced_bf16"])
+def test_plan_layout_workloads(wl):
+    w = synth.WORKLOADS[wl]
+    d = w.dims
+    idx, _ = synth.routing(d, synth.zipf_for(w, w.maxvio_targets[0]), w.base_seed)
+    gp = GpuPlan(d.R, d.S, d.K, d.E, d.B)
+    pl = oracle.plan(idx, d.E, d.B)
+    assert pl.status == 0
+    for r in range(d.R):
+        gp.run(_dev(idx), r)
+        check_plan_layout(gp, idx, r, pl)
+
+
+def test_plan_layout_exactly_balanced():
+    d = synth.WORKLOADS["balanced_bf16"].dims
+    idx, _ = synth.balanced_routing(d)
+    gp = GpuPlan(d.R, d.S, d.K, d.E, d.B)
+    gp.run(_dev(idx), 0)
+    pl = check_plan_layout(gp, idx, 0)
+    assert pl.replicas == []
+
+
+# ------------------------------------------------------------------------------------------
+# permute, combine, fold, prefetch
+# ------------------------------------------------------------------------------------------
+
+def _plan_for(R, S, K, E, B, seed, skew=0.5):
+    rng = np.random.default_rng(seed)
+    idx = _random_routing(rng, R, S, K, E, skew)
+    return idx, oracle.plan(idx, E, B)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scaled", [False, True])
+def test_permute(dtype, scaled):
+    R, S, K, E, B, H = 4, 300, 3, 16, 1, 136
+    idx, pl = _plan_for(R, S, K, E, B, 3, skew=0.2)
+    m = mod()
+    d = m.dims(R, S, K, E, B)
+    rank = 0
+    _, _, src = oracle.layout(idx, pl, rank)
+    x = synth.host_normal(7, 1, (R * S, H))
+    x = synth.to_bf16_bits(x) if dtype == "bf16" else x
+    w = synth.routing(synth.Dims(R, S, K, E, B, H, H), 0.3, 9)[1].reshape(-1)
+    xd = from_bits(x)
+    xp = poisoned((S * K, H), xd.dtype)
+    m.moe_permute(d, xd, _dev(src), xp, row_scale=_dev(w) if scaled else None)
+    ref = oracle.permute(x, src, K, row_scale=w if scaled else None, dtype=dtype)
+    got = bits(xp)
+    assert (got.view(np.uint8) == ref.view(np.uint8)).all()
+    if pl.status:
+        assert (src == -1).any() and (got[src == -1] == 0).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("K", [2, 8, 17])
+def test_combine(dtype, K):
+    R, S, E, B, W = 3, 200, 24, 2, 264
+    idx, pl = _plan_for(R, S, K, E, B, 5 + K)
+    m = mod()
+    d = m.dims(R, S, K, E, B)
+    _, dest, _ = oracle.layout(idx, pl, 0)
+    dest = dest.copy()
+    dest[::37] = -1                          # copies without a destination add nothing
+    w = np.random.default_rng(1).random(R * S * K).astype(np.float32)
+    y = synth.host_normal(8, 2, (R * S * K, W))
+    y = synth.to_bf16_bits(y) if dtype == "bf16" else y
+    for rank in (0, R - 1):
+        out = poisoned((S, W), torch.bfloat16 if dtype == "bf16" else torch.float32)
+        m.moe_combine(d, rank, from_bits(y), _dev(dest), _dev(w), out)
+        ref = oracle.combine(y, dest, w, rank, S, K, dtype)
+        check_close(bits(out), ref, dtype, what=f"combine K={K} rank={rank}")
+
+
+def test_combine_integer_exact():
+    R, S, K, E, B, W = 4, 128, 8, 32, 4, 512
+    idx, pl = _plan_for(R, S, K, E, B, 21)
+    m = mod()
+    d = m.dims(R, S, K, E, B)
+    _, dest, _ = oracle.layout(idx, pl, 1)
+    w = np.random.default_rng(2).choice(np.array([0.25, 0.5, 1.0], np.float32), R * S * K)
+    y = synth.to_bf16_bits(synth.host_ternary(3, 3, (R * S * K, W)))
+    out = poisoned((S, W), torch.bfloat16)
+    m.moe_combine(d, 1, from_bits(y), _dev(dest), _dev(w), out)
+    assert (bits(out) == oracle.combine(y, dest, w, 1, S, K, "bf16")).all()
+
+
+def test_fold_and_prefetch():
+    R, S, K, E, B = 8, 400, 4, 32, 4
+    idx, pl = _plan_for(R, S, K, E, B, 31, skew=0.3)
+    m = mod()
+    d = m.dims(R, S, K, E, B)
+    plan_d = _dev(pl.to_blob())
+    row = 8 * 24
+    for rank in range(R):
+        dw = synth.host_normal(rank, 4, (E + B, row))
+        dwd = _dev(dw)
+        m.moe_replica_grad_fold(d, rank, plan_d, dwd)
+        assert (dwd.cpu().numpy() == oracle.replica_grad_fold(dw, pl, rank)).all()
+        wt = synth.to_bf16_bits(synth.host_normal(rank, 5, (E + B, 8, 24)))
+        wd = from_bits(wt)
+        m.moe_prefetch(d, rank, plan_d, wd)
+        assert (bits(wd) == oracle.prefetch(wt, pl, rank)).all()
+    assert any(m_.slot >= 0 for m_ in pl.replicas)
+
+
+# ------------------------------------------------------------------------------------------
+# grouped GEMM
+# ------------------------------------------------------------------------------------------
+
+def _segments(rng, G, M_total, empties=True):
+    cuts = np.sort(rng.integers(0, M_total + 1, size=G - 1))
+    cu = np.concatenate([[0], cuts, [M_total]]).astype(np.int32)
+    if empties and G > 3:
+        cu[2] = cu[1]  # an empty segment
+    return cu
+
+
+def _gemm_inputs(op, G, M, Kd, N, dtype, gen):
+    """a, b for the op; gen(tag, shape) -> float32 array."""
+    if op == "fwd":
+        a, b = gen(1, (M, Kd)), gen(2, (G, Kd, N))
+    elif op == "dgrad":
+        a, b = gen(1, (M, N)), gen(2, (G, Kd, N))
+    else:
+        a, b = gen(1, (M, Kd)), gen(2, (M, N))
+    if dtype == "bf16":
+        a, b = synth.to_bf16_bits(a), synth.to_bf16_bits(b)
+    return a, b
+
+
+def _run_gemm(op, a, b, cu, Kd, N, dtype, out_init=None):
+    m = mod()
+    opc = {"fwd": m.GEMM_FWD, "dgrad": m.GEMM_DGRAD, "wgrad": m.GEMM_WGRAD}[op]
+    ad, bd, cud = from_bits(a), from_bits(b), _dev(cu)
+    M = a.shape[0]
+    G = cu.size - 1
+    if op == "wgrad":
+        out = _dev(out_init.astype(np.float32))
+    else:
+        cols = N if op == "fwd" else Kd
+        out = poisoned((M, cols), torch.bfloat16 if dtype == "bf16" else torch.float32)
+    m.moe_group_gemm(opc, ad, bd, cud, out, Kd, N)
+    return bits(out) if op != "wgrad" else out.cpu().numpy()
+
+
+GEMM_SHAPES = [
+    # G, M, Kd, N
+    (5, 700, 64, 256),
+    (6, 1000, 136, 392),      # Kd, N not multiples of the tile
+    (18, 600, 256, 512),
+    (3, 2100, 520, 264),
+    (9, 257, 1408, 2048),
+]
+
+
+@pytest.mark.parametrize("op", ["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
+def test_group_gemm_integer_exact(op, shape):
+    G, M, Kd, N = shape
+    rng = np.random.default_rng(G * 7 + M)
+    cu = _segments(rng, G, M - 3)           # a few rows outside every segment
+    a, b = _gemm_inputs(op, G, M, Kd, N, "bf16",
+                        lambda t, s: synth.host_ternary(G + M, t, s))
+    init = synth.host_ternary(G, 9, (G, Kd, N)) if op == "wgrad" else None
+    log(f"gemm int op={op} shape={shape}")
+    got = _run_gemm(op, a, b, cu, Kd, N, "bf16", init)
+    ref = oracle.group_gemm(op, a, b, cu, "bf16", out=init)
+    if op == "wgrad":
+        assert (got == ref).all()
+    else:
+        rows = cu[-1]
+        assert (got[:rows] == ref[:rows]).all()
+        assert (got[rows:].view(np.uint16) == 0x7F7F).all(), "rows outside segments untouched"
+
+
+@pytest.mark.parametrize("op", ["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("shape", GEMM_SHAPES[:4])
+def test_group_gemm_random_bf16(op, shape):
+    G, M, Kd, N = shape
+    rng = np.random.default_rng(G * 11 + M)
+    cu = _segments(rng, G, M)
+    a, b = _gemm_inputs(op, G, M, Kd, N, "bf16",
+                        lambda t, s: synth.host_normal(G + M, t, s, 1.0 if t == 1 else 0.05))
+    init = synth.host_normal(G, 9, (G, Kd, N)) if op == "wgrad" else None
+    got = _run_gemm(op, a, b, cu, Kd, N, "bf16", init)
+    ref = oracle.group_gemm(op, a, b, cu, "bf16", out=init)
+    if op == "wgrad":
+        err = float(np.abs(got - ref).max() / np.abs(ref).max())
+        assert err <= 1e-4, err
+    else:
+        check_close(got, ref, "bf16", what=f"gemm {op} {shape}")
+
+
+@pytest.mark.parametrize("op", ["fwd", "dgrad", "wgrad"])
+def test_group_gemm_f32(op):
+    G, M, Kd, N = 18, 256, 256, 512
+    rng = np.random.default_rng(4)
+    cu = _segments(rng, G, M)
+    a, b = _gemm_inputs(op, G, M, Kd, N, "f32", lambda t, s: synth.host_normal(3, t, s))
+    init = np.zeros((G, Kd, N), np.float32) if op == "wgrad" else None
+    got = _run_gemm(op, a, b, cu, Kd, N, "f32", init)
+    ref = oracle.group_gemm(op, a, b, cu, "f32", out=init)
+    check_close(got, ref, "f32", what=f"f32 gemm {op}")
+
+
+def test_group_gemm_deterministic():
+    G, M, Kd, N = 9, 1500, 512, 768
+    rng = np.random.default_rng(8)
+    cu = _segments(rng, G, M)
+    a, b = _gemm_inputs("fwd", G, M, Kd, N, "bf16", lambda t, s: synth.host_normal(1, t, s))
+    r1 = _run_gemm("fwd", a, b, cu, Kd, N, "bf16")
+    r2 = _run_gemm("fwd", a, b, cu, Kd, N, "bf16")
+    assert (r1 == r2).all()
+
+
+# ------------------------------------------------------------------------------------------
+# tiny fp32 workload end to end (plan, permute, one projection, combine; rank 0)
+# ------------------------------------------------------------------------------------------
+
+def test_tiny_f32_workload_end_to_end():
+    w = synth.WORKLOADS["tiny_f32"]
+    d = w.dims
+    idx, topk_w = synth.routing(d, w.zipf_s, w.base_seed)
+    x = synth.host_normal(w.base_seed, 10, (d.R * d.S, d.H))
+    W_up = synth.host_normal(w.base_seed, 11, (d.G, d.H, d.Hp), 0.02)
+    Y_stage = synth.host_normal(w.base_seed, 12, (d.R * d.SK, d.Hp))
+    rank = 0
+    pl = oracle.plan(idx, d.E, d.B)
+    assert pl.status == 0
+    W_up = oracle.prefetch(W_up, pl, rank)   # the oracle's view of the slot rows
+    m = mod()
+    gp = GpuPlan(d.R, d.S, d.K, d.E, d.B)
+    gp.run(_dev(idx), rank)
+    check_plan_layout(gp, idx, rank, pl)
+    Wd = _dev(synth.host_normal(w.base_seed, 11, (d.G, d.H, d.Hp), 0.02))
+    m.moe_prefetch(gp.d, rank, gp.plan, Wd)
+    assert (Wd.cpu().numpy() == W_up).all()
+    xp = poisoned((d.SK, d.H), torch.float32)
+    m.moe_permute(gp.d, _dev(x), gp.src, xp)
+    Y = _dev(Y_stage)
+    y_view = Y[rank * d.SK:(rank + 1) * d.SK]
+    m.moe_group_gemm(m.GEMM_FWD, xp, Wd, gp.cu, y_view, d.H, d.Hp)
+    out = poisoned((d.S, d.Hp), torch.float32)
+    m.moe_combine(gp.d, rank, Y, gp.dest, _dev(topk_w.reshape(-1)), out)
+    # oracle
+    _, dest, src = oracle.layout(idx, pl, rank)
+    cu = pl.cu_seqlens()[rank]
+    xp_ref = oracle.permute(x, src, d.K, dtype="f32")
+    assert (xp.cpu().numpy() == xp_ref).all()
+    y_ref = oracle.group_gemm("fwd", xp_ref, W_up, cu, "f32")
+    check_close(y_view.cpu().numpy(), y_ref, "f32", what="tiny up-projection")
+    Y_ref = Y_stage.copy()
+    Y_ref[rank * d.SK:(rank + 1) * d.SK] = y_ref
+    out_ref = oracle.combine(Y_ref, dest, topk_w, rank, d.S, d.K, "f32")
+    check_close(out.cpu().numpy(), out_ref, "f32", what="tiny combine")
