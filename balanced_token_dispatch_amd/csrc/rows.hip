@@ -101,9 +101,9 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict
             acc[2 * q + 1] = __builtin_fmaf(wt[k], bf16_hi(t[k][q]), acc[2 * q + 1]);
           }
         } else {
+          const f32x4 f = __builtin_bit_cast(f32x4, t[k]);
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[q] = __builtin_fmaf(wt[k], __builtin_bit_cast(float, t[k][q]), acc[q]);
+          for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(wt[k], f[q], acc[q]);
         }
       }
       u32x4 r;
@@ -111,8 +111,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict
 #pragma unroll
         for (int q = 0; q < 4; ++q) r[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
       } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = __builtin_bit_cast(uint32_t, acc[q]);
+        r = __builtin_bit_cast(u32x4, (f32x4){acc[0], acc[1], acc[2], acc[3]});
       }
       __builtin_nontemporal_store(r, o + v);
     }
@@ -146,8 +145,9 @@ __global__ __launch_bounds__(kRowThreads) void k_combine_anyk(const u32x4 *__res
             acc[2 * q + 1] = __builtin_fmaf(w, bf16_hi(t[q]), acc[2 * q + 1]);
           }
         } else {
+          const f32x4 f = __builtin_bit_cast(f32x4, t);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(w, __builtin_bit_cast(float, t[q]), acc[q]);
+          for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(w, f[q], acc[q]);
         }
       }
       u32x4 r;
@@ -155,8 +155,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine_anyk(const u32x4 *__res
 #pragma unroll
         for (int q = 0; q < 4; ++q) r[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
       } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = __builtin_bit_cast(uint32_t, acc[q]);
+        r = __builtin_bit_cast(u32x4, (f32x4){acc[0], acc[1], acc[2], acc[3]});
       }
       o[v] = r;
     }
