@@ -1,0 +1,126 @@
+"""One MoE layer step on one rank, as a sequence of libmoe.so calls.
+
+Buffers are allocated once (static shapes: every rank receives exactly S*K
+rows, so nothing here depends on the routing).  ``forward`` and
+``backward`` only enqueue C-ABI calls on torch's current stream; every
+number is computed by the HIP kernels.
+
+Forward (rank r):  plan -> dispatch layout -> prefetch slot rows of both
+projections -> permute -> up GEMM -> down GEMM (written into rank r's
+slice of the all-ranks expert-output buffer) -> combine.
+Backward:          weighted permute of the output gradient (combine's
+adjoint) -> down DGRAD -> down WGRAD -> up DGRAD -> up WGRAD -> fold the
+replica rows of both weight gradients into their home experts.
+The activation between the projections is the identity.
+"""
+from dataclasses import dataclass
+
+import torch
+
+from . import (GEMM_DGRAD, GEMM_FWD, GEMM_WGRAD, dims as _mk_dims, dispatch_layout_workspace_bytes,
+               moe_combine, moe_dispatch_layout, moe_group_gemm, moe_permute, moe_plan,
+               moe_prefetch, moe_replica_grad_fold, plan_words, plan_workspace_bytes)
+
+
+@dataclass
+class Shape:
+    R: int
+    S: int
+    K: int
+    E: int
+    B: int
+    H: int
+    Hp: int
+
+    @property
+    def SK(self):
+        return self.S * self.K
+
+    @property
+    def G(self):
+        return self.E + self.B
+
+
+class LayerStep:
+    def __init__(self, shape: Shape, rank: int = 0, dtype=torch.bfloat16, device="cuda",
+                 backward: bool = True):
+        s = shape
+        self.s, self.rank, self.dtype, self.device = s, rank, dtype, device
+        self.d = _mk_dims(s.R, s.S, s.K, s.E, s.B)
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        act = dict(dtype=dtype, device=device)
+        self.topk_idx = torch.zeros((s.R, s.S, s.K), **i32)
+        self.topk_w = torch.zeros((s.R, s.S, s.K), **f32)
+        self.counts = torch.zeros((s.R, s.E), **i32)
+        self.plan = torch.zeros(plan_words(self.d), **i32)
+        self.status = torch.zeros(1, **i32)
+        ws = max(plan_workspace_bytes(self.d), dispatch_layout_workspace_bytes(self.d))
+        self.ws = torch.zeros(ws, dtype=torch.uint8, device=device)
+        self.cu = torch.zeros(s.G + 1, **i32)
+        self.dest = torch.zeros(s.R * s.SK, **i32)
+        self.src = torch.zeros(s.SK, **i32)
+        self.x_all = torch.zeros((s.R * s.S, s.H), **act)
+        self.w_up = torch.zeros((s.G, s.H, s.Hp), **act)
+        self.w_down = torch.zeros((s.G, s.Hp, s.H), **act)
+        self.xp = torch.zeros((s.SK, s.H), **act)
+        self.z = torch.zeros((s.SK, s.Hp), **act)
+        self.y_all = torch.zeros((s.R * s.SK, s.H), **act)
+        self.out = torch.zeros((s.S, s.H), **act)
+        self.backward_enabled = backward
+        if backward:
+            self.dout_all = torch.zeros((s.R * s.S, s.H), **act)
+            self.dy = torch.zeros((s.SK, s.H), **act)
+            self.dz = torch.zeros((s.SK, s.Hp), **act)
+            self.dxp = torch.zeros((s.SK, s.H), **act)
+            self.dw_up = torch.zeros((s.G, s.H, s.Hp), **f32)
+            self.dw_down = torch.zeros((s.G, s.Hp, s.H), **f32)
+
+    @property
+    def y(self):
+        """This rank's slice of the expert-output buffer (the down GEMM writes here)."""
+        r, SK = self.rank, self.s.SK
+        return self.y_all[r * SK:(r + 1) * SK]
+
+    @staticmethod
+    def _call(timer, name, fn, *args):
+        if timer is None:
+            fn(*args)
+        else:
+            timer(name, fn, *args)
+
+    def forward(self, timer=None):
+        s, r, c = self.s, self.rank, self._call
+        c(timer, "plan", moe_plan, self.d, self.topk_idx, self.counts, self.plan, self.status,
+          self.ws)
+        c(timer, "dispatch_layout", moe_dispatch_layout, self.d, r, self.topk_idx, self.plan,
+          self.cu, self.dest, self.src, self.ws)
+        c(timer, "prefetch", moe_prefetch, self.d, r, self.plan, self.w_up)
+        c(timer, "prefetch", moe_prefetch, self.d, r, self.plan, self.w_down)
+        c(timer, "permute", moe_permute, self.d, self.x_all, self.src, self.xp)
+        c(timer, "gemm_fwd", moe_group_gemm, GEMM_FWD, self.xp, self.w_up, self.cu, self.z, s.H,
+          s.Hp)
+        c(timer, "gemm_fwd", moe_group_gemm, GEMM_FWD, self.z, self.w_down, self.cu, self.y, s.Hp,
+          s.H)
+        c(timer, "combine", moe_combine, self.d, r, self.y_all, self.dest,
+          self.topk_w.view(-1), self.out)
+
+    def backward(self, timer=None):
+        s, r, c = self.s, self.rank, self._call
+        c(timer, "permute_weighted", moe_permute, self.d, self.dout_all, self.src, self.dy,
+          self.topk_w.view(-1))
+        c(timer, "gemm_dgrad", moe_group_gemm, GEMM_DGRAD, self.dy, self.w_down, self.cu, self.dz,
+          s.Hp, s.H)
+        c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.z, self.dy, self.cu, self.dw_down,
+          s.Hp, s.H)
+        c(timer, "gemm_dgrad", moe_group_gemm, GEMM_DGRAD, self.dz, self.w_up, self.cu, self.dxp,
+          s.H, s.Hp)
+        c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.xp, self.dz, self.cu, self.dw_up,
+          s.H, s.Hp)
+        c(timer, "fold", moe_replica_grad_fold, self.d, r, self.plan, self.dw_up)
+        c(timer, "fold", moe_replica_grad_fold, self.d, r, self.plan, self.dw_down)
+
+    def step(self, timer=None):
+        self.forward(timer)
+        if self.backward_enabled:
+            self.backward(timer)

@@ -1,0 +1,336 @@
+"""Benchmark: MoE-layer tokens/s on one MI355X for the redundant-expert dispatch path.
+
+Default workload: R=32 simulated ranks, S=4096 tokens/rank, E=256 experts (8 per rank),
+K=8, B=8 replica slots, H=7168, H'=2048, bf16, Zipf-skewed routing at maxvio ~8; one step =
+the whole hot path on rank 0, forward and backward:
+  plan, dispatch layout, slot prefetch (both projections), permute, up/down grouped GEMMs,
+  combine; weighted permute, down/up DGRAD and WGRAD, replica-gradient folds.
+value = input tokens of rank 0 per second (S / step time), inputs resident in HBM.
+
+Also printed in the same JSON line: per-kernel times and roofline fractions, the roofline
+entry of the dominant kernel (HIP events around every launch in the timed region), the same
+step at maxvio 0 and 1 (per-rank time flatness), and the CPU oracle timed on a bounded sample
+of the same step on this host.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-sweep]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s per GPU at maxvio 0/1/8; GEMM MFMA %, permute HBM GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class EventTimer:
+    """HIP events around every launch, on torch's current stream (the one the library uses)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.events = defaultdict(list)
+
+    def __call__(self, name, fn, *args):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        fn(*args)
+        e.record()
+        self.events[name].append((s, e))
+
+    def ms(self):
+        return {k: [s.elapsed_time(e) for s, e in v] for k, v in self.events.items()}
+
+
+def algorithmic_work(shape, n_slots_used):
+    """Minimum bytes (or flops) per launch of each kernel of the step."""
+    R, S, K, E, H, Hp = shape.R, shape.S, shape.K, shape.E, shape.H, shape.Hp
+    SK = S * K
+    gemm = 2.0 * SK * H * Hp
+    return {
+        "plan": ("hbm", 4.0 * R * SK + 4.0 * R * E),
+        "dispatch_layout": ("hbm", 8.0 * R * SK + 4.0 * SK),
+        "prefetch": ("hbm", 2.0 * n_slots_used * H * Hp * 2),
+        "permute": ("hbm", 2.0 * SK * H * 2 + 4.0 * SK),
+        "gemm_fwd": ("mfma", gemm),
+        "combine": ("hbm", SK * H * 2.0 + S * H * 2.0 + 8.0 * SK),
+        "permute_weighted": ("hbm", 2.0 * SK * H * 2 + 8.0 * SK),
+        "gemm_dgrad": ("mfma", gemm),
+        "gemm_wgrad": ("mfma", gemm),
+        "fold": ("hbm", 3.0 * n_slots_used * H * Hp * 4),
+    }
+
+
+def setup_layer(wl, target, rank, placement="receiver0", layer=None):
+    import numpy as np
+    import torch
+    import synth
+    from balanced_token_dispatch_amd.layer import LayerStep, Shape
+    d = wl.dims
+    zipf = synth.zipf_for(wl, target, placement)
+    t0 = time.time()
+    idx, w = synth.routing(d, zipf, wl.base_seed, placement)
+    log(f"routing {wl.name} maxvio target {target}: zipf s={zipf:.4f}, {time.time() - t0:.1f}s")
+    if layer is None:
+        layer = LayerStep(Shape(d.R, d.S, d.K, d.E, d.B, d.H, d.Hp), rank=rank)
+        seed = wl.base_seed
+        synth.fill_normal_(layer.x_all, 1.0, seed * 10 + 1)
+        synth.fill_normal_(layer.w_up, 0.02, seed * 10 + 2)
+        synth.fill_normal_(layer.w_down, 0.02, seed * 10 + 3)
+        synth.fill_normal_(layer.y_all, 1.0, seed * 10 + 4)
+        if layer.backward_enabled:
+            synth.fill_normal_(layer.dout_all, 1.0, seed * 10 + 5)
+    layer.topk_idx.copy_(torch.from_numpy(idx))
+    layer.topk_w.copy_(torch.from_numpy(w))
+    torch.cuda.synchronize()
+    info = {"maxvio": synth.realised_maxvio(idx, d.E), "zipf_s": zipf,
+            "home_load_ratio": synth.home_load_ratio(idx, d)}
+    return layer, idx, w, info
+
+
+def run_steps(layer, steps, warmup, timer=None):
+    import torch
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.step(timer)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+class _LazyRows:
+    """Host copies of selected rows of a device weight tensor, fetched on first use."""
+
+    def __init__(self, dev, prefetch_map):
+        self.dev, self.map, self.cache = dev, prefetch_map, {}
+        self.shape = tuple(dev.shape)
+
+    def __getitem__(self, rho):
+        import numpy as np
+        import torch
+        rho = int(rho)
+        if rho not in self.cache:
+            src = self.map.get(rho, rho)
+            self.cache[rho] = self.dev[src].view(torch.int16).cpu().numpy().view(np.uint16)
+        return self.cache[rho]
+
+
+def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
+    """The oracle as it stands, on a bounded sample of the same step, scaled to tokens/s.
+
+    Timed on this host: the full plan and layout of all R ranks' routing, then permute,
+    both projections forward, the weighted permute, both DGRADs and WGRADs on the first
+    ``rows_sample`` rows of rank r's buffer, the combine of ``tokens_sample`` tokens, and
+    the fold on 1/8 of each replica row.  Each part is scaled to the full step.
+    """
+    import numpy as np
+    import torch
+    import oracle
+    s, r = layer.s, layer.rank
+    t = {}
+    t0 = time.perf_counter()
+    pl = oracle.plan(idx, s.E, s.B)
+    t["plan"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    cu, dest, src = oracle.layout(idx, pl, r)
+    t["layout"] = time.perf_counter() - t0
+    n = int(min(rows_sample, cu[-1]))
+    se, _, _ = pl.slot_table()
+    pmap = {s.E + j: int(se[r, j]) for j in range(s.B) if se[r, j] >= 0}
+    wu, wd = _LazyRows(layer.w_up, pmap), _LazyRows(layer.w_down, pmap)
+    cu_s = np.minimum(cu, n)
+    toks = np.unique(src[:n] // s.K)
+    x_rows = layer.x_all[torch.from_numpy(toks).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    g_rows = layer.dout_all[torch.from_numpy(toks).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    remap = {int(tk): i for i, tk in enumerate(toks)}
+    src_l = np.array([remap[int(c) // s.K] * s.K + int(c) % s.K for c in src[:n]], np.int64)
+    w_flat = np.zeros(len(toks) * s.K, np.float32)
+    w_all = w.reshape(-1)
+    for i, c in enumerate(src[:n]):
+        w_flat[src_l[i]] = w_all[c]
+    for rho in range(s.G):                       # weight rows fetched outside the timed parts
+        if cu_s[rho + 1] > cu_s[rho]:
+            wu[rho], wd[rho]
+    t0 = time.perf_counter()
+    xp = oracle.permute(x_rows, src_l.astype(np.int32), s.K)
+    z = oracle.group_gemm("fwd", xp, wu, cu_s)
+    oracle.group_gemm("fwd", z, wd, cu_s)
+    dy = oracle.permute(g_rows, src_l.astype(np.int32), s.K, row_scale=w_flat)
+    dz = oracle.group_gemm("dgrad", dy, wd, cu_s)
+    oracle.group_gemm("dgrad", dz, wu, cu_s)
+    act = [rho for rho in range(s.G) if cu_s[rho + 1] > cu_s[rho]]
+    for a, b, K_, N_ in ((z, dy, s.Hp, s.H), (xp, dz, s.H, s.Hp)):
+        for rho in act:                          # wgrad of the sampled segments only
+            lo, hi = cu_s[rho], cu_s[rho + 1]
+            sub = np.array([0, hi - lo])
+            oracle.group_gemm("wgrad", a[lo:hi], b[lo:hi], sub,
+                              out=np.zeros((1, K_, N_), np.float32))
+    t["rows"] = time.perf_counter() - t0
+    # combine: tokens_sample tokens of rank r, expert outputs gathered from a staged buffer
+    ts = np.arange(min(tokens_sample, s.S))
+    need = dest.reshape(s.R, s.S, s.K)[r, ts].reshape(-1)
+    need = need[need >= 0]
+    y_rows = layer.y_all[torch.from_numpy(need.astype(np.int64)).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    ymap = np.full(s.R * s.SK, -1, np.int64)
+    ymap[need] = np.arange(need.size)
+    dest_l = np.where(dest >= 0, ymap[np.maximum(dest, 0)], -1)
+    t0 = time.perf_counter()
+    oracle.combine(y_rows, dest_l, w, r, s.S, s.K, tokens=ts)
+    t["combine"] = time.perf_counter() - t0
+    frac = 8
+    dw = np.zeros((s.G, s.H * s.Hp // frac), np.float32)
+    t0 = time.perf_counter()
+    oracle.replica_grad_fold(dw, pl, r)
+    oracle.replica_grad_fold(dw, pl, r)
+    t["fold"] = (time.perf_counter() - t0) * frac
+    est = (t["plan"] + t["layout"] + t["rows"] * s.SK / max(n, 1)
+           + t["combine"] * s.S / max(len(ts), 1) + t["fold"])
+    return est, t, n, len(ts)
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        return max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        return 1
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="skew8_large_fwdbwd")
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=16384)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures the one-GPU share of one rank; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported: this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import balanced_token_dispatch_amd as moe  # noqa: F401  (fails loudly if not built)
+
+    wl = synth.WORKLOADS[args.workload]
+    target = wl.maxvio_targets[-1] if wl.maxvio_targets[-1] is not None else None
+    layer, idx, w, info = setup_layer(wl, target, args.rank)
+    s = layer.s
+    timer = EventTimer()
+    elapsed = run_steps(layer, args.steps, args.warmup, timer)
+    status = int(layer.status.item())
+    plan = layer.plan.cpu().numpy()
+    if status != 0:
+        log(f"WARNING: plan status {status} (bad ids / slot overflow)")
+    E, R, B = s.E, s.R, s.B
+    off_sexp = 8 + 4 * E + 5 * (E + R)
+    slots = plan[off_sexp + args.rank * B: off_sexp + (args.rank + 1) * B]
+    n_slots = int((slots >= 0).sum())
+    ms_step = elapsed * 1000.0 / args.steps
+    value = s.S * args.steps / elapsed
+
+    work = algorithmic_work(s, n_slots)
+    kernels = {}
+    totals = {}
+    for name, times in timer.ms().items():
+        bound, amount = work[name]
+        avg = float(np.mean(times))
+        per_step = float(np.sum(times)) / args.steps
+        totals[name] = per_step
+        if bound == "mfma":
+            ach = amount / (avg * 1e-3) / 1e12
+            kernels[name] = {"avg_ms": round(avg, 4), "launches_per_step": len(times) // args.steps,
+                             "tflops": round(ach, 1), "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+        else:
+            ach = amount / (avg * 1e-3) / 1e9 if avg > 0 else 0.0
+            kernels[name] = {"avg_ms": round(avg, 4), "launches_per_step": len(times) // args.steps,
+                             "gbs": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4)}
+    dom = max(totals, key=totals.get)
+    bound, amount = work[dom]
+    avg = kernels[dom]["avg_ms"]
+    if bound == "mfma":
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(amount / (avg * 1e-3) / 1e12, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(amount / (avg * 1e-3) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    log(f"main: {ms_step:.3f} ms/step, {value:.0f} tokens/s, status {status}, slots used {n_slots}")
+
+    sweep = {}
+    if not args.no_sweep and wl.name == "skew8_large_fwdbwd":
+        sweep[f"{info['maxvio']:.2f}"] = {"ms_per_step": round(ms_step, 4),
+                                          "tokens_per_s": round(value, 1),
+                                          "home_load_ratio": round(info["home_load_ratio"], 3)}
+        for t in (0.0, 1.0):
+            wl_t = synth.WORKLOADS["skew1_large"]
+            layer, idx_t, _, info_t = setup_layer(wl_t, t, args.rank, layer=layer)
+            el = run_steps(layer, max(5, args.steps // 2), 2)
+            ms_t = el * 1000.0 / max(5, args.steps // 2)
+            sweep[f"{info_t['maxvio']:.2f}"] = {
+                "ms_per_step": round(ms_t, 4), "tokens_per_s": round(s.S / (ms_t * 1e-3), 1),
+                "home_load_ratio": round(info_t["home_load_ratio"], 3),
+                "status": int(layer.status.item())}
+            log(f"sweep maxvio {info_t['maxvio']:.2f}: {ms_t:.3f} ms/step")
+        # restore the headline routing for the CPU baseline below
+        layer, idx, w, info = setup_layer(wl, target, args.rank, layer=layer)
+        t_all = [v["ms_per_step"] for v in sweep.values()]
+        sweep["flatness_max_over_min"] = round(max(t_all) / min(t_all), 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        est, parts, n_rows, n_tok = cpu_baseline(layer, idx, w, args.cpu_rows, args.cpu_tokens)
+        cpu = {"value": round(s.S / est, 2), "unit": "tokens/s", "cores": blas_threads(),
+               "kind": "oracle",
+               "sample": (f"plan+layout of all {s.R} ranks' routing in full; permute, fwd up/down, "
+                          f"weighted permute, dgrad x2, wgrad x2 on {n_rows} of {s.SK} rows; "
+                          f"combine of {n_tok} of {s.S} tokens; fold on 1/8 of each row; "
+                          f"each part scaled to the full step"),
+               "seconds_measured": round(time.time() - t0, 1),
+               "parts_s": {k: round(v, 3) for k, v in parts.items()}}
+        log(f"cpu baseline: {cpu['value']} tokens/s ({cpu['seconds_measured']} s)")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "R": s.R, "S": s.S, "K": s.K, "E": s.E, "B": s.B,
+                   "H": s.H, "H_prime": s.Hp, "rank": args.rank, "step": "forward+backward",
+                   "maxvio": round(info["maxvio"], 3), "zipf_s": info["zipf_s"],
+                   "plan_status": status, "replica_slots_used_on_rank": n_slots},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "maxvio_sweep": sweep or None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

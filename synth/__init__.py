@@ -293,8 +293,26 @@ def device_normal(shape, std: float, seed: int, dtype, device="cuda", chunk_rows
     return out
 
 
+def fill_normal_(t, std: float, seed: int, chunk_rows: int = 8192):
+    """Fill a device tensor in place with seeded N(0, std^2) values (chunked over dim 0)."""
+    import torch
+    rows = t.shape[0]
+    flat = t.view(rows, -1)
+    for c0 in range(0, rows, chunk_rows):
+        c1 = min(rows, c0 + chunk_rows)
+        g = torch.Generator(device=t.device)
+        g.manual_seed((int(seed) * 1000003 + c0 // chunk_rows) & 0x7FFFFFFFFFFFFFFF)
+        r = torch.randn((c1 - c0, flat.shape[1]), generator=g, device=t.device,
+                        dtype=torch.float32)
+        if std != 1.0:
+            r.mul_(std)
+        flat[c0:c1].copy_(r)
+    return t
+
+
 __all__ = [
     "Dims", "Workload", "WORKLOADS", "routing", "balanced_routing", "realised_maxvio",
     "home_load_ratio", "calibrate_zipf", "zipf_for", "zipf_bias", "popularity_rank_of_expert",
-    "host_normal", "host_ternary", "to_bf16_bits", "device_normal", "load_calibration",
+    "host_normal", "host_ternary", "to_bf16_bits", "device_normal", "fill_normal_",
+    "load_calibration",
 ]
