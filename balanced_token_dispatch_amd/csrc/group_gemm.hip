@@ -39,19 +39,24 @@ constexpr int kMaxG = 1088;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
+// Buffer resource over [base, base + bytes): loads past the end return zero.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, long long bytes) {
+  const int n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+constexpr int kOOB = 0x7FFFFFF0;  // an offset past every resource: the load returns zero
+
 // Contraction-contiguous operand: row r, contraction c at base[r*ld + c].
 // Each thread moves 8 chunks of 8 elements: chunk q = tid + 256*u -> row q/8, col (q%8)*8.
 struct ContigLoad {
   u32x4 v[8];
-  __device__ void load(const uint16_t *base, long long ld, int row_lim, int c0, int c_lim) {
+  __device__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int row_lim, int c0, int c_lim) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int q = threadIdx.x + kGemmThreads * u;
       const int r = q >> 3, c = c0 + (q & 7) * 8;
-      if (r < row_lim && c < c_lim)
-        v[u] = *(const u32x4 *)(base + (long long)r * ld + c);
-      else
-        v[u] = (u32x4){0, 0, 0, 0};
+      const int off = (r < row_lim && c < c_lim) ? (r * ld + c) * 2 : kOOB;
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
     }
   }
   __device__ void store(uint16_t *lds) const {
@@ -64,24 +69,24 @@ struct ContigLoad {
 };
 
 // Contraction-strided operand: row r, contraction c at base[c*ld + r].
-// Each thread moves one 8x8 block: contraction rows cb*8..+8, rows ib*8..+8,
-// with cb = tid/32, ib = tid%32, and transposes it in registers.
+// Each thread moves one 8x8 block: contraction rows cb*8..+8, rows ib*8..+8, and
+// transposes it in registers.  cb = tid%8, ib = tid/8: a load instruction reads 128
+// contiguous bytes per contraction row, and the 16 lanes of each LDS write group hit
+// 8 column chunks x 2 row parities = 16 distinct bank quads (rows are 144 B apart).
 struct StridedLoad {
   u32x4 v[8];  // v[kk] = 8 row values at contraction index cb*8+kk
-  __device__ void load(const uint16_t *base, long long ld, int row_lim, int c0, int c_lim) {
-    const int cb = threadIdx.x >> 5, ib = threadIdx.x & 31;
+  __device__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int row_lim, int c0, int c_lim) {
+    const int cb = threadIdx.x & 7, ib = threadIdx.x >> 3;
     const int r = ib * 8;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int c = c0 + cb * 8 + kk;
-      if (r < row_lim && c < c_lim)
-        v[kk] = *(const u32x4 *)(base + (long long)c * ld + r);
-      else
-        v[kk] = (u32x4){0, 0, 0, 0};
+      const int off = (r < row_lim && c < c_lim) ? (c * ld + r) * 2 : kOOB;
+      v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
     }
   }
   __device__ void store(uint16_t *lds) const {
-    const int cb = threadIdx.x >> 5, ib = threadIdx.x & 31;
+    const int cb = threadIdx.x & 7, ib = threadIdx.x >> 3;
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
       // row ib*8+rr: contraction values cb*8+0..7 = element rr of v[0..7]
@@ -104,11 +109,38 @@ struct Loader<true> { typedef ContigLoad T; };
 template <>
 struct Loader<false> { typedef StridedLoad T; };
 
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+__device__ inline void read_frags(Frags &f, const uint16_t *As, const uint16_t *Bs, int wi, int wj,
+                                  int lane, int ks) {
+  const int col = ks * 16 + (lane >> 5) * 8;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f.a[t] = __builtin_bit_cast(bf16x8,
+                                *(const u32x4 *)(As + (wi + t * 32 + (lane & 31)) * LDS_STRIDE + col));
+    f.b[t] = __builtin_bit_cast(bf16x8,
+                                *(const u32x4 *)(Bs + (wj + t * 32 + (lane & 31)) * LDS_STRIDE + col));
+  }
+}
+
+__device__ inline void mma16(f32x16 (&acc)[4][4], const Frags &f) {
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tm][tn], 0, 0, 0);
+}
+
 // One 256x256 output tile: out_tile[i][j] = sum_c Aop(i, c) * Bop(j, c).
-// Aop rows i (activations or x^T), Bop rows j (weights or dy^T).
+// Aop rows i (activations or x^T), Bop rows j (weights or dy^T).  Pipeline per K step kt:
+// fragments of step kt come from LDS buffer kt&1 (double-buffered in registers across the
+// four 16-wide MFMA sub-steps); meanwhile tile kt+1, loaded into registers during step
+// kt-1, is written to the other LDS buffer and tile kt+2 is requested from memory.
 template <bool A_CONTIG, bool B_CONTIG>
-__device__ inline void tile_mma(uint16_t *lds, const uint16_t *a_base, long long lda, int a_rows,
-                                const uint16_t *b_base, long long ldb, int b_rows, int c_len,
+__device__ inline void tile_mma(uint16_t *lds, __amdgpu_buffer_rsrc_t ra, int lda, int a_rows,
+                                __amdgpu_buffer_rsrc_t rb, int ldb, int b_rows, int c_len,
                                 f32x16 (&acc)[4][4]) {
   typename Loader<A_CONTIG>::T la;
   typename Loader<B_CONTIG>::T lb;
@@ -121,37 +153,45 @@ __device__ inline void tile_mma(uint16_t *lds, const uint16_t *a_base, long long
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = (f32x16){};
 
-  la.load(a_base, lda, a_rows, 0, c_len);
-  lb.load(b_base, ldb, b_rows, 0, c_len);
-  for (int kt = 0; kt < nk; ++kt) {
-    uint16_t *As = lds + (kt & 1) * 2 * TILE_ELEMS;
-    uint16_t *Bs = As + TILE_ELEMS;
-    la.store(As);
-    lb.store(Bs);
-    __syncthreads();
-    if (kt + 1 < nk) {
-      la.load(a_base, lda, a_rows, (kt + 1) * BK, c_len);
-      lb.load(b_base, ldb, b_rows, (kt + 1) * BK, c_len);
-    }
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int col = ks * 16 + (lane >> 5) * 8;
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        af[t] = __builtin_bit_cast(bf16x8,
-                                   *(const u32x4 *)(As + (wi + t * 32 + (lane & 31)) * LDS_STRIDE + col));
-        bfr[t] = __builtin_bit_cast(bf16x8,
-                                    *(const u32x4 *)(Bs + (wj + t * 32 + (lane & 31)) * LDS_STRIDE + col));
-      }
-#pragma unroll
-      for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[tn], af[tm], acc[tm][tn], 0, 0, 0);
-    }
+  la.load(ra, lda, a_rows, 0, c_len);
+  lb.load(rb, ldb, b_rows, 0, c_len);
+  la.store(lds);
+  lb.store(lds + TILE_ELEMS);
+  if (nk > 1) {
+    la.load(ra, lda, a_rows, BK, c_len);
+    lb.load(rb, ldb, b_rows, BK, c_len);
   }
-  __syncthreads();  // LDS reused by the next tile
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint16_t *As = lds + (kt & 1) * 2 * TILE_ELEMS;
+    const uint16_t *Bs = As + TILE_ELEMS;
+    uint16_t *An = lds + ((kt + 1) & 1) * 2 * TILE_ELEMS;
+    Frags f0, f1;
+    read_frags(f0, As, Bs, wi, wj, lane, 0);
+    if (kt + 1 < nk) {
+      la.store(An);
+      lb.store(An + TILE_ELEMS);
+      if (kt + 2 < nk) {
+        la.load(ra, lda, a_rows, (kt + 2) * BK, c_len);
+        lb.load(rb, ldb, b_rows, (kt + 2) * BK, c_len);
+      }
+    }
+    read_frags(f1, As, Bs, wi, wj, lane, 1);
+    // keep each sub-step's fragment reads ahead of the previous sub-step's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    mma16(acc, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(f0, As, Bs, wi, wj, lane, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mma16(acc, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(f1, As, Bs, wi, wj, lane, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mma16(acc, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma16(acc, f1);
+    __syncthreads();
+  }
 }
 
 // Decode a tile index into (row tile, col tile) walking groups of kGroupM row tiles.
@@ -251,10 +291,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
       const int j0 = ct * BN;
       const uint16_t *w = b + (size_t)rho * Kd * N;
       if (OP == MOE_GEMM_FWD)
-        tile_mma<true, false>(lds, a + (size_t)m0 * Kd, Kd, rows, w + j0, N, N - j0, Kd, acc);
+        tile_mma<true, false>(lds, make_rsrc(a + (size_t)m0 * Kd, (long long)rows * Kd * 2), Kd,
+                              rows, make_rsrc(w + j0, ((long long)Kd * N - j0) * 2), N, N - j0, Kd,
+                              acc);
       else
-        tile_mma<true, true>(lds, a + (size_t)m0 * N, N, rows, w + (size_t)j0 * N, N, Kd - j0, N,
-                             acc);
+        tile_mma<true, true>(lds, make_rsrc(a + (size_t)m0 * N, (long long)rows * N * 2), N, rows,
+                             make_rsrc(w + (size_t)j0 * N, (long long)(Kd - j0) * N * 2), N,
+                             Kd - j0, N, acc);
       uint16_t *o = (uint16_t *)out + (size_t)m0 * ncols + j0;
 #pragma unroll
       for (int tm = 0; tm < 4; ++tm) {
@@ -282,8 +325,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
       const int rho = find_seg(sStart, G, sidx);
       const int m0 = sCu[rho], len = sCu[rho + 1] - m0;
       const int i0 = it * BM, j0 = ct * BN;
-      tile_mma<false, false>(lds, a + (size_t)m0 * Kd + i0, Kd, Kd - i0, b + (size_t)m0 * N + j0,
-                             N, N - j0, len, acc);
+      tile_mma<false, false>(lds, make_rsrc(a + (size_t)m0 * Kd + i0, ((long long)len * Kd - i0) * 2),
+                             Kd, Kd - i0,
+                             make_rsrc(b + (size_t)m0 * N + j0, ((long long)len * N - j0) * 2), N,
+                             N - j0, len, acc);
       float *o = (float *)out + ((size_t)rho * Kd + i0) * N + j0;
 #pragma unroll
       for (int tm = 0; tm < 4; ++tm) {

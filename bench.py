@@ -220,7 +220,7 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=16384)
+    ap.add_argument("--cpu-rows", type=int, default=32768)
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
