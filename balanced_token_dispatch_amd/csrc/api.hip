@@ -5,15 +5,13 @@
 
 namespace moe {
 
-void gemm_set_attributes();
-
 namespace {
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices];
 std::once_flag g_once[kMaxDevices];
 }  // namespace
 
-// Compute units of the current device (cached; first use also sets kernel attributes).
+// Compute units of the current device (cached per device).
 int device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
@@ -22,7 +20,6 @@ int device_cu_count() {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
     g_cu_count[dev] = n;
-    gemm_set_attributes();
   });
   return g_cu_count[dev];
 }

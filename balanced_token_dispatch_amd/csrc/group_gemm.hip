@@ -10,8 +10,8 @@
 //   * persistent grid of one 256-thread workgroup per CU; every workgroup
 //     rebuilds the tile table from cu_seqlens in LDS (no host sync, the
 //     grid is sized from the machine, not from the routing);
-//   * 256x256 output tile, K step 64, 4 waves in 2x2, each wave 128x128 as
-//     4x4 v_mfma_f32_32x32x16_bf16 blocks (fp32 accumulators);
+//   * 256x256 output tile, K step 32, 8 waves in 2x4, each wave 128x64 as
+//     4x2 v_mfma_f32_32x32x16_bf16 blocks (fp32 accumulators);
 //   * operands staged global -> registers -> LDS, double-buffered, one
 //     barrier per K step, next tile's global loads in flight during the
 //     MFMAs; an operand whose contraction index is strided in memory (the
@@ -31,10 +31,12 @@ namespace moe {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kGemmThreads = 256;
-constexpr int LDS_STRIDE = BK + 8;            // bf16 elements per LDS row (144 B)
-constexpr int TILE_ELEMS = BM * LDS_STRIDE;   // one operand tile (BM == BN)
+constexpr int BM = 256, BN = 256, BK = 32;
+// 8 waves (two per SIMD, so one wave's MFMAs overlap the other's waits), laid out 2 x 4 over
+// the 256x256 tile: each wave owns 128 x 64 = 4 x 2 blocks of 32x32.
+constexpr int kWavesM = 2, kWavesN = 4, kWaves = kWavesM * kWavesN;
+constexpr int kGemmThreads = 64 * kWaves;
+constexpr int TM = BM / (32 * kWavesM), TN = BN / (32 * kWavesN);
 constexpr int kMaxG = 1088;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
@@ -46,152 +48,174 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, long long b
 }
 constexpr int kOOB = 0x7FFFFFF0;  // an offset past every resource: the load returns zero
 
-// Contraction-contiguous operand: row r, contraction c at base[r*ld + c].
-// Each thread moves 8 chunks of 8 elements: chunk q = tid + 256*u -> row q/8, col (q%8)*8.
-struct ContigLoad {
-  u32x4 v[8];
-  __device__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int row_lim, int c0, int c_lim) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int q = threadIdx.x + kGemmThreads * u;
-      const int r = q >> 3, c = c0 + (q & 7) * 8;
-      const int off = (r < row_lim && c < c_lim) ? (r * ld + c) * 2 : kOOB;
-      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-    }
-  }
-  __device__ void store(uint16_t *lds) const {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int q = threadIdx.x + kGemmThreads * u;
-      *(u32x4 *)(lds + (q >> 3) * LDS_STRIDE + (q & 7) * 8) = v[u];
-    }
-  }
-};
+typedef __attribute__((address_space(3))) void *lds_vptr;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef __attribute__((address_space(3))) bf16x4_t *lds_bf16x4_ptr;
 
-// Contraction-strided operand: row r, contraction c at base[c*ld + r].
-// Each thread moves one 8x8 block: contraction rows cb*8..+8, rows ib*8..+8, and
-// transposes it in registers.  cb = tid%8, ib = tid/8: a load instruction reads 128
-// contiguous bytes per contraction row, and the 16 lanes of each LDS write group hit
-// 8 column chunks x 2 row parities = 16 distinct bank quads (rows are 144 B apart).
-struct StridedLoad {
-  u32x4 v[8];  // v[kk] = 8 row values at contraction index cb*8+kk
-  __device__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int row_lim, int c0, int c_lim) {
-    const int cb = threadIdx.x & 7, ib = threadIdx.x >> 3;
-    const int r = ib * 8;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int c = c0 + cb * 8 + kk;
-      const int off = (r < row_lim && c < c_lim) ? (c * ld + r) * 2 : kOOB;
-      v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-    }
-  }
-  __device__ void store(uint16_t *lds) const {
-    const int cb = threadIdx.x & 7, ib = threadIdx.x >> 3;
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      // row ib*8+rr: contraction values cb*8+0..7 = element rr of v[0..7]
-      u32x4 o;
-      const int half = rr & 1, w = rr >> 1;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t a = v[2 * p][w], b = v[2 * p + 1][w];
-        o[p] = half ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-      }
-      *(u32x4 *)(lds + (ib * 8 + rr) * LDS_STRIDE + cb * 8) = o;
-    }
-  }
-};
+// LDS ring: kStages K-steps of BK=32; each stage holds the row-side operand then the
+// column-side operand, 256 x 32 bf16 = 16 KB each, no padding (bank spreading is done by
+// an XOR swizzle of 16-byte chunks, applied on the global side of the direct-to-LDS loads).
+constexpr int kStages = 4;
+constexpr int OP_ELEMS = 256 * BK;            // one operand of one stage
+constexpr int STAGE_ELEMS = 2 * OP_ELEMS;
 
+// Direct-to-LDS load of one operand tile (256 rows x BK contraction) into `dst`.
+// Each wave instruction writes 64 lanes x 16 B = 1 KB of LDS contiguously.
+//  contiguous source (row r, contraction c at base[r*ld + c]): LDS is [256][BK], 64 B per row;
+//    16-byte chunk k of row r sits at position k ^ ((r >> 2) & 3);
+//  strided source (row r, contraction c at base[c*ld + r]): LDS is [BK][256], 512 B per
+//    contraction row; chunk k (rows 8k..8k+7) of contraction row c sits at k ^ (4 * (c & 3)).
 template <bool CONTIG>
-struct Loader;
-template <>
-struct Loader<true> { typedef ContigLoad T; };
-template <>
-struct Loader<false> { typedef StridedLoad T; };
-
-struct Frags {
-  bf16x8 a[4], b[4];
-};
-
-__device__ inline void read_frags(Frags &f, const uint16_t *As, const uint16_t *Bs, int wi, int wj,
-                                  int lane, int ks) {
-  const int col = ks * 16 + (lane >> 5) * 8;
+__device__ inline void dma_tile(uint16_t *dst, __amdgpu_buffer_rsrc_t rs, int ld, int row_lim,
+                                int c0, int c_lim) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f.a[t] = __builtin_bit_cast(bf16x8,
-                                *(const u32x4 *)(As + (wi + t * 32 + (lane & 31)) * LDS_STRIDE + col));
-    f.b[t] = __builtin_bit_cast(bf16x8,
-                                *(const u32x4 *)(Bs + (wj + t * 32 + (lane & 31)) * LDS_STRIDE + col));
+  for (int u = 0; u < 16 / kWaves; ++u) {
+    const int blk = u * kWaves + wid;              // 1-KB block of the 16-KB tile
+    const int o = blk * 1024 + lane * 16;          // this lane's LDS byte offset
+    int off;
+    if (CONTIG) {
+      const int r = o >> 6, p = (o >> 4) & 3;
+      const int k = p ^ ((r >> 2) & 3);
+      const int c = c0 + k * 8;
+      off = (r < row_lim && c < c_lim) ? (r * ld + c) * 2 : kOOB;
+    } else {
+      const int cr = o >> 9, p = (o >> 4) & 31;
+      const int k = p ^ (4 * (cr & 3));
+      const int c = c0 + cr, r = k * 8;
+      off = (r < row_lim && c < c_lim) ? (c * ld + r) * 2 : kOOB;
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr)(dst + blk * 512), 16, off, 0, 0, 0);
   }
 }
 
-__device__ inline void mma16(f32x16 (&acc)[4][4], const Frags &f) {
+// MFMA operand t of lane `lane` (rows wbase + 32t .. +31 for a contiguous operand) at
+// contraction 16*ks + 8*(lane/32) .. +8.
+template <bool CONTIG>
+__device__ inline bf16x8 read_operand(const uint16_t *src, int wbase, int t, int lane, int ks) {
+  if (CONTIG) {
+    const int r = wbase + 32 * t + (lane & 31);
+    const int k = 2 * ks + (lane >> 5);
+    const int p = k ^ ((r >> 2) & 3);
+    return __builtin_bit_cast(bf16x8, *(const u32x4 *)(src + r * BK + p * 8));
+  } else {
+    // Two transposing reads of 4 contraction values each.  Lane rule of
+    // ds_read_b64_tr_b16 (per 16-lane group): lane a = 4u+q supplies the address of 4
+    // consecutive row values at contraction c0+u, rows r0+4q..+3; lane j of the group then
+    // receives row r0+j at contraction c0..c0+3.  The stored 16-byte chunk of rows r..r+7
+    // at contraction c sits at position (r>>3) ^ 4(c&3), and c&3 == u here, so the
+    // address depends on (t, lane) only; sub-step and half are immediate offsets.
+    const int g = lane >> 4, a = lane & 15;
+    const int u = a >> 2, q = a & 3;
+    const int r = wbase + 32 * t + 16 * (g & 1) + 4 * q;
+    const int c = ks * 16 + 8 * (g >> 1) + u;
+    const uint16_t *p0 = src + c * 256 + ((r >> 3) ^ (4 * u)) * 8 + (r & 7);
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)p0);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p0 + 4 * 256));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+constexpr int kLoadsPerStep = 2 * (16 / kWaves);  // direct-to-LDS loads per thread per K step
+
+template <int N>
+__device__ inline void waitcnt_vm() {
+  // s_waitcnt vmcnt(N), expcnt and lgkmcnt at their maximum (no wait on them);
+  // vmcnt bits [3:0] low, [15:14] high
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Wait until at most `steps` K steps of loads (the newest) are still in flight.
+__device__ inline void wait_steps(int steps) {
+  if (steps >= 3) waitcnt_vm<3 * kLoadsPerStep>();
+  else if (steps == 2) waitcnt_vm<2 * kLoadsPerStep>();
+  else if (steps == 1) waitcnt_vm<kLoadsPerStep>();
+  else waitcnt_vm<0>();
+}
+
+struct Frags {
+  bf16x8 a[TM], b[TN];
+};
+
+template <bool A_CONTIG, bool B_CONTIG>
+__device__ inline void read_frags(Frags &f, const uint16_t *stage, int wi, int wj, int lane,
+                                  int ks) {
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm)
+  for (int t = 0; t < TM; ++t) f.a[t] = read_operand<A_CONTIG>(stage, wi, t, lane, ks);
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn)
+  for (int t = 0; t < TN; ++t) f.b[t] = read_operand<B_CONTIG>(stage + OP_ELEMS, wj, t, lane, ks);
+}
+
+__device__ inline void mma16(f32x16 (&acc)[TM][TN], const Frags &f) {
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
       acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tm][tn], 0, 0, 0);
 }
 
-// One 256x256 output tile: out_tile[i][j] = sum_c Aop(i, c) * Bop(j, c).
-// Aop rows i (activations or x^T), Bop rows j (weights or dy^T).  Pipeline per K step kt:
-// fragments of step kt come from LDS buffer kt&1 (double-buffered in registers across the
-// four 16-wide MFMA sub-steps); meanwhile tile kt+1, loaded into registers during step
-// kt-1, is written to the other LDS buffer and tile kt+2 is requested from memory.
+struct TileArgs {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  int lda, a_rows, ldb, b_rows, c_len, nk;
+};
+
 template <bool A_CONTIG, bool B_CONTIG>
-__device__ inline void tile_mma(uint16_t *lds, __amdgpu_buffer_rsrc_t ra, int lda, int a_rows,
-                                __amdgpu_buffer_rsrc_t rb, int ldb, int b_rows, int c_len,
-                                f32x16 (&acc)[4][4]) {
-  typename Loader<A_CONTIG>::T la;
-  typename Loader<B_CONTIG>::T lb;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wi = (wid >> 1) * 128, wj = (wid & 1) * 128;
-  const int nk = (c_len + BK - 1) / BK;
+__device__ inline void dma_step(uint16_t *dst, const TileArgs &ta, int kt) {
+  dma_tile<A_CONTIG>(dst, ta.ra, ta.lda, ta.a_rows, kt * BK, ta.c_len);
+  dma_tile<B_CONTIG>(dst + OP_ELEMS, ta.rb, ta.ldb, ta.b_rows, kt * BK, ta.c_len);
+}
 
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = (f32x16){};
-
-  la.load(ra, lda, a_rows, 0, c_len);
-  lb.load(rb, ldb, b_rows, 0, c_len);
-  la.store(lds);
-  lb.store(lds + TILE_ELEMS);
-  if (nk > 1) {
-    la.load(ra, lda, a_rows, BK, c_len);
-    lb.load(rb, ldb, b_rows, BK, c_len);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const uint16_t *As = lds + (kt & 1) * 2 * TILE_ELEMS;
-    const uint16_t *Bs = As + TILE_ELEMS;
-    uint16_t *An = lds + ((kt + 1) & 1) * 2 * TILE_ELEMS;
-    Frags f0, f1;
-    read_frags(f0, As, Bs, wi, wj, lane, 0);
-    if (kt + 1 < nk) {
-      la.store(An);
-      lb.store(An + TILE_ELEMS);
-      if (kt + 2 < nk) {
-        la.load(ra, lda, a_rows, (kt + 2) * BK, c_len);
-        lb.load(rb, ldb, b_rows, (kt + 2) * BK, c_len);
-      }
-    }
-    read_frags(f1, As, Bs, wi, wj, lane, 1);
-    // keep each sub-step's fragment reads ahead of the previous sub-step's MFMAs
-    __builtin_amdgcn_sched_barrier(0);
-    mma16(acc, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(f0, As, Bs, wi, wj, lane, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    mma16(acc, f1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(f1, As, Bs, wi, wj, lane, 3);
-    __builtin_amdgcn_sched_barrier(0);
-    mma16(acc, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma16(acc, f1);
+// K step kt: `cur` holds step kt, `nxt` step kt+1.  Saying the two are distinct
+// (restrict) lets the compiler see that the direct-to-LDS loads issued into `cur` cannot
+// feed the fragment reads of `nxt`, so it adds no wait for them; the waits that order
+// the stages are the explicit ones below.  Per step: read the second sub-step's fragments
+// of `cur`, MFMAs of the first sub-step, wait for step kt+1's loads and barrier (every
+// wave has now finished reading `cur`), read step kt+1's first fragments, start step
+// kt+4's loads into `cur`, MFMAs of the second sub-step.  Loads are three steps ahead.
+template <bool A_CONTIG, bool B_CONTIG>
+__device__ __attribute__((always_inline)) inline void k_step(
+    const TileArgs &ta, int kt, uint16_t *__restrict__ cur, const uint16_t *__restrict__ nxt,
+    Frags &f0, Frags &f1, f32x16 (&acc)[TM][TN], int wi, int wj, int lane) {
+  read_frags<A_CONTIG, B_CONTIG>(f1, cur, wi, wj, lane, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma16(acc, f0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (kt + 1 < ta.nk) {
+    wait_steps(min(2, ta.nk - 2 - kt));
     __syncthreads();
+    read_frags<A_CONTIG, B_CONTIG>(f0, nxt, wi, wj, lane, 0);
+    if (kt + 4 < ta.nk) dma_step<A_CONTIG, B_CONTIG>(cur, ta, kt + 4);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  mma16(acc, f1);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One 256x256 output tile: out_tile[i][j] = sum_c Aop(i, c) * Bop(j, c), BK = 32 per K
+// step, K step kt in LDS stage kt % 4, up to four K steps of loads in flight.
+template <bool A_CONTIG, bool B_CONTIG>
+__device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta, f32x16 (&acc)[TM][TN]) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wi = (wid / kWavesN) * (32 * TM), wj = (wid % kWavesN) * (32 * TN);
+  const int nk = ta.nk;
+
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = (f32x16){};
+
+  for (int kt = 0; kt < kStages && kt < nk; ++kt)
+    dma_step<A_CONTIG, B_CONTIG>(lds + kt * STAGE_ELEMS, ta, kt);
+  wait_steps(min(3, nk - 1));
+  __syncthreads();
+  Frags f0, f1;
+  read_frags<A_CONTIG, B_CONTIG>(f0, lds, wi, wj, lane, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    k_step<A_CONTIG, B_CONTIG>(ta, kt, lds + (kt & 3) * STAGE_ELEMS,
+                               lds + ((kt + 1) & 3) * STAGE_ELEMS, f0, f1, acc, wi, wj, lane);
+  }
+  __syncthreads();  // stages reused by the next tile
 }
 
 // Decode a tile index into (row tile, col tile) walking groups of kGroupM row tiles.
@@ -214,7 +238,7 @@ __device__ inline int logical_block() {
 // Segment table: sCu[rho] (clamped to [0, M_total]) and sStart[rho] = first row tile of rho.
 __device__ inline int build_tiles(const int32_t *cu, int G, int M_total, int *sCu, int *sStart,
                                   bool wgrad) {
-  __shared__ int tmp[4];
+  __shared__ int tmp[kWaves];
   __shared__ int carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   for (int i = tid; i <= G; i += kGemmThreads) sCu[i] = min(max(cu[i], 0), M_total);
@@ -237,7 +261,7 @@ __device__ inline int build_tiles(const int32_t *cu, int G, int M_total, int *sC
     __syncthreads();
     int before = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       before += w < wid ? tmp[w] : 0;
       tot += tmp[w];
     }
@@ -267,7 +291,7 @@ template <int OP>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
     const int32_t *__restrict__ cu, void *__restrict__ out, int G, int M_total, int Kd, int N) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * STAGE_ELEMS];
   __shared__ int sCu[kMaxG + 1], sStart[kMaxG + 1];
   const bool wgrad = OP == MOE_GEMM_WGRAD;
   const int n_rt_total = build_tiles(cu, G, M_total, sCu, sStart, wgrad);
@@ -278,10 +302,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
   const int n_it = (Kd + BM - 1) / BM;
   const long long total = wgrad ? (long long)n_rt_total * n_it * n_ct : (long long)n_rt_total * n_ct;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wi = (wid >> 1) * 128, wj = (wid & 1) * 128;
+  const int wi = (wid / kWavesN) * (32 * TM), wj = (wid % kWavesN) * (32 * TN);
 
   for (long long t = logical_block(); t < total; t += gridDim.x) {
-    f32x16 acc[4][4];
+    f32x16 acc[TM][TN];
     if (!wgrad) {
       int rt, ct;
       swizzle((int)t, n_rt_total, n_ct, &rt, &ct);
@@ -290,21 +314,35 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
       const int rows = min(BM, sCu[rho + 1] - m0);
       const int j0 = ct * BN;
       const uint16_t *w = b + (size_t)rho * Kd * N;
+      TileArgs ta;
+      if (OP == MOE_GEMM_FWD) {
+        ta.ra = make_rsrc(a + (size_t)m0 * Kd, (long long)rows * Kd * 2);
+        ta.lda = Kd;
+        ta.rb = make_rsrc(w + j0, ((long long)Kd * N - j0) * 2);
+        ta.ldb = N;
+        ta.b_rows = N - j0;
+        ta.c_len = Kd;
+      } else {
+        ta.ra = make_rsrc(a + (size_t)m0 * N, (long long)rows * N * 2);
+        ta.lda = N;
+        ta.rb = make_rsrc(w + (size_t)j0 * N, (long long)(Kd - j0) * N * 2);
+        ta.ldb = N;
+        ta.b_rows = Kd - j0;
+        ta.c_len = N;
+      }
+      ta.a_rows = rows;
+      ta.nk = (ta.c_len + BK - 1) / BK;
       if (OP == MOE_GEMM_FWD)
-        tile_mma<true, false>(lds, make_rsrc(a + (size_t)m0 * Kd, (long long)rows * Kd * 2), Kd,
-                              rows, make_rsrc(w + j0, ((long long)Kd * N - j0) * 2), N, N - j0, Kd,
-                              acc);
+        tile_mma<true, false>(lds, ta, acc);
       else
-        tile_mma<true, true>(lds, make_rsrc(a + (size_t)m0 * N, (long long)rows * N * 2), N, rows,
-                             make_rsrc(w + (size_t)j0 * N, (long long)(Kd - j0) * N * 2), N,
-                             Kd - j0, N, acc);
+        tile_mma<true, true>(lds, ta, acc);
       uint16_t *o = (uint16_t *)out + (size_t)m0 * ncols + j0;
 #pragma unroll
-      for (int tm = 0; tm < 4; ++tm) {
+      for (int tm = 0; tm < TM; ++tm) {
         const int i = wi + tm * 32 + (lane & 31);
         if (i >= rows) continue;
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
+        for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int j = wj + tn * 32 + g * 8 + (lane >> 5) * 4;
@@ -325,17 +363,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
       const int rho = find_seg(sStart, G, sidx);
       const int m0 = sCu[rho], len = sCu[rho + 1] - m0;
       const int i0 = it * BM, j0 = ct * BN;
-      tile_mma<false, false>(lds, make_rsrc(a + (size_t)m0 * Kd + i0, ((long long)len * Kd - i0) * 2),
-                             Kd, Kd - i0,
-                             make_rsrc(b + (size_t)m0 * N + j0, ((long long)len * N - j0) * 2), N,
-                             N - j0, len, acc);
+      TileArgs ta;
+      ta.ra = make_rsrc(a + (size_t)m0 * Kd + i0, ((long long)len * Kd - i0) * 2);
+      ta.lda = Kd;
+      ta.a_rows = Kd - i0;
+      ta.rb = make_rsrc(b + (size_t)m0 * N + j0, ((long long)len * N - j0) * 2);
+      ta.ldb = N;
+      ta.b_rows = N - j0;
+      ta.c_len = len;
+      ta.nk = (len + BK - 1) / BK;
+      tile_mma<false, false>(lds, ta, acc);
       float *o = (float *)out + ((size_t)rho * Kd + i0) * N + j0;
 #pragma unroll
-      for (int tm = 0; tm < 4; ++tm) {
+      for (int tm = 0; tm < TM; ++tm) {
         const int i = wi + tm * 32 + (lane & 31);
         if (i0 + i >= Kd) continue;
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
+        for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int j = wj + tn * 32 + g * 8 + (lane >> 5) * 4;
@@ -350,12 +394,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
               *p = v;
             }
           }
+        // at most one row block of read-modify-writes in flight (bounds live registers)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 }
 
-constexpr size_t kGemmLds = 2 * 2 * TILE_ELEMS * sizeof(uint16_t);
 
 // ---------------------------------------------------------------------------------------
 // fp32 vector-ALU path (small shapes)
@@ -447,31 +492,19 @@ extern "C" moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t 
   const int grid = device_cu_count();
   switch (op) {
     case MOE_GEMM_FWD:
-      hipLaunchKernelGGL(k_ggemm_bf16<MOE_GEMM_FWD>, dim3(grid), dim3(kGemmThreads), kGemmLds,
+      hipLaunchKernelGGL(k_ggemm_bf16<MOE_GEMM_FWD>, dim3(grid), dim3(kGemmThreads), 0,
                          stream, (const uint16_t *)a, (const uint16_t *)b, cu_seqlens, out, G,
                          M_total, Kd, N);
       break;
     case MOE_GEMM_DGRAD:
-      hipLaunchKernelGGL(k_ggemm_bf16<MOE_GEMM_DGRAD>, dim3(grid), dim3(kGemmThreads), kGemmLds,
+      hipLaunchKernelGGL(k_ggemm_bf16<MOE_GEMM_DGRAD>, dim3(grid), dim3(kGemmThreads), 0,
                          stream, (const uint16_t *)a, (const uint16_t *)b, cu_seqlens, out, G,
                          M_total, Kd, N);
       break;
     default:
-      hipLaunchKernelGGL(k_ggemm_bf16<MOE_GEMM_WGRAD>, dim3(grid), dim3(kGemmThreads), kGemmLds,
+      hipLaunchKernelGGL(k_ggemm_bf16<MOE_GEMM_WGRAD>, dim3(grid), dim3(kGemmThreads), 0,
                          stream, (const uint16_t *)a, (const uint16_t *)b, cu_seqlens, out, G,
                          M_total, Kd, N);
   }
   return launch_status();
 }
-
-namespace moe {
-// Allow the GEMM kernels their full dynamic LDS; called once per device from api.hip.
-void gemm_set_attributes() {
-  (void)hipFuncSetAttribute((const void *)k_ggemm_bf16<MOE_GEMM_FWD>,
-                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-  (void)hipFuncSetAttribute((const void *)k_ggemm_bf16<MOE_GEMM_DGRAD>,
-                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-  (void)hipFuncSetAttribute((const void *)k_ggemm_bf16<MOE_GEMM_WGRAD>,
-                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-}
-}  // namespace moe
