@@ -1,0 +1,234 @@
+"""Full-size parity: every workload shape, the launch configuration bench.py times.
+
+One forward + backward step of rank 0 runs call by call through the C ABI (via LayerStep).
+Plan, counts, cu_seqlens, dest_pos and src_flat are compared with the oracle bit for bit
+over the whole routing; the dense outputs are checked on sampled rows / tokens / weight
+entries, each recomputed by the oracle from the generated inputs alone (x -> z -> y, dOut ->
+dy -> dz -> dxp): no value the HIP path produced is ever fed to the oracle.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_common import check_close, log
+
+pytestmark = pytest.mark.gpu
+
+
+def host_rows(t, idx):
+    idx = torch.as_tensor(np.asarray(idx, np.int64), device=t.device)
+    r = t[idx]
+    if r.dtype == torch.bfloat16:
+        return r.view(torch.int16).cpu().numpy().view(np.uint16)
+    return r.cpu().numpy()
+
+
+class HostWeights:
+    """Oracle view of a device weight tensor after prefetch: slot row E+j reads expert e."""
+
+    def __init__(self, dev, pl, rank):
+        self.dev = dev
+        se, _, _ = pl.slot_table()
+        self.map = {pl.E + j: int(se[rank, j]) for j in range(pl.B) if se[rank, j] >= 0}
+        self.shape = tuple(dev.shape)
+        self.cache = {}
+
+    def __getitem__(self, rho):
+        rho = int(rho)
+        if rho not in self.cache:
+            self.cache[rho] = host_rows(self.dev, [self.map.get(rho, rho)])[0]
+        return self.cache[rho]
+
+
+def compact_cu(seg, G):
+    counts = np.bincount(np.asarray(seg, np.int64), minlength=G)
+    return np.concatenate([[0], np.cumsum(counts)])
+
+
+WORKLOADS = [("balanced_bf16", None), ("skew1_large", 1.0), ("skew8_large_fwdbwd", 8.0),
+             ("sweep_r64", 16.0), ("sweep_r64", 0.0)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("name,target", WORKLOADS)
+def test_full_size_step(name, target):
+    from balanced_token_dispatch_amd import (GEMM_DGRAD, GEMM_FWD, GEMM_WGRAD, moe_combine,
+                                             moe_dispatch_layout, moe_group_gemm, moe_permute,
+                                             moe_plan, moe_prefetch, moe_replica_grad_fold)
+    from balanced_token_dispatch_amd.layer import LayerStep, Shape
+    wl = synth.WORKLOADS[name]
+    d = wl.dims
+    rank = 0
+    zipf = synth.zipf_for(wl, target)
+    idx, w = synth.routing(d, zipf, wl.base_seed)
+    log(f"full size {name} target={target} maxvio={synth.realised_maxvio(idx, d.E):.3f}")
+    L = LayerStep(Shape(d.R, d.S, d.K, d.E, d.B, d.H, d.Hp), rank=rank)
+    seed = wl.base_seed
+    synth.fill_normal_(L.x_all, 1.0, seed * 10 + 1)
+    synth.fill_normal_(L.w_up, 0.02, seed * 10 + 2)
+    synth.fill_normal_(L.w_down, 0.02, seed * 10 + 3)
+    synth.fill_normal_(L.y_all, 1.0, seed * 10 + 4)
+    synth.fill_normal_(L.dout_all, 1.0, seed * 10 + 5)
+    L.topk_idx.copy_(torch.from_numpy(idx))
+    L.topk_w.copy_(torch.from_numpy(w))
+    SK, S, K, E, B, H, Hp, G = d.SK, d.S, d.K, d.E, d.B, d.H, d.Hp, d.G
+    rng = np.random.default_rng(seed)
+    w_flat = w.reshape(-1)
+
+    # --- plan + layout: bit-exact over the whole routing
+    moe_plan(L.d, L.topk_idx, L.counts, L.plan, L.status, L.ws)
+    moe_dispatch_layout(L.d, rank, L.topk_idx, L.plan, L.cu, L.dest, L.src, L.ws)
+    torch.cuda.synchronize()
+    pl = oracle.plan(idx, E, B)
+    assert pl.status == 0, "no overflow at the workload shapes"
+    assert (L.plan.cpu().numpy() == pl.to_blob()).all()
+    assert (L.counts.cpu().numpy() == pl.counts).all()
+    cu, dest, src = oracle.layout(idx, pl, rank)
+    assert (L.cu.cpu().numpy() == cu).all()
+    assert (L.dest.cpu().numpy() == dest).all()
+    assert (L.src.cpu().numpy() == src).all()
+    assert cu[-1] == SK
+    log(f"  plan+layout exact; replicas={len(pl.replicas)} max/rank={pl.max_needed}")
+
+    # --- prefetch: each used slot row is a bitwise copy of its expert
+    w_up0 = L.w_up.clone() if G * H * Hp * 2 < 12e9 else None
+    moe_prefetch(L.d, rank, L.plan, L.w_up)
+    moe_prefetch(L.d, rank, L.plan, L.w_down)
+    se, _, _ = pl.slot_table()
+    for j in range(B):
+        e = int(se[rank, j])
+        if e >= 0:
+            assert torch.equal(L.w_up[E + j], L.w_up[e]) and torch.equal(L.w_down[E + j], L.w_down[e])
+    if w_up0 is not None:
+        assert torch.equal(L.w_up[:E], w_up0[:E]), "home rows untouched"
+        del w_up0
+
+    Wu, Wd = HostWeights(L.w_up, pl, rank), HostWeights(L.w_down, pl, rank)
+    # sampled buffer rows: the first and last row of every active segment plus random rows,
+    # restricted to a few segments so the oracle fetches few weight rows
+    act = [rho for rho in range(G) if cu[rho + 1] > cu[rho]]
+    pick = sorted(set(rng.choice(act, size=min(3, len(act)), replace=False).tolist())
+                  | {act[-1]})
+    rows = []
+    for rho in pick:
+        lo, hi = int(cu[rho]), int(cu[rho + 1])
+        rows += [lo, hi - 1] + rng.integers(lo, hi, size=4).tolist()
+    rows = np.array(sorted(set(rows)), np.int64)
+    seg = np.searchsorted(cu, rows, side="right") - 1
+    cu_c = compact_cu(seg, G)
+    toks = src[rows] // K
+
+    # --- forward: permute, up, down, combine
+    moe_permute(L.d, L.x_all, L.src, L.xp)
+    moe_group_gemm(GEMM_FWD, L.xp, L.w_up, L.cu, L.z, H, Hp)
+    moe_group_gemm(GEMM_FWD, L.z, L.w_down, L.cu, L.y, Hp, H)
+    moe_combine(L.d, rank, L.y_all, L.dest, L.topk_w.view(-1), L.out)
+    torch.cuda.synchronize()
+    x_rows = host_rows(L.x_all, toks)
+    assert (host_rows(L.xp, rows) == x_rows).all(), "permute rows"
+    _, z_ref = oracle.group_gemm_rows("fwd", x_rows, Wu, cu_c, np.arange(rows.size))
+    check_close(host_rows(L.z, rows), z_ref, "bf16", what="up projection rows")
+    _, y_ref = oracle.group_gemm_rows("fwd", z_ref, Wd, cu_c, np.arange(rows.size))
+    check_close(host_rows(L.y, rows), y_ref, "bf16", what="down projection rows")
+    # combine: tokens whose copies landing on rank 0 are all in the sampled segments
+    tok_s = []
+    for s_ in rng.permutation(S)[:4096]:
+        ds = dest[(rank * S + s_) * K:(rank * S + s_ + 1) * K]
+        mine = ds[(ds >= rank * SK) & (ds < (rank + 1) * SK)] - rank * SK
+        if np.isin(np.searchsorted(cu, mine, side="right") - 1, pick).all():
+            tok_s.append(int(s_))
+        if len(tok_s) == 6:
+            break
+    if len(tok_s) < 2:
+        tok_s = sorted(set(tok_s) | {0, S - 1})
+    need = dest.reshape(d.R, S, K)[rank, tok_s].reshape(-1)
+    y_tab = host_rows(L.y_all, need)          # staged rows of other ranks: generated inputs
+    for k_, dd in enumerate(need):             # rank-0 rows: the oracle's own chain
+        if rank * SK <= dd < (rank + 1) * SK:
+            r_ = dd - rank * SK
+            rho = int(np.searchsorted(cu, r_, side="right") - 1)
+            xr = host_rows(L.x_all, [src[r_] // K])
+            cu1 = compact_cu([rho], G)
+            _, zr = oracle.group_gemm_rows("fwd", xr, Wu, cu1, [0])
+            _, yr = oracle.group_gemm_rows("fwd", zr, Wd, cu1, [0])
+            y_tab[k_] = yr[0]
+    copies = ((rank * S + np.array(tok_s))[:, None] * K + np.arange(K)[None, :]).reshape(-1)
+    dest_l = np.full(dest.size, -1, np.int64)
+    dest_l[copies] = np.arange(copies.size)          # need[i] is the row of copies[i]
+    out_ref = oracle.combine(y_tab, dest_l, w, rank, S, K, "bf16", tokens=tok_s)
+    check_close(host_rows(L.out, tok_s), out_ref, "bf16", what="combine tokens")
+    log("  forward sampled rows within tolerance")
+
+    # --- backward: weighted permute, down dgrad/wgrad, up dgrad/wgrad, fold
+    moe_permute(L.d, L.dout_all, L.src, L.dy, L.topk_w.view(-1))
+    moe_group_gemm(GEMM_DGRAD, L.dy, L.w_down, L.cu, L.dz, Hp, H)
+    L.dw_down.zero_()
+    L.dw_up.zero_()
+    moe_group_gemm(GEMM_WGRAD, L.z, L.dy, L.cu, L.dw_down, Hp, H)
+    moe_group_gemm(GEMM_DGRAD, L.dz, L.w_up, L.cu, L.dxp, H, Hp)
+    moe_group_gemm(GEMM_WGRAD, L.xp, L.dz, L.cu, L.dw_up, H, Hp)
+    torch.cuda.synchronize()
+    g_rows = host_rows(L.dout_all, toks)
+    src_l = (np.arange(rows.size) * K + src[rows] % K).astype(np.int32)   # compact copy ids
+    rs = np.zeros(rows.size * K, np.float32)
+    rs[src_l] = w_flat[src[rows]]
+    dy_ref = oracle.permute(g_rows, src_l, K, row_scale=rs)
+    assert (host_rows(L.dy, rows) == dy_ref).all(), "weighted permute rows"
+    _, dz_ref = oracle.group_gemm_rows("dgrad", dy_ref, Wd, cu_c, np.arange(rows.size))
+    check_close(host_rows(L.dz, rows), dz_ref, "bf16", what="down dgrad rows")
+    _, dxp_ref = oracle.group_gemm_rows("dgrad", dz_ref, Wu, cu_c, np.arange(rows.size))
+    check_close(host_rows(L.dxp, rows), dxp_ref, "bf16", what="up dgrad rows")
+    # wgrad entries of the smallest sampled segment: the oracle recomputes the whole segment
+    rho = min(pick, key=lambda r_: cu[r_ + 1] - cu[r_])
+    lo, hi = int(cu[rho]), int(cu[rho + 1])
+    if hi - lo <= 4096:
+        seg_rows = np.arange(lo, hi)
+        stoks = src[seg_rows] // K
+        xs = host_rows(L.x_all, stoks)
+        cu1 = np.array([0] * (rho + 1) + [hi - lo] * (G - rho), np.int64)
+        _, zs = oracle.group_gemm_rows("fwd", xs, Wu, cu1, np.arange(hi - lo))
+        gs = host_rows(L.dout_all, stoks)
+        wsc = w_flat[src[seg_rows]]
+        dys = oracle.permute(gs, (np.arange(hi - lo) * K).astype(np.int32), K,
+                             row_scale=np.repeat(wsc, K).astype(np.float32))
+        _, dzs = oracle.group_gemm_rows("dgrad", dys, Wd, cu1, np.arange(hi - lo))
+        ii = rng.integers(0, Hp, 6)
+        jj = rng.integers(0, H, 6)
+        cu2 = np.array([0, hi - lo])
+        ent = oracle.wgrad_entries(zs, dys, cu2, 0, ii, jj, "bf16")
+        got = L.dw_down[rho][torch.as_tensor(ii, device="cuda"),
+                             torch.as_tensor(jj, device="cuda")].cpu().numpy()
+        assert np.abs(got - ent).max() <= 1e-3 * max(1.0, np.abs(ent).max()), (got, ent)
+        ii2 = rng.integers(0, H, 6)
+        jj2 = rng.integers(0, Hp, 6)
+        ent2 = oracle.wgrad_entries(xs, dzs, cu2, 0, ii2, jj2, "bf16")
+        got2 = L.dw_up[rho][torch.as_tensor(ii2, device="cuda"),
+                            torch.as_tensor(jj2, device="cuda")].cpu().numpy()
+        assert np.abs(got2 - ent2).max() <= 1e-3 * max(1.0, np.abs(ent2).max()), (got2, ent2)
+        log(f"  wgrad entries of segment {rho} ({hi - lo} rows) within tolerance")
+    # fold: home rows gain the slot rows, slot rows end zero (bitwise, on a sampled column block)
+    cols = slice(0, 4096)
+    before = {int(e): (L.dw_up[e].view(-1)[cols].cpu().numpy(),
+                       L.dw_up[E + j].view(-1)[cols].cpu().numpy())
+              for j, e in enumerate(se[rank]) if e >= 0}
+    moe_replica_grad_fold(L.d, rank, L.plan, L.dw_up)
+    torch.cuda.synchronize()
+    for j, e in enumerate(se[rank]):
+        if e < 0:
+            continue
+        h0, s0 = before[int(e)]
+        assert (L.dw_up[e].view(-1)[cols].cpu().numpy() == h0 + s0).all()
+        assert not L.dw_up[E + j].any()
+    log(f"  backward sampled rows within tolerance; folded {len(before)} slot rows")
+    del L
+    gc.collect()
+    torch.cuda.empty_cache()
