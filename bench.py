@@ -54,6 +54,81 @@ class EventTimer:
         return {k: [s.elapsed_time(e) for s, e in v] for k, v in self.events.items()}
 
 
+KERNEL_SOURCES = {  # bench kernel name -> (rocprof name prefix, source files that define it)
+    "gemm_fwd": ("moe::k_ggemm_bf16<0>", ("group_gemm.hip", "common.hpp")),
+    "gemm_dgrad": ("moe::k_ggemm_bf16<1>", ("group_gemm.hip", "common.hpp")),
+    "gemm_wgrad": ("moe::k_ggemm_bf16<2>", ("group_gemm.hip", "common.hpp")),
+    "permute": ("moe::k_permute<false>", ("rows.hip", "common.hpp")),
+    "permute_weighted": ("moe::k_permute<true>", ("rows.hip", "common.hpp")),
+    "combine": ("moe::k_combine<true>", ("rows.hip", "common.hpp")),
+    "fold": ("moe::k_fold", ("rows.hip", "common.hpp")),
+    "prefetch": ("moe::k_prefetch", ("rows.hip", "common.hpp")),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_skew8_fwdbwd.md")
+COPY_BYTES = 1 << 30          # calibration copy: reads and writes exactly this many bytes
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel][1]:
+        with open(os.path.join(ROOT, "balanced_token_dispatch_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if still current."""
+    import re
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"\| `(\w+)` \| ([0-9a-f]{16}) \| ([0-9.]+) \| ([0-9.]+) \| ([0-9.]+) \|", line)
+        if m and m.group(1) == kernel and m.group(2) == source_hash(kernel):
+            return float(m.group(5)) * 1e6
+    return None
+
+
+def render_traffic(fetch_csv, write_csv):
+    """Summarise two rocprofv3 --pmc runs of `bench.py --probe` (FETCH_SIZE, WRITE_SIZE)."""
+    import csv
+    import collections
+
+    def per_dispatch(path, counter):
+        vals = collections.defaultdict(float)
+        names = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        return vals, names
+
+    out = []
+    f_vals, names = per_dispatch(fetch_csv, "FETCH_SIZE")
+    w_vals, _ = per_dispatch(write_csv, "WRITE_SIZE")
+    # the calibration copy is the torch copy kernel dispatched right before the probed step
+    copies = [d for d, n in names.items() if "copy" in n.lower() and "moe::" not in n]
+    big = max(copies, key=lambda d: f_vals[d])
+    kf = COPY_BYTES / (f_vals[big] * 1024.0)
+    kw = COPY_BYTES / (w_vals[big] * 1024.0)
+    out.append(f"calibration copy ({COPY_BYTES} B read + written): FETCH_SIZE "
+               f"{f_vals[big]:.0f} KiB, WRITE_SIZE {w_vals[big]:.0f} KiB -> scale "
+               f"fetch x{kf:.4f}, write x{kw:.4f}")
+    out.append("")
+    out.append("| kernel | source sha256[:16] | fetch MB/launch | write MB/launch | traffic MB/launch |")
+    out.append("|---|---|---|---|---|")
+    for k, (prefix, _) in KERNEL_SOURCES.items():
+        ds = [d for d, n in names.items() if n.startswith(prefix) or n.startswith("void " + prefix)]
+        if not ds:
+            continue
+        ds = sorted(ds, key=int)[len(ds) // 2:]  # the probed step's launches (after the warm-up step)
+        fb = sum(f_vals[d] for d in ds) / len(ds) * 1024 * kf / 1e6
+        wb = sum(w_vals[d] for d in ds) / len(ds) * 1024 * kw / 1e6
+        out.append(f"| `{k}` | {source_hash(k)} | {fb:.1f} | {wb:.1f} | {fb + wb:.1f} |")
+    print("\n".join(out))
+
+
 def algorithmic_work(shape, n_slots_used):
     """Minimum bytes (or flops) per launch of each kernel of the step."""
     R, S, K, E, H, Hp = shape.R, shape.S, shape.K, shape.E, shape.H, shape.Hp
@@ -222,7 +297,13 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32768)
     ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--probe", action="store_true",
+                    help="one warm-up step, a 1 GiB calibration copy, one step (for --pmc runs)")
+    ap.add_argument("--render-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.render_traffic:
+        render_traffic(*args.render_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures the one-GPU share of one rank; --gpus {args.gpus} "
@@ -239,6 +320,17 @@ def main():
     target = wl.maxvio_targets[-1] if wl.maxvio_targets[-1] is not None else None
     layer, idx, w, info = setup_layer(wl, target, args.rank)
     s = layer.s
+    if args.probe:
+        layer.step()
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        layer.step()
+        torch.cuda.synchronize()
+        log("probe done")
+        return
     timer = EventTimer()
     elapsed = run_steps(layer, args.steps, args.warmup, timer)
     status = int(layer.status.item())
@@ -278,7 +370,10 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(amount / (avg * 1e-3) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    tr = recorded_traffic(dom)
+    roof["traffic"] = None if tr is None else round(tr / 1e6, 1)
+    if tr is not None:
+        roof["traffic_unit"] = "MB per launch (HBM, FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
     log(f"main: {ms_step:.3f} ms/step, {value:.0f} tokens/s, status {status}, slots used {n_slots}")
 
     sweep = {}
