@@ -126,14 +126,6 @@ __device__ inline void waitcnt_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// Wait until at most `steps` K steps of loads (the newest) are still in flight.
-__device__ inline void wait_steps(int steps) {
-  if (steps >= 3) waitcnt_vm<3 * kLoadsPerStep>();
-  else if (steps == 2) waitcnt_vm<2 * kLoadsPerStep>();
-  else if (steps == 1) waitcnt_vm<kLoadsPerStep>();
-  else waitcnt_vm<0>();
-}
-
 struct Frags {
   bf16x8 a[TM], b[TN];
 };
@@ -166,13 +158,17 @@ __device__ inline void dma_step(uint16_t *dst, const TileArgs &ta, int kt) {
   dma_tile<B_CONTIG>(dst + OP_ELEMS, ta.rb, ta.ldb, ta.b_rows, kt * BK, ta.c_len);
 }
 
-// K step kt: `cur` holds step kt, `nxt` step kt+1.  Saying the two are distinct
-// (restrict) lets the compiler see that the direct-to-LDS loads issued into `cur` cannot
-// feed the fragment reads of `nxt`, so it adds no wait for them; the waits that order
-// the stages are the explicit ones below.  Per step: read the second sub-step's fragments
-// of `cur`, MFMAs of the first sub-step, wait for step kt+1's loads and barrier (every
-// wave has now finished reading `cur`), read step kt+1's first fragments, start step
-// kt+4's loads into `cur`, MFMAs of the second sub-step.  Loads are three steps ahead.
+// Steady K step kt (kt + 1 < nk): `cur` holds step kt, `nxt` step kt+1.  Saying the two
+// are distinct (restrict) lets the compiler see that the direct-to-LDS loads issued into
+// `cur` cannot feed the fragment reads of `nxt`, so it adds no wait for them; the waits
+// that order the stages are the explicit ones below.  Per step: read the second sub-step's
+// fragments of `cur`, MFMAs of the first sub-step, wait for step kt+1's loads (steps kt+2
+// and kt+3 may stay in flight) and barrier (every wave has now finished reading `cur`),
+// read step kt+1's first fragments, start step kt+4's loads into `cur`, MFMAs of the second
+// sub-step.  The step has no branch: loads past the last K step have every offset out of
+// range and write zeros into a stage no later step reads, so the wait count is constant
+// and the compiler's LDS-wait bookkeeping stays exact (a join point here made it wait for
+// the next step's fragment reads before the second MFMA burst).
 template <bool A_CONTIG, bool B_CONTIG>
 __device__ __attribute__((always_inline)) inline void k_step(
     const TileArgs &ta, int kt, uint16_t *__restrict__ cur, const uint16_t *__restrict__ nxt,
@@ -181,12 +177,10 @@ __device__ __attribute__((always_inline)) inline void k_step(
   __builtin_amdgcn_sched_barrier(0);
   mma16(acc, f0);
   __builtin_amdgcn_sched_barrier(0);
-  if (kt + 1 < ta.nk) {
-    wait_steps(min(2, ta.nk - 2 - kt));
-    __syncthreads();
-    read_frags<A_CONTIG, B_CONTIG>(f0, nxt, wi, wj, lane, 0);
-    if (kt + 4 < ta.nk) dma_step<A_CONTIG, B_CONTIG>(cur, ta, kt + 4);
-  }
+  waitcnt_vm<2 * kLoadsPerStep>();
+  __syncthreads();
+  read_frags<A_CONTIG, B_CONTIG>(f0, nxt, wi, wj, lane, 0);
+  dma_step<A_CONTIG, B_CONTIG>(cur, ta, kt + 4);
   __builtin_amdgcn_sched_barrier(0);
   mma16(acc, f1);
   __builtin_amdgcn_sched_barrier(0);
@@ -205,17 +199,22 @@ __device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta, f32x16 (&acc)
 #pragma unroll
     for (int b = 0; b < TN; ++b) acc[a][b] = (f32x16){};
 
-  for (int kt = 0; kt < kStages && kt < nk; ++kt)
-    dma_step<A_CONTIG, B_CONTIG>(lds + kt * STAGE_ELEMS, ta, kt);
-  wait_steps(min(3, nk - 1));
+#pragma unroll
+  for (int kt = 0; kt < kStages; ++kt) dma_step<A_CONTIG, B_CONTIG>(lds + kt * STAGE_ELEMS, ta, kt);
+  waitcnt_vm<(kStages - 1) * kLoadsPerStep>();
   __syncthreads();
   Frags f0, f1;
   read_frags<A_CONTIG, B_CONTIG>(f0, lds, wi, wj, lane, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt + 1 < nk; ++kt) {
     k_step<A_CONTIG, B_CONTIG>(ta, kt, lds + (kt & 3) * STAGE_ELEMS,
                                lds + ((kt + 1) & 3) * STAGE_ELEMS, f0, f1, acc, wi, wj, lane);
   }
-  __syncthreads();  // stages reused by the next tile
+  // last K step: no next step to prepare
+  read_frags<A_CONTIG, B_CONTIG>(f1, lds + ((nk - 1) & 3) * STAGE_ELEMS, wi, wj, lane, 1);
+  mma16(acc, f0);
+  mma16(acc, f1);
+  waitcnt_vm<0>();  // the trailing out-of-range loads land before the stages are reused
+  __syncthreads();
 }
 
 // Decode a tile index into (row tile, col tile) walking groups of kGroupM row tiles.

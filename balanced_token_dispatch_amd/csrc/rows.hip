@@ -1,7 +1,11 @@
 // Row-streaming kernels: gather-permute, weighted combine, replica-gradient
-// fold and slot prefetch.  All are HBM-bound; each moves whole rows with
-// 16-byte vector loads/stores, one wavefront per row, several rows in flight
-// per lane.
+// fold and slot prefetch.  All are HBM-bound and move whole rows with 16-byte
+// vector loads/stores.  Every kernel is launched one-shot: a block owns one
+// row (or one 16 KB chunk of a long row) and exits, so the hardware
+// dispatcher keeps every CU saturated with fresh loads; a persistent
+// grid-stride loop over rows measured 10-15 points of HBM peak slower on
+// gfx950.  Both grid axes are clamped and the kernels stride past the clamp,
+// so any row count or width is covered.
 //
 // Pages: moses-y.github.io "MoonEP", "What This Does" and "Real-World Use";
 // findrepo.work "MoonEP" card, "Strengths" (fused permute / unpermute);
@@ -11,8 +15,12 @@
 
 namespace moe {
 
-constexpr int kRowThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kRowThreads = 256;      // combine / fold / prefetch blocks
+constexpr int kPermMaxThreads = 1024; // permute: one block spans a whole row
+constexpr int kCombU = 4;             // vectors per thread per combine block
+constexpr int kStreamU = 4;           // vectors per thread per fold / prefetch block
+constexpr int kMaxGridX = 1 << 20;
+constexpr int kMaxGridY = 65535;
 
 __device__ inline u32x4 scale_row16(u32x4 v, float w, bool bf16) {
   if (bf16) {
@@ -26,56 +34,70 @@ __device__ inline u32x4 scale_row16(u32x4 v, float w, bool bf16) {
   return __builtin_bit_cast(u32x4, f);
 }
 
-// xp[i] = x_all[src_flat[i] / K] (optionally * row_scale[src]); one wave per row.
+// xp[i] = x_all[src_flat[i] / K] (optionally * row_scale[src]).  grid (rows, chunks),
+// block = one chunk of up to kPermMaxThreads vectors, one vector per thread.
 template <bool SCALED>
-__global__ __launch_bounds__(kRowThreads) void k_permute(const u32x4 *__restrict__ x_all,
-                                                        const int32_t *__restrict__ src_flat,
-                                                        const float *__restrict__ scale,
-                                                        u32x4 *__restrict__ xp, int SK, int K,
-                                                        int vec_per_row, int bf16) {
-  const int lane = threadIdx.x & 63;
-  const int wave = (blockIdx.x * kRowThreads + threadIdx.x) >> 6;
-  const int nwaves = (gridDim.x * kRowThreads) >> 6;
-  for (int i = wave; i < SK; i += nwaves) {
+__global__ __launch_bounds__(kPermMaxThreads) void k_permute(const u32x4 *__restrict__ x_all,
+                                                            const int32_t *__restrict__ src_flat,
+                                                            const float *__restrict__ scale,
+                                                            u32x4 *__restrict__ xp, int SK, int K,
+                                                            int vec_per_row, int bf16) {
+  for (int i = blockIdx.x; i < SK; i += gridDim.x) {
     const int src = src_flat[i];
+    const float w = (SCALED && src >= 0) ? scale[src] : 1.0f;
+    const u32x4 *row = x_all + (size_t)(src < 0 ? 0 : src / K) * vec_per_row;
     u32x4 *dst = xp + (size_t)i * vec_per_row;
-    if (src < 0) {
-      for (int v = lane; v < vec_per_row; v += kWave) dst[v] = (u32x4){0, 0, 0, 0};
-      continue;
-    }
-    const u32x4 *row = x_all + (size_t)(src / K) * vec_per_row;
-    const float w = SCALED ? scale[src] : 1.0f;
-    int v = lane;
-    for (; v + (kUnroll - 1) * kWave < vec_per_row; v += kUnroll * kWave) {
-      u32x4 t[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) t[u] = __builtin_nontemporal_load(row + v + u * kWave);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const u32x4 o = SCALED ? scale_row16(t[u], w, bf16) : t[u];
-        __builtin_nontemporal_store(o, dst + v + u * kWave);
+    for (int v = blockIdx.y * blockDim.x + threadIdx.x; v < vec_per_row;
+         v += gridDim.y * blockDim.x) {
+      u32x4 t = (u32x4){0, 0, 0, 0};
+      if (src >= 0) {
+        t = row[v];
+        if (SCALED) t = scale_row16(t, w, bf16);
       }
-    }
-    for (; v < vec_per_row; v += kWave) {
-      const u32x4 t = __builtin_nontemporal_load(row + v);
-      __builtin_nontemporal_store(SCALED ? scale_row16(t, w, bf16) : t, dst + v);
+      __builtin_nontemporal_store(t, dst + v);
     }
   }
 }
 
 constexpr int kMaxKUnrolled = 16;
 
-// out[s] = sum_k w[c] * y_all[dest_pos[c]], c = (rank*S + s)*K + k; one wave per token.
+template <bool BF16>
+__device__ inline void fma_row16(float (&acc)[8], float w, u32x4 t) {
+  if (BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = __builtin_fmaf(w, bf16_lo(t[q]), acc[2 * q]);
+      acc[2 * q + 1] = __builtin_fmaf(w, bf16_hi(t[q]), acc[2 * q + 1]);
+    }
+  } else {
+    const f32x4 f = __builtin_bit_cast(f32x4, t);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(w, f[q], acc[q]);
+  }
+}
+
+template <bool BF16>
+__device__ inline u32x4 round_row16(const float (&acc)[8]) {
+  u32x4 r;
+  if (BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+  } else {
+    r = __builtin_bit_cast(u32x4, (f32x4){acc[0], acc[1], acc[2], acc[3]});
+  }
+  return r;
+}
+
+// out[s] = sum_k w[c] * y_all[dest_pos[c]], c = (rank*S + s)*K + k.  grid (tokens, chunks);
+// a block covers kRowThreads*kCombU vectors of one token, all K source rows in flight.
 template <bool BF16>
 __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict__ y_all,
                                                         const int32_t *__restrict__ dest_pos,
                                                         const float *__restrict__ topk_w,
                                                         u32x4 *__restrict__ out, int S, int K,
                                                         int rank, int vec_per_row) {
-  const int lane = threadIdx.x & 63;
-  const int wave = (blockIdx.x * kRowThreads + threadIdx.x) >> 6;
-  const int nwaves = (gridDim.x * kRowThreads) >> 6;
-  for (int s = wave; s < S; s += nwaves) {
+  constexpr int kChunk = kRowThreads * kCombU;
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
     const size_t c0 = ((size_t)rank * S + s) * K;
     int dst[kMaxKUnrolled];
     float wt[kMaxKUnrolled];
@@ -85,129 +107,115 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict
       wt[k] = (k < K) ? topk_w[c0 + k] : 0.0f;
     }
     u32x4 *o = out + (size_t)s * vec_per_row;
-    for (int v = lane; v < vec_per_row; v += kWave) {
-      u32x4 t[kMaxKUnrolled];
+    for (int base = blockIdx.y * kChunk; base < vec_per_row; base += gridDim.y * kChunk) {
 #pragma unroll
-      for (int k = 0; k < kMaxKUnrolled; ++k)
-        if (dst[k] >= 0) t[k] = y_all[(size_t)dst[k] * vec_per_row + v];
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int u = 0; u < kCombU; ++u) {
+        const int v = base + u * kRowThreads + threadIdx.x;
+        if (v >= vec_per_row) break;
+        u32x4 t[kMaxKUnrolled];
 #pragma unroll
-      for (int k = 0; k < kMaxKUnrolled; ++k) {
-        if (dst[k] < 0) continue;
-        if (BF16) {
+        for (int k = 0; k < kMaxKUnrolled; ++k)
+          if (dst[k] >= 0) t[k] = __builtin_nontemporal_load(y_all + (size_t)dst[k] * vec_per_row + v);
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[2 * q] = __builtin_fmaf(wt[k], bf16_lo(t[k][q]), acc[2 * q]);
-            acc[2 * q + 1] = __builtin_fmaf(wt[k], bf16_hi(t[k][q]), acc[2 * q + 1]);
-          }
-        } else {
-          const f32x4 f = __builtin_bit_cast(f32x4, t[k]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(wt[k], f[q], acc[q]);
-        }
+        for (int k = 0; k < kMaxKUnrolled; ++k)
+          if (dst[k] >= 0) fma_row16<BF16>(acc, wt[k], t[k]);
+        __builtin_nontemporal_store(round_row16<BF16>(acc), o + v);
       }
-      u32x4 r;
-      if (BF16) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-      } else {
-        r = __builtin_bit_cast(u32x4, (f32x4){acc[0], acc[1], acc[2], acc[3]});
-      }
-      __builtin_nontemporal_store(r, o + v);
     }
   }
 }
 
-// Generic-K combine for K > kMaxKUnrolled: same arithmetic, loads one k at a time.
+// Generic-K combine for K > kMaxKUnrolled: same arithmetic and order, one k at a time.
 template <bool BF16>
 __global__ __launch_bounds__(kRowThreads) void k_combine_anyk(const u32x4 *__restrict__ y_all,
                                                              const int32_t *__restrict__ dest_pos,
                                                              const float *__restrict__ topk_w,
                                                              u32x4 *__restrict__ out, int S,
                                                              int K, int rank, int vec_per_row) {
-  const int lane = threadIdx.x & 63;
-  const int wave = (blockIdx.x * kRowThreads + threadIdx.x) >> 6;
-  const int nwaves = (gridDim.x * kRowThreads) >> 6;
-  for (int s = wave; s < S; s += nwaves) {
+  constexpr int kChunk = kRowThreads * kCombU;
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
     const size_t c0 = ((size_t)rank * S + s) * K;
     u32x4 *o = out + (size_t)s * vec_per_row;
-    for (int v = lane; v < vec_per_row; v += kWave) {
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int k = 0; k < K; ++k) {
-        const int d = dest_pos[c0 + k];
-        if (d < 0) continue;
-        const float w = topk_w[c0 + k];
-        const u32x4 t = y_all[(size_t)d * vec_per_row + v];
-        if (BF16) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[2 * q] = __builtin_fmaf(w, bf16_lo(t[q]), acc[2 * q]);
-            acc[2 * q + 1] = __builtin_fmaf(w, bf16_hi(t[q]), acc[2 * q + 1]);
-          }
-        } else {
-          const f32x4 f = __builtin_bit_cast(f32x4, t);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(w, f[q], acc[q]);
+    for (int base = blockIdx.y * kChunk; base < vec_per_row; base += gridDim.y * kChunk) {
+      for (int u = 0; u < kCombU; ++u) {
+        const int v = base + u * kRowThreads + threadIdx.x;
+        if (v >= vec_per_row) break;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int k = 0; k < K; ++k) {
+          const int d = dest_pos[c0 + k];
+          if (d < 0) continue;
+          fma_row16<BF16>(acc, topk_w[c0 + k], y_all[(size_t)d * vec_per_row + v]);
         }
+        o[v] = round_row16<BF16>(acc);
       }
-      u32x4 r;
-      if (BF16) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-      } else {
-        r = __builtin_bit_cast(u32x4, (f32x4){acc[0], acc[1], acc[2], acc[3]});
-      }
-      o[v] = r;
     }
   }
 }
 
-// dw[e] += dw[E+j]; dw[E+j] = 0 for every used slot j of `rank`.  grid (blocks, B).
+// dw[e] += dw[E+j]; dw[E+j] = 0 for every used slot j of `rank`.  grid (chunks, B);
+// a block covers kRowThreads*kStreamU vectors of one slot row.
 __global__ __launch_bounds__(kRowThreads) void k_fold(const int32_t *__restrict__ plan,
                                                      f32x4 *__restrict__ dw, int E, int R, int B,
                                                      int rank, long long vec_per_row) {
+  constexpr int kChunk = kRowThreads * kStreamU;
   const PlanLayout L(E, R, B);
   const int j = blockIdx.y;
   const int e = plan[L.off_sexp + rank * B + j];
   if (e < 0) return;
   f32x4 *home = dw + (size_t)e * vec_per_row;
   f32x4 *slot = dw + (size_t)(E + j) * vec_per_row;
-  const long long stride = (long long)gridDim.x * kRowThreads;
-  long long v = (long long)blockIdx.x * kRowThreads + threadIdx.x;
-  for (; v + stride < vec_per_row; v += 2 * stride) {
-    const f32x4 a0 = home[v], b0 = __builtin_nontemporal_load(slot + v);
-    const f32x4 a1 = home[v + stride], b1 = __builtin_nontemporal_load(slot + v + stride);
-    home[v] = a0 + b0;
-    home[v + stride] = a1 + b1;
-    __builtin_nontemporal_store((f32x4){0, 0, 0, 0}, slot + v);
-    __builtin_nontemporal_store((f32x4){0, 0, 0, 0}, slot + v + stride);
-  }
-  for (; v < vec_per_row; v += stride) {
-    home[v] = home[v] + slot[v];
-    slot[v] = (f32x4){0, 0, 0, 0};
+  for (long long base = (long long)blockIdx.x * kChunk; base < vec_per_row;
+       base += (long long)gridDim.x * kChunk) {
+    f32x4 a[kStreamU], b[kStreamU];
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+      const long long v = base + u * kRowThreads + threadIdx.x;
+      if (v < vec_per_row) {
+        a[u] = home[v];
+        b[u] = __builtin_nontemporal_load(slot + v);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+      const long long v = base + u * kRowThreads + threadIdx.x;
+      if (v < vec_per_row) {
+        home[v] = a[u] + b[u];
+        __builtin_nontemporal_store((f32x4){0, 0, 0, 0}, slot + v);
+      }
+    }
   }
 }
 
-// w[E+j] = w[e] for every used slot j of `rank`.  grid (blocks, B).
+// w[E+j] = w[e] for every used slot j of `rank`.  grid (chunks, B).
 __global__ __launch_bounds__(kRowThreads) void k_prefetch(const int32_t *__restrict__ plan,
                                                          u32x4 *__restrict__ w, int E, int R,
                                                          int B, int rank, long long vec_per_row) {
+  constexpr int kChunk = kRowThreads * kStreamU;
   const PlanLayout L(E, R, B);
   const int j = blockIdx.y;
   const int e = plan[L.off_sexp + rank * B + j];
   if (e < 0) return;
   const u32x4 *src = w + (size_t)e * vec_per_row;
   u32x4 *dst = w + (size_t)(E + j) * vec_per_row;
-  const long long stride = (long long)gridDim.x * kRowThreads;
-  for (long long v = (long long)blockIdx.x * kRowThreads + threadIdx.x; v < vec_per_row;
-       v += stride)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(src + v), dst + v);
+  for (long long base = (long long)blockIdx.x * kChunk; base < vec_per_row;
+       base += (long long)gridDim.x * kChunk) {
+    u32x4 t[kStreamU];
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+      const long long v = base + u * kRowThreads + threadIdx.x;
+      if (v < vec_per_row) t[u] = __builtin_nontemporal_load(src + v);
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+      const long long v = base + u * kRowThreads + threadIdx.x;
+      if (v < vec_per_row) __builtin_nontemporal_store(t[u], dst + v);
+    }
+  }
 }
 
-static int row_grid(long long rows, int waves_per_block = kRowThreads / kWave) {
-  const long long want = (rows + waves_per_block - 1) / waves_per_block;
-  const long long cap = (long long)device_cu_count() * 16;
-  return (int)(want < cap ? (want < 1 ? 1 : want) : cap);
+static unsigned clamp_grid(long long want, long long cap) {
+  return (unsigned)(want < 1 ? 1 : (want < cap ? want : cap));
 }
 
 }  // namespace moe
@@ -221,18 +229,20 @@ extern "C" moe_status_t moe_permute(const moe_dims *d, moe_dtype dtype, int64_t 
                                     const float *row_scale, void *xp, hipStream_t stream) {
   if (!dims_ok(d) || !x_all || !src_flat || !xp) return MOE_EINVAL;
   const int eb = elem_bytes(dtype);
-  if (!eb || width <= 0 || (width * eb) % 16 != 0) return MOE_EINVAL;
+  if (!eb || width <= 0 || (width * eb) % 16 != 0 || width * eb / 16 > INT32_MAX) return MOE_EINVAL;
   const int SK = d->S * d->K;
   const int vec = (int)(width * eb / 16);
-  const int grid = row_grid(SK);
+  // One block per row chunk; the block is as wide as the row (rounded to a wave) up to
+  // kPermMaxThreads, one 16-byte vector per thread.
+  const int threads = (int)(vec < kPermMaxThreads ? ((vec + kWave - 1) / kWave) * kWave
+                                                  : kPermMaxThreads);
+  const dim3 grid(clamp_grid(SK, kMaxGridX), clamp_grid(ceil_div(vec, threads), kMaxGridY));
   if (row_scale)
-    hipLaunchKernelGGL(k_permute<true>, dim3(grid), dim3(kRowThreads), 0, stream,
-                       (const u32x4 *)x_all, src_flat, row_scale, (u32x4 *)xp, SK, d->K, vec,
-                       dtype == MOE_BF16);
+    hipLaunchKernelGGL(k_permute<true>, grid, dim3(threads), 0, stream, (const u32x4 *)x_all,
+                       src_flat, row_scale, (u32x4 *)xp, SK, d->K, vec, dtype == MOE_BF16);
   else
-    hipLaunchKernelGGL(k_permute<false>, dim3(grid), dim3(kRowThreads), 0, stream,
-                       (const u32x4 *)x_all, src_flat, row_scale, (u32x4 *)xp, SK, d->K, vec,
-                       dtype == MOE_BF16);
+    hipLaunchKernelGGL(k_permute<false>, grid, dim3(threads), 0, stream, (const u32x4 *)x_all,
+                       src_flat, row_scale, (u32x4 *)xp, SK, d->K, vec, dtype == MOE_BF16);
   return launch_status();
 }
 
@@ -242,26 +252,27 @@ extern "C" moe_status_t moe_combine(const moe_dims *d, moe_dtype dtype, int64_t 
   if (!dims_ok(d) || !y_all || !dest_pos || !topk_w || !out) return MOE_EINVAL;
   if (rank < 0 || rank >= d->R) return MOE_EINVAL;
   const int eb = elem_bytes(dtype);
-  if (!eb || width <= 0 || (width * eb) % 16 != 0) return MOE_EINVAL;
+  if (!eb || width <= 0 || (width * eb) % 16 != 0 || width * eb / 16 > INT32_MAX) return MOE_EINVAL;
   const int vec = (int)(width * eb / 16);
-  const int grid = row_grid(d->S);
+  const dim3 grid(clamp_grid(d->S, kMaxGridX),
+                  clamp_grid(ceil_div(vec, kRowThreads * kCombU), kMaxGridY));
   const bool bf = dtype == MOE_BF16;
   if (d->K <= kMaxKUnrolled) {
     if (bf)
-      hipLaunchKernelGGL(k_combine<true>, dim3(grid), dim3(kRowThreads), 0, stream,
+      hipLaunchKernelGGL(k_combine<true>, grid, dim3(kRowThreads), 0, stream,
                          (const u32x4 *)y_all, dest_pos, topk_w, (u32x4 *)out, d->S, d->K, rank,
                          vec);
     else
-      hipLaunchKernelGGL(k_combine<false>, dim3(grid), dim3(kRowThreads), 0, stream,
+      hipLaunchKernelGGL(k_combine<false>, grid, dim3(kRowThreads), 0, stream,
                          (const u32x4 *)y_all, dest_pos, topk_w, (u32x4 *)out, d->S, d->K, rank,
                          vec);
   } else {
     if (bf)
-      hipLaunchKernelGGL(k_combine_anyk<true>, dim3(grid), dim3(kRowThreads), 0, stream,
+      hipLaunchKernelGGL(k_combine_anyk<true>, grid, dim3(kRowThreads), 0, stream,
                          (const u32x4 *)y_all, dest_pos, topk_w, (u32x4 *)out, d->S, d->K, rank,
                          vec);
     else
-      hipLaunchKernelGGL(k_combine_anyk<false>, dim3(grid), dim3(kRowThreads), 0, stream,
+      hipLaunchKernelGGL(k_combine_anyk<false>, grid, dim3(kRowThreads), 0, stream,
                          (const u32x4 *)y_all, dest_pos, topk_w, (u32x4 *)out, d->S, d->K, rank,
                          vec);
   }
@@ -275,11 +286,11 @@ extern "C" moe_status_t moe_replica_grad_fold(const moe_dims *d, int32_t rank,
   if (rank < 0 || rank >= d->R) return MOE_EINVAL;
   if (d->B == 0) return MOE_OK;
   const long long vec = row_elems / 4;
-  long long bx = (vec + kRowThreads * 2 - 1) / (kRowThreads * 2);
-  const long long cap = (long long)device_cu_count() * 8;
-  if (bx > cap) bx = cap;
-  hipLaunchKernelGGL(k_fold, dim3((unsigned)bx, d->B), dim3(kRowThreads), 0, stream, plan,
-                     (f32x4 *)dw, d->E, d->R, d->B, rank, vec);
+  const dim3 grid(clamp_grid((vec + kRowThreads * kStreamU - 1) / (kRowThreads * kStreamU),
+                             kMaxGridX),
+                  d->B);
+  hipLaunchKernelGGL(k_fold, grid, dim3(kRowThreads), 0, stream, plan, (f32x4 *)dw, d->E, d->R,
+                     d->B, rank, vec);
   return launch_status();
 }
 
@@ -289,10 +300,10 @@ extern "C" moe_status_t moe_prefetch(const moe_dims *d, int32_t rank, const int3
   if (rank < 0 || rank >= d->R) return MOE_EINVAL;
   if (d->B == 0) return MOE_OK;
   const long long vec = row_bytes / 16;
-  long long bx = (vec + kRowThreads - 1) / kRowThreads;
-  const long long cap = (long long)device_cu_count() * 8;
-  if (bx > cap) bx = cap;
-  hipLaunchKernelGGL(k_prefetch, dim3((unsigned)bx, d->B), dim3(kRowThreads), 0, stream, plan,
-                     (u32x4 *)w, d->E, d->R, d->B, rank, vec);
+  const dim3 grid(clamp_grid((vec + kRowThreads * kStreamU - 1) / (kRowThreads * kStreamU),
+                             kMaxGridX),
+                  d->B);
+  hipLaunchKernelGGL(k_prefetch, grid, dim3(kRowThreads), 0, stream, plan, (u32x4 *)w, d->E,
+                     d->R, d->B, rank, vec);
   return launch_status();
 }

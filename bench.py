@@ -371,9 +371,9 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     tr = recorded_traffic(dom)
-    roof["traffic"] = None if tr is None else round(tr / 1e6, 1)
+    roof["traffic"] = None if tr is None else int(tr)
     if tr is not None:
-        roof["traffic_unit"] = "MB per launch (HBM, FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
+        roof["traffic_unit"] = "bytes per launch (HBM, FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
     log(f"main: {ms_step:.3f} ms/step, {value:.0f} tokens/s, status {status}, slots used {n_slots}")
 
     sweep = {}
