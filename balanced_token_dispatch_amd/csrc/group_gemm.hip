@@ -7,19 +7,21 @@
 // (experts are addressed by row index, so the tensor must be contiguous).
 //
 // bf16 path (MFMA, gfx950):
-//   * persistent grid of one 256-thread workgroup per CU; every workgroup
+//   * persistent grid of one 512-thread workgroup per CU; every workgroup
 //     rebuilds the tile table from cu_seqlens in LDS (no host sync, the
 //     grid is sized from the machine, not from the routing);
 //   * 256x256 output tile, K step 32, 8 waves in 2x4, each wave 128x64 as
 //     4x2 v_mfma_f32_32x32x16_bf16 blocks (fp32 accumulators);
-//   * operands staged global -> registers -> LDS, double-buffered, one
-//     barrier per K step, next tile's global loads in flight during the
-//     MFMAs; an operand whose contraction index is strided in memory (the
-//     weight in FWD, both operands in WGRAD) is transposed 8x8 in registers
-//     on its way to LDS so every LDS row holds contiguous contraction values;
-//   * the MFMA is issued as (weight-side x activation-side) so each lane
-//     ends with 4 consecutive output columns: 8-byte bf16 / 16-byte fp32
-//     stores;
+//   * operands go global -> LDS with direct-to-LDS buffer loads (no register
+//     staging) into a 4-stage ring, XOR-swizzled by 16-byte chunks so the
+//     fragment reads are conflict-free; an operand whose contraction index is
+//     contiguous is read with ds_read_b128, one whose contraction index is
+//     strided (the weight in FWD, both operands in WGRAD) with the
+//     transposing ds_read_b64_tr_b16;
+//   * ping-pong K loop: the two waves sharing a SIMD alternate between an
+//     MFMA half step and a memory half step (see tile_mma);
+//   * the MFMA is issued as (column-side x row-side) so each lane ends with
+//     4 consecutive output columns: 8-byte bf16 / 16-byte fp32 stores;
 //   * blockIdx is remapped so the 32 workgroups of one XCD work on
 //     neighbouring tiles (shared weight and activation panels in that XCD's
 //     L2); tiles are walked in groups of 8 row-tiles.
@@ -85,7 +87,15 @@ __device__ inline void dma_tile(uint16_t *dst, __amdgpu_buffer_rsrc_t rs, int ld
       const int c = c0 + cr, r = k * 8;
       off = (r < row_lim && c < c_lim) ? (c * ld + r) * 2 : kOOB;
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr)(dst + blk * 512), 16, off, 0, 0, 0);
+    // buffer_load_dwordx4 ... lds: 16 bytes per lane straight into LDS at M0 + 16 * lane.
+    // Written as asm so the compiler does not track it: its alias analysis cannot tell the
+    // ping-pong groups' stages apart and would drain every load at each barrier.  The load
+    // has no register result (nothing in flight can overwrite a VGPR); the "memory"
+    // clobber keeps LDS accesses on their side of it; completion is ordered only by the
+    // explicit vmcnt waits and barriers of the K loop.
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_vptr)(dst + blk * 512);
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rs), "{m0}"(m0)
+                 : "memory");
   }
 }
 
@@ -158,61 +168,80 @@ __device__ inline void dma_step(uint16_t *dst, const TileArgs &ta, int kt) {
   dma_tile<B_CONTIG>(dst + OP_ELEMS, ta.rb, ta.ldb, ta.b_rows, kt * BK, ta.c_len);
 }
 
-// Steady K step kt (kt + 1 < nk): `cur` holds step kt, `nxt` step kt+1.  Saying the two
-// are distinct (restrict) lets the compiler see that the direct-to-LDS loads issued into
-// `cur` cannot feed the fragment reads of `nxt`, so it adds no wait for them; the waits
-// that order the stages are the explicit ones below.  Per step: read the second sub-step's
-// fragments of `cur`, MFMAs of the first sub-step, wait for step kt+1's loads (steps kt+2
-// and kt+3 may stay in flight) and barrier (every wave has now finished reading `cur`),
-// read step kt+1's first fragments, start step kt+4's loads into `cur`, MFMAs of the second
-// sub-step.  The step has no branch: loads past the last K step have every offset out of
-// range and write zeros into a stage no later step reads, so the wait count is constant
-// and the compiler's LDS-wait bookkeeping stays exact (a join point here made it wait for
-// the next step's fragment reads before the second MFMA burst).
+// One 256x256 output tile: out_tile[i][j] = sum_c Aop(i, c) * Bop(j, c), BK = 32 per K
+// step, K step k in LDS stage k % 4.
+//
+// Ping-pong schedule.  Waves w and w+4 share a SIMD; waves 0-3 form group X, waves 4-7
+// group Y.  The loop runs in half steps separated by barriers, and in each half step one
+// group issues the 16 MFMAs of a K step while the other reads its fragments of a K step
+// from LDS and issues its share of the direct-to-LDS loads.  A wave issues in order, so
+// a load stalled on a full address queue only delays the memory-phase wave, never the
+// MFMAs of the SIMD's other wave.  Numbering half steps h = 0, 1, ...:
+//   X reads step k at h = 2k and runs its MFMAs at h = 2k+1;
+//   Y reads step k at h = 2k+1 and runs its MFMAs at h = 2k+2;
+//   each memory phase of either group issues its loads for step k+3 into stage
+//   (k+3) % 4, whose previous occupant, step k-1, was last read at h = 2k-1, and then
+//   waits until at most two steps of its own loads are in flight, so step k+1 has landed
+//   before the barrier that precedes its first read.
+// The prologue issues steps 0-2 and waits for steps 0 and 1.  Loads of steps past the
+// last have every offset out of range and write zeros into stages no later read uses.
 template <bool A_CONTIG, bool B_CONTIG>
-__device__ __attribute__((always_inline)) inline void k_step(
-    const TileArgs &ta, int kt, uint16_t *__restrict__ cur, const uint16_t *__restrict__ nxt,
-    Frags &f0, Frags &f1, f32x16 (&acc)[TM][TN], int wi, int wj, int lane) {
-  read_frags<A_CONTIG, B_CONTIG>(f1, cur, wi, wj, lane, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  mma16(acc, f0);
-  __builtin_amdgcn_sched_barrier(0);
-  waitcnt_vm<2 * kLoadsPerStep>();
-  __syncthreads();
-  read_frags<A_CONTIG, B_CONTIG>(f0, nxt, wi, wj, lane, 0);
-  dma_step<A_CONTIG, B_CONTIG>(cur, ta, kt + 4);
-  __builtin_amdgcn_sched_barrier(0);
-  mma16(acc, f1);
-  __builtin_amdgcn_sched_barrier(0);
+__device__ __attribute__((always_inline)) inline void mem_phase(
+    const TileArgs &ta, int kt_dma, uint16_t *__restrict__ dst, const uint16_t *__restrict__ src,
+    Frags (&f)[2], int wi, int wj, int lane) {
+  read_frags<A_CONTIG, B_CONTIG>(f[0], src, wi, wj, lane, 0);
+  read_frags<A_CONTIG, B_CONTIG>(f[1], src, wi, wj, lane, 1);
+  dma_step<A_CONTIG, B_CONTIG>(dst, ta, kt_dma);
 }
 
-// One 256x256 output tile: out_tile[i][j] = sum_c Aop(i, c) * Bop(j, c), BK = 32 per K
-// step, K step kt in LDS stage kt % 4, up to four K steps of loads in flight.
 template <bool A_CONTIG, bool B_CONTIG>
 __device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta, f32x16 (&acc)[TM][TN]) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wi = (wid / kWavesN) * (32 * TM), wj = (wid % kWavesN) * (32 * TN);
   const int nk = ta.nk;
+  // (wid is wave-uniform; reading it through readfirstlane makes the compiler restructure
+  // the loop and spill, so the branch below is left to the divergent-branch lowering,
+  // whose skip-if-no-lane-active jumps make it uniform at run time.)
+  const bool X = wid < kWaves / 2;
 
 #pragma unroll
   for (int a = 0; a < TM; ++a)
 #pragma unroll
     for (int b = 0; b < TN; ++b) acc[a][b] = (f32x16){};
 
+  Frags f[2];
 #pragma unroll
-  for (int kt = 0; kt < kStages; ++kt) dma_step<A_CONTIG, B_CONTIG>(lds + kt * STAGE_ELEMS, ta, kt);
-  waitcnt_vm<(kStages - 1) * kLoadsPerStep>();
+  for (int kt = 0; kt < 3; ++kt) dma_step<A_CONTIG, B_CONTIG>(lds + kt * STAGE_ELEMS, ta, kt);
+  waitcnt_vm<kLoadsPerStep>();
   __syncthreads();
-  Frags f0, f1;
-  read_frags<A_CONTIG, B_CONTIG>(f0, lds, wi, wj, lane, 0);
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    k_step<A_CONTIG, B_CONTIG>(ta, kt, lds + (kt & 3) * STAGE_ELEMS,
-                               lds + ((kt + 1) & 3) * STAGE_ELEMS, f0, f1, acc, wi, wj, lane);
+  if (X) {  // h = 0
+    mem_phase<A_CONTIG, B_CONTIG>(ta, 3, lds + 3 * STAGE_ELEMS, lds, f, wi, wj, lane);
+    waitcnt_vm<2 * kLoadsPerStep>();
   }
-  // last K step: no next step to prepare
-  read_frags<A_CONTIG, B_CONTIG>(f1, lds + ((nk - 1) & 3) * STAGE_ELEMS, wi, wj, lane, 1);
-  mma16(acc, f0);
-  mma16(acc, f1);
+  __syncthreads();
+  for (int k = 0; k < nk; ++k) {
+    if (X) {
+      __builtin_amdgcn_sched_barrier(0);
+      mma16(acc, f[0]);  // h = 2k+1
+      mma16(acc, f[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      mem_phase<A_CONTIG, B_CONTIG>(ta, k + 4, lds + (k & 3) * STAGE_ELEMS,  // h = 2k+2
+                                    lds + ((k + 1) & 3) * STAGE_ELEMS, f, wi, wj, lane);
+      waitcnt_vm<2 * kLoadsPerStep>();
+      __syncthreads();
+    } else {
+      mem_phase<A_CONTIG, B_CONTIG>(ta, k + 3, lds + ((k + 3) & 3) * STAGE_ELEMS,  // h = 2k+1
+                                    lds + (k & 3) * STAGE_ELEMS, f, wi, wj, lane);
+      waitcnt_vm<2 * kLoadsPerStep>();
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      mma16(acc, f[0]);  // h = 2k+2
+      mma16(acc, f[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    }
+  }
   waitcnt_vm<0>();  // the trailing out-of-range loads land before the stages are reused
   __syncthreads();
 }
