@@ -61,41 +61,81 @@ constexpr int kStages = 4;
 constexpr int OP_ELEMS = 256 * BK;            // one operand of one stage
 constexpr int STAGE_ELEMS = 2 * OP_ELEMS;
 
-// Direct-to-LDS load of one operand tile (256 rows x BK contraction) into `dst`.
-// Each wave instruction writes 64 lanes x 16 B = 1 KB of LDS contiguously.
+// Direct-to-LDS loads of one operand tile (256 rows x BK contraction per K step).  Each
+// wave instruction writes 64 lanes x 16 B = 1 KB of LDS contiguously; each wave issues two
+// per operand per K step.
 //  contiguous source (row r, contraction c at base[r*ld + c]): LDS is [256][BK], 64 B per row;
 //    16-byte chunk k of row r sits at position k ^ ((r >> 2) & 3);
 //  strided source (row r, contraction c at base[c*ld + r]): LDS is [BK][256], 512 B per
 //    contraction row; chunk k (rows 8k..8k+7) of contraction row c sits at k ^ (4 * (c & 3)).
+// The per-lane byte offset of each block is fixed for the tile (rows past the tile get an
+// offset past every buffer, so they load zeros); a K step only moves the buffer resource:
+// its base advances by one step and its byte count shrinks by the same amount, so the
+// hardware range check still zero-fills contraction rows past the end of a strided operand,
+// and a step past the last gets a zero-byte resource.  A contiguous operand whose
+// contraction length is not a multiple of BK also needs a per-lane column test in its last
+// step (RAGGED).
+struct DmaOp {
+  const char *base;  // byte address of element (row 0, contraction 0) of the tile
+  long long bytes;   // bytes readable from base
+  long long step;    // bytes per K step
+  int voff[2];       // per-lane byte offset of this wave's two blocks, or kOOB
+  int kc[2];         // contraction index of each block's chunk within a K step
+};
+
 template <bool CONTIG>
-__device__ inline void dma_tile(uint16_t *dst, __amdgpu_buffer_rsrc_t rs, int ld, int row_lim,
-                                int c0, int c_lim) {
+__device__ inline void dma_init(DmaOp &d, const uint16_t *base, long long bytes, int ld,
+                                int row_lim) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  d.base = (const char *)base;
+  d.bytes = bytes;
+  d.step = CONTIG ? BK * 2 : (long long)BK * ld * 2;
 #pragma unroll
-  for (int u = 0; u < 16 / kWaves; ++u) {
+  for (int u = 0; u < 2; ++u) {
     const int blk = u * kWaves + wid;              // 1-KB block of the 16-KB tile
     const int o = blk * 1024 + lane * 16;          // this lane's LDS byte offset
-    int off;
     if (CONTIG) {
       const int r = o >> 6, p = (o >> 4) & 3;
       const int k = p ^ ((r >> 2) & 3);
-      const int c = c0 + k * 8;
-      off = (r < row_lim && c < c_lim) ? (r * ld + c) * 2 : kOOB;
+      d.voff[u] = r < row_lim ? (r * ld + k * 8) * 2 : kOOB;
+      d.kc[u] = k * 8;
     } else {
       const int cr = o >> 9, p = (o >> 4) & 31;
       const int k = p ^ (4 * (cr & 3));
-      const int c = c0 + cr, r = k * 8;
-      off = (r < row_lim && c < c_lim) ? (c * ld + r) * 2 : kOOB;
+      d.voff[u] = k * 8 < row_lim ? (cr * ld + k * 8) * 2 : kOOB;
+      d.kc[u] = cr;
     }
+  }
+}
+
+// Issue this wave's two loads of K step kt into the operand's LDS region at byte address
+// `lds_op` (+ this wave's block offset `wave_off`).
+template <bool CONTIG, bool RAGGED>
+__device__ inline void dma_issue(const DmaOp &d, uint32_t lds_op, uint32_t wave_off, int kt,
+                                 int nk, int c_lim) {
+  const long long c0b = (long long)kt * d.step;
+  const long long rem = d.bytes - c0b;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(d.base + c0b, (kt < nk && rem > 0) ? rem : 0);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    int off = d.voff[u];
+    if (CONTIG && RAGGED) off = kt * BK + d.kc[u] < c_lim ? off : kOOB;
     // buffer_load_dwordx4 ... lds: 16 bytes per lane straight into LDS at M0 + 16 * lane.
     // Written as asm so the compiler does not track it: its alias analysis cannot tell the
     // ping-pong groups' stages apart and would drain every load at each barrier.  The load
     // has no register result (nothing in flight can overwrite a VGPR); the "memory"
     // clobber keeps LDS accesses on their side of it; completion is ordered only by the
     // explicit vmcnt waits and barriers of the K loop.
-    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_vptr)(dst + blk * 512);
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rs), "{m0}"(m0)
-                 : "memory");
+    // M0 is written inside the same asm, one wait state ahead of the load: on this
+    // architecture family an LDS-DMA load must not read M0 in the cycle after a scalar
+    // write to it (the compiler pads its own LDS-DMA loads the same way).
+    const uint32_t m0 = lds_op + wave_off + u * kWaves * 1024;
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off),
+        "s"(rs), "s"(m0)
+        : "memory", "m0");
   }
 }
 
@@ -158,14 +198,17 @@ __device__ inline void mma16(f32x16 (&acc)[TM][TN], const Frags &f) {
 }
 
 struct TileArgs {
-  __amdgpu_buffer_rsrc_t ra, rb;
-  int lda, a_rows, ldb, b_rows, c_len, nk;
+  DmaOp a, b;
+  int c_len, nk;
+  uint32_t wave_off;  // this wave's 1-KB block offset within an operand tile (wave-uniform)
 };
 
-template <bool A_CONTIG, bool B_CONTIG>
-__device__ inline void dma_step(uint16_t *dst, const TileArgs &ta, int kt) {
-  dma_tile<A_CONTIG>(dst, ta.ra, ta.lda, ta.a_rows, kt * BK, ta.c_len);
-  dma_tile<B_CONTIG>(dst + OP_ELEMS, ta.rb, ta.ldb, ta.b_rows, kt * BK, ta.c_len);
+// This wave's loads of K step kt (both operands) into LDS stage `stage`.
+template <bool A_CONTIG, bool B_CONTIG, bool RAGGED>
+__device__ inline void dma_step(const uint16_t *lds, int stage, const TileArgs &ta, int kt) {
+  const uint32_t st = (uint32_t)(uintptr_t)(lds_vptr)(lds + stage * STAGE_ELEMS);
+  dma_issue<A_CONTIG, RAGGED>(ta.a, st, ta.wave_off, kt, ta.nk, ta.c_len);
+  dma_issue<B_CONTIG, RAGGED>(ta.b, st + OP_ELEMS * 2, ta.wave_off, kt, ta.nk, ta.c_len);
 }
 
 // One 256x256 output tile: out_tile[i][j] = sum_c Aop(i, c) * Bop(j, c), BK = 32 per K
@@ -185,16 +228,18 @@ __device__ inline void dma_step(uint16_t *dst, const TileArgs &ta, int kt) {
 //   before the barrier that precedes its first read.
 // The prologue issues steps 0-2 and waits for steps 0 and 1.  Loads of steps past the
 // last have every offset out of range and write zeros into stages no later read uses.
-template <bool A_CONTIG, bool B_CONTIG>
-__device__ __attribute__((always_inline)) inline void mem_phase(
-    const TileArgs &ta, int kt_dma, uint16_t *__restrict__ dst, const uint16_t *__restrict__ src,
-    Frags (&f)[2], int wi, int wj, int lane) {
+template <bool A_CONTIG, bool B_CONTIG, bool RAGGED>
+__device__ __attribute__((always_inline)) inline void mem_phase(const uint16_t *lds,
+                                                                const TileArgs &ta, int k_read,
+                                                                int k_dma, Frags (&f)[2], int wi,
+                                                                int wj, int lane) {
+  const uint16_t *src = lds + (k_read & 3) * STAGE_ELEMS;
   read_frags<A_CONTIG, B_CONTIG>(f[0], src, wi, wj, lane, 0);
   read_frags<A_CONTIG, B_CONTIG>(f[1], src, wi, wj, lane, 1);
-  dma_step<A_CONTIG, B_CONTIG>(dst, ta, kt_dma);
+  dma_step<A_CONTIG, B_CONTIG, RAGGED>(lds, k_dma & 3, ta, k_dma);
 }
 
-template <bool A_CONTIG, bool B_CONTIG>
+template <bool A_CONTIG, bool B_CONTIG, bool RAGGED>
 __device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta, f32x16 (&acc)[TM][TN]) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wi = (wid / kWavesN) * (32 * TM), wj = (wid % kWavesN) * (32 * TN);
@@ -211,11 +256,11 @@ __device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta, f32x16 (&acc)
 
   Frags f[2];
 #pragma unroll
-  for (int kt = 0; kt < 3; ++kt) dma_step<A_CONTIG, B_CONTIG>(lds + kt * STAGE_ELEMS, ta, kt);
+  for (int kt = 0; kt < 3; ++kt) dma_step<A_CONTIG, B_CONTIG, RAGGED>(lds, kt, ta, kt);
   waitcnt_vm<kLoadsPerStep>();
   __syncthreads();
   if (X) {  // h = 0
-    mem_phase<A_CONTIG, B_CONTIG>(ta, 3, lds + 3 * STAGE_ELEMS, lds, f, wi, wj, lane);
+    mem_phase<A_CONTIG, B_CONTIG, RAGGED>(lds, ta, 0, 3, f, wi, wj, lane);
     waitcnt_vm<2 * kLoadsPerStep>();
   }
   __syncthreads();
@@ -226,13 +271,11 @@ __device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta, f32x16 (&acc)
       mma16(acc, f[1]);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
-      mem_phase<A_CONTIG, B_CONTIG>(ta, k + 4, lds + (k & 3) * STAGE_ELEMS,  // h = 2k+2
-                                    lds + ((k + 1) & 3) * STAGE_ELEMS, f, wi, wj, lane);
+      mem_phase<A_CONTIG, B_CONTIG, RAGGED>(lds, ta, k + 1, k + 4, f, wi, wj, lane);  // h = 2k+2
       waitcnt_vm<2 * kLoadsPerStep>();
       __syncthreads();
     } else {
-      mem_phase<A_CONTIG, B_CONTIG>(ta, k + 3, lds + ((k + 3) & 3) * STAGE_ELEMS,  // h = 2k+1
-                                    lds + (k & 3) * STAGE_ELEMS, f, wi, wj, lane);
+      mem_phase<A_CONTIG, B_CONTIG, RAGGED>(lds, ta, k, k + 3, f, wi, wj, lane);  // h = 2k+1
       waitcnt_vm<2 * kLoadsPerStep>();
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
@@ -315,7 +358,7 @@ __device__ inline int find_seg(const int *sStart, int G, int t) {
   return lo;
 }
 
-template <int OP>
+template <int OP, bool RAGGED>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
     const int32_t *__restrict__ cu, void *__restrict__ out, int G, int M_total, int Kd, int N) {
@@ -331,6 +374,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
   const long long total = wgrad ? (long long)n_rt_total * n_it * n_ct : (long long)n_rt_total * n_ct;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wi = (wid / kWavesN) * (32 * TM), wj = (wid % kWavesN) * (32 * TN);
+  const uint32_t wave_off = __builtin_amdgcn_readfirstlane(wid) * 1024;
 
   for (long long t = logical_block(); t < total; t += gridDim.x) {
     f32x16 acc[TM][TN];
@@ -343,27 +387,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
       const int j0 = ct * BN;
       const uint16_t *w = b + (size_t)rho * Kd * N;
       TileArgs ta;
+      ta.wave_off = wave_off;
       if (OP == MOE_GEMM_FWD) {
-        ta.ra = make_rsrc(a + (size_t)m0 * Kd, (long long)rows * Kd * 2);
-        ta.lda = Kd;
-        ta.rb = make_rsrc(w + j0, ((long long)Kd * N - j0) * 2);
-        ta.ldb = N;
-        ta.b_rows = N - j0;
+        dma_init<true>(ta.a, a + (size_t)m0 * Kd, (long long)rows * Kd * 2, Kd, rows);
+        dma_init<false>(ta.b, w + j0, ((long long)Kd * N - j0) * 2, N, N - j0);
         ta.c_len = Kd;
       } else {
-        ta.ra = make_rsrc(a + (size_t)m0 * N, (long long)rows * N * 2);
-        ta.lda = N;
-        ta.rb = make_rsrc(w + (size_t)j0 * N, (long long)(Kd - j0) * N * 2);
-        ta.ldb = N;
-        ta.b_rows = Kd - j0;
+        dma_init<true>(ta.a, a + (size_t)m0 * N, (long long)rows * N * 2, N, rows);
+        dma_init<true>(ta.b, w + (size_t)j0 * N, (long long)(Kd - j0) * N * 2, N, Kd - j0);
         ta.c_len = N;
       }
-      ta.a_rows = rows;
       ta.nk = (ta.c_len + BK - 1) / BK;
       if (OP == MOE_GEMM_FWD)
-        tile_mma<true, false>(lds, ta, acc);
+        tile_mma<true, false, RAGGED>(lds, ta, acc);
       else
-        tile_mma<true, true>(lds, ta, acc);
+        tile_mma<true, true, RAGGED>(lds, ta, acc);
       uint16_t *o = (uint16_t *)out + (size_t)m0 * ncols + j0;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
@@ -392,15 +430,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
       const int m0 = sCu[rho], len = sCu[rho + 1] - m0;
       const int i0 = it * BM, j0 = ct * BN;
       TileArgs ta;
-      ta.ra = make_rsrc(a + (size_t)m0 * Kd + i0, ((long long)len * Kd - i0) * 2);
-      ta.lda = Kd;
-      ta.a_rows = Kd - i0;
-      ta.rb = make_rsrc(b + (size_t)m0 * N + j0, ((long long)len * N - j0) * 2);
-      ta.ldb = N;
-      ta.b_rows = N - j0;
+      ta.wave_off = wave_off;
+      dma_init<false>(ta.a, a + (size_t)m0 * Kd + i0, ((long long)len * Kd - i0) * 2, Kd, Kd - i0);
+      dma_init<false>(ta.b, b + (size_t)m0 * N + j0, ((long long)len * N - j0) * 2, N, N - j0);
       ta.c_len = len;
       ta.nk = (len + BK - 1) / BK;
-      tile_mma<false, false>(lds, ta, acc);
+      tile_mma<false, false, false>(lds, ta, acc);
       float *o = (float *)out + ((size_t)rho * Kd + i0) * N + j0;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
@@ -518,21 +553,29 @@ extern "C" moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t 
     return launch_status();
   }
   const int grid = device_cu_count();
+  const uint16_t *a16 = (const uint16_t *)a, *b16 = (const uint16_t *)b;
+  // A contiguous operand whose contraction length is not a multiple of the K step needs a
+  // per-lane column test in its last K step; every other shape runs the test-free loop.
   switch (op) {
     case MOE_GEMM_FWD:
-      hipLaunchKernelGGL(k_ggemm_bf16<MOE_GEMM_FWD>, dim3(grid), dim3(kGemmThreads), 0,
-                         stream, (const uint16_t *)a, (const uint16_t *)b, cu_seqlens, out, G,
-                         M_total, Kd, N);
+      if (Kd % BK)
+        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_FWD, true>), dim3(grid), dim3(kGemmThreads), 0,
+                           stream, a16, b16, cu_seqlens, out, G, M_total, Kd, N);
+      else
+        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_FWD, false>), dim3(grid), dim3(kGemmThreads),
+                           0, stream, a16, b16, cu_seqlens, out, G, M_total, Kd, N);
       break;
     case MOE_GEMM_DGRAD:
-      hipLaunchKernelGGL(k_ggemm_bf16<MOE_GEMM_DGRAD>, dim3(grid), dim3(kGemmThreads), 0,
-                         stream, (const uint16_t *)a, (const uint16_t *)b, cu_seqlens, out, G,
-                         M_total, Kd, N);
+      if (N % BK)
+        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_DGRAD, true>), dim3(grid), dim3(kGemmThreads),
+                           0, stream, a16, b16, cu_seqlens, out, G, M_total, Kd, N);
+      else
+        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_DGRAD, false>), dim3(grid), dim3(kGemmThreads),
+                           0, stream, a16, b16, cu_seqlens, out, G, M_total, Kd, N);
       break;
     default:
-      hipLaunchKernelGGL(k_ggemm_bf16<MOE_GEMM_WGRAD>, dim3(grid), dim3(kGemmThreads), 0,
-                         stream, (const uint16_t *)a, (const uint16_t *)b, cu_seqlens, out, G,
-                         M_total, Kd, N);
+      hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_WGRAD, false>), dim3(grid), dim3(kGemmThreads), 0,
+                         stream, a16, b16, cu_seqlens, out, G, M_total, Kd, N);
   }
   return launch_status();
 }
