@@ -358,6 +358,41 @@ __device__ inline int find_seg(const int *sStart, int G, int t) {
   return lo;
 }
 
+// bf16 output-tile epilogue.  The accumulator layout leaves each lane 4 consecutive columns
+// of one row, so a store straight from registers writes 32 rows x 16 B per instruction.
+// The tile goes through LDS instead (free once the K loop has drained): each wave writes its
+// fragments, then the whole 256 x 256 tile (128 KB) leaves in row segments of 16 B per lane,
+// 512 B of one row per 32 lanes.  16-byte LDS chunks are XOR-swizzled by row so the
+// fragment writes spread over the banks and the row reads are conflict-free.  Rows >= rows
+// and columns >= cols of the tile are not written (cols is a multiple of 8).
+__device__ inline void epilogue_bf16(uint16_t *lds, const f32x16 (&acc)[TM][TN], uint16_t *o,
+                                     long long ld, int rows, int cols, int wi, int wj,
+                                     int lane, int wid) {
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int i = wi + tm * 32 + (lane & 31);
+        const int c = (wj + tn * 32 + g * 8) >> 3;  // 8-column chunk
+        const f32x16 &a = acc[tm][tn];
+        uint2 v;
+        v.x = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
+        v.y = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
+        *(uint2 *)(lds + i * 256 + (c ^ (i & 31)) * 8 + (lane >> 5) * 4) = v;
+      }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {  // wave wid: rows 32 wid .. +31, two per instruction
+    const int i = wid * 32 + 2 * r + (lane >> 5);
+    const int c = lane & 31;
+    const u32x4 v = *(const u32x4 *)(lds + i * 256 + (c ^ (i & 31)) * 8);
+    if (i < rows && c * 8 < cols) *(u32x4 *)(o + i * ld + c * 8) = v;
+  }
+  __syncthreads();
+}
+
 template <int OP, bool RAGGED>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
@@ -402,25 +437,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
         tile_mma<true, false, RAGGED>(lds, ta, acc);
       else
         tile_mma<true, true, RAGGED>(lds, ta, acc);
-      uint16_t *o = (uint16_t *)out + (size_t)m0 * ncols + j0;
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int i = wi + tm * 32 + (lane & 31);
-        if (i >= rows) continue;
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int j = wj + tn * 32 + g * 8 + (lane >> 5) * 4;
-            if (j0 + j < ncols) {
-              const f32x16 &c = acc[tm][tn];
-              uint2 v;
-              v.x = pack_bf16x2(c[4 * g + 0], c[4 * g + 1]);
-              v.y = pack_bf16x2(c[4 * g + 2], c[4 * g + 3]);
-              *(uint2 *)(o + (size_t)i * ncols + j) = v;
-            }
-          }
-      }
+      epilogue_bf16(lds, acc, (uint16_t *)out + (size_t)m0 * ncols + j0, ncols, rows,
+                    ncols - j0, wi, wj, lane, wid);
     } else {
       const int per_seg = n_it * n_ct;
       const int sidx = (int)(t / per_seg);
@@ -436,6 +454,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
       ta.c_len = len;
       ta.nk = (len + BK - 1) / BK;
       tile_mma<false, false, false>(lds, ta, acc);
+      // fp32 += straight from registers: staging this epilogue through LDS (as the bf16 one
+      // is) measured slower, and so did starting the accumulator from the old values.
       float *o = (float *)out + ((size_t)rho * Kd + i0) * N + j0;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {

@@ -55,9 +55,9 @@ class EventTimer:
 
 
 KERNEL_SOURCES = {  # bench kernel name -> (rocprof name prefix, source files that define it)
-    "gemm_fwd": ("moe::k_ggemm_bf16<0>", ("group_gemm.hip", "common.hpp")),
-    "gemm_dgrad": ("moe::k_ggemm_bf16<1>", ("group_gemm.hip", "common.hpp")),
-    "gemm_wgrad": ("moe::k_ggemm_bf16<2>", ("group_gemm.hip", "common.hpp")),
+    "gemm_fwd": ("moe::k_ggemm_bf16<0", ("group_gemm.hip", "common.hpp")),
+    "gemm_dgrad": ("moe::k_ggemm_bf16<1", ("group_gemm.hip", "common.hpp")),
+    "gemm_wgrad": ("moe::k_ggemm_bf16<2", ("group_gemm.hip", "common.hpp")),
     "permute": ("moe::k_permute<false>", ("rows.hip", "common.hpp")),
     "permute_weighted": ("moe::k_permute<true>", ("rows.hip", "common.hpp")),
     "combine": ("moe::k_combine<true>", ("rows.hip", "common.hpp")),
