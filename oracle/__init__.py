@@ -12,9 +12,12 @@ are listed per function in the tests:
   optimal replica counts on tiny inputs, and special cases that reduce to a
   stable argsort / bincount (one rank) or to plain expert parallelism
   (balanced routing).
-* ``permute``, ``group_gemm``, ``combine``, ``replica_grad_fold``: a
-  simulation of every rank that must reproduce the dense MoE definition and
-  its per-expert weight gradients exactly on small-integer inputs.
+* ``permute``, ``group_gemm``, ``combine``, ``replica_grad_fold``,
+  ``unpermute_reduce``, ``combine_weight_grad``: a simulation of every rank
+  that must reproduce the dense MoE definition, its per-expert weight
+  gradients, its input gradient and its router-weight gradient exactly on
+  small-integer inputs; ``unpermute_reduce`` is also checked as the adjoint
+  of ``permute``.
 * ``bf16``: torch's CPU cast on sampled bit patterns.
 
 Parity unpinned: any specific plan versus the original library's planner
@@ -23,7 +26,7 @@ Parity unpinned: any specific plan versus the original library's planner
 from .moe_ref import (  # noqa: F401
     STATUS_BAD_EXPERT_ID, STATUS_SLOT_OVERFLOW, HEADER_WORDS, Plan, Replica, maxvio, histogram,
     plan, plan_words, layout, layout_loops, permute, group_gemm, group_gemm_rows, wgrad_entries,
-    combine, replica_grad_fold, prefetch,
+    combine, replica_grad_fold, prefetch, unpermute_reduce, combine_weight_grad,
 )
 from .bf16 import (  # noqa: F401
     bf16_bits_to_f32, bf16_bits_to_f64, f32_to_bf16_bits, f64_to_bf16_bits,

@@ -491,6 +491,52 @@ def combine(y_all, dest_pos, topk_w, rank: int, S: int, K: int, dtype="bf16", to
     return _narrow(acc, dtype)
 
 
+def unpermute_reduce(dxp_all, dest_pos, rank: int, S: int, K: int, dtype="bf16", tokens=None):
+    """dx[s] = sum over k of dxp_all[dest_pos of copy (rank, s, k)]: the dispatch's backward.
+
+    [blog] "What This Does" (dispatch places each token's K copies at their
+    expert-grouped rows) and "Real-World Use" (the per-layer training loop
+    runs backward through the same path).  READING: the dispatch copies a
+    token row unchanged to K rows, so the gradient of the token row is the
+    plain sum of the K rows' gradients, pulled back through dest_pos the way
+    the combine pulls outputs; ascending k in float64, one rounding; copies
+    with dest_pos < 0 add nothing.  ``dxp_all`` holds rank q's rows at
+    q*S*K ..; ``tokens`` restricts the computation to those token indices.
+    """
+    toks = np.arange(S) if tokens is None else np.asarray(tokens, np.int64)
+    acc = np.zeros((toks.size, dxp_all.shape[1]), np.float64)
+    dp = np.asarray(dest_pos).reshape(-1)
+    for t, s in enumerate(toks):
+        for k in range(K):
+            d = int(dp[(rank * S + int(s)) * K + k])
+            if d >= 0:
+                acc[t] += _widen(dxp_all[d], dtype)
+    return _narrow(acc, dtype)
+
+
+def combine_weight_grad(y_all, dest_pos, dout, rank: int, S: int, K: int, dtype="bf16",
+                        tokens=None):
+    """dw[s*K + k] = <dout[s], y_all[dest_pos of copy (rank, s, k)]>: the router-weight gradient.
+
+    [blog] "Real-World Use" (backward of the combine that gathers the expert
+    outputs).  READING: the combine is linear in each router weight, so the
+    weight's gradient is the dot product of the token's output gradient with
+    the expert output it scaled; float64 dot product rounded once to float32;
+    0 for copies with dest_pos < 0.  ``dout`` holds rank ``rank``'s S token
+    rows; the result is [len(tokens), K] (all S tokens by default).
+    """
+    toks = np.arange(S) if tokens is None else np.asarray(tokens, np.int64)
+    out = np.zeros((toks.size, K), np.float64)
+    dp = np.asarray(dest_pos).reshape(-1)
+    for t, s in enumerate(toks):
+        g = _widen(dout[int(s)], dtype)
+        for k in range(K):
+            d = int(dp[(rank * S + int(s)) * K + k])
+            if d >= 0:
+                out[t, k] = float(np.dot(g, _widen(y_all[d], dtype)))
+    return out.astype(np.float32)
+
+
 def replica_grad_fold(dw: np.ndarray, pl: Plan, rank: int) -> np.ndarray:
     """Fold replica weight-gradient rows of ``rank`` into their home expert rows.
 
