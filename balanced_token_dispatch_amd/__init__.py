@@ -24,7 +24,8 @@ GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_plan_words", "moe_plan_workspace_bytes", "moe_plan",
            "moe_dispatch_layout_workspace_bytes", "moe_dispatch_layout", "moe_prefetch",
-           "moe_permute", "moe_group_gemm", "moe_combine", "moe_replica_grad_fold")
+           "moe_permute", "moe_group_gemm", "moe_combine", "moe_replica_grad_fold",
+           "moe_unpermute_reduce", "moe_combine_weight_grad")
 
 
 class MoeDims(ctypes.Structure):
@@ -49,6 +50,8 @@ _lib.moe_group_gemm.argtypes = [ctypes.c_int, ctypes.c_int, _I32, _I32, _I32, _I
                                 _P, _P]
 _lib.moe_combine.argtypes = [_D, ctypes.c_int, _I64, _I32, _P, _P, _P, _P, _P]
 _lib.moe_replica_grad_fold.argtypes = [_D, _I32, _P, _P, _I64, _P]
+_lib.moe_unpermute_reduce.argtypes = [_D, ctypes.c_int, _I64, _I32, _P, _P, _P, _P]
+_lib.moe_combine_weight_grad.argtypes = [_D, ctypes.c_int, _I64, _I32, _P, _P, _P, _P, _P]
 for _n in EXPORTS[3:]:
     if _n.endswith("_bytes"):
         continue
@@ -137,6 +140,18 @@ def moe_combine(d, rank, y_all, dest_pos, topk_w, out, stream=None):
     _check(_lib.moe_combine(ctypes.byref(d), _dtype(y_all), y_all.shape[1], rank, _ptr(y_all),
                             _ptr(dest_pos), _ptr(topk_w), _ptr(out), _stream(stream)),
            "moe_combine")
+
+
+def moe_unpermute_reduce(d, rank, dxp_all, dest_pos, dx, stream=None):
+    _check(_lib.moe_unpermute_reduce(ctypes.byref(d), _dtype(dxp_all), dxp_all.shape[1], rank,
+                                     _ptr(dxp_all), _ptr(dest_pos), _ptr(dx), _stream(stream)),
+           "moe_unpermute_reduce")
+
+
+def moe_combine_weight_grad(d, rank, y_all, dest_pos, dout, dw, stream=None):
+    _check(_lib.moe_combine_weight_grad(ctypes.byref(d), _dtype(y_all), y_all.shape[1], rank,
+                                        _ptr(y_all), _ptr(dest_pos), _ptr(dout), _ptr(dw),
+                                        _stream(stream)), "moe_combine_weight_grad")
 
 
 def moe_replica_grad_fold(d, rank, plan, dw, stream=None):

@@ -90,7 +90,9 @@ __device__ inline u32x4 round_row16(const float (&acc)[8]) {
 
 // out[s] = sum_k w[c] * y_all[dest_pos[c]], c = (rank*S + s)*K + k.  grid (tokens, chunks);
 // a block covers kRowThreads*kCombU vectors of one token, all K source rows in flight.
-template <bool BF16>
+// Without WEIGHTED every weight is 1 (the un-permute reduce of the dispatch's backward): the
+// fused multiply-add by 1 rounds exactly like a plain add.
+template <bool BF16, bool WEIGHTED = true>
 __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict__ y_all,
                                                         const int32_t *__restrict__ dest_pos,
                                                         const float *__restrict__ topk_w,
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict
 #pragma unroll
     for (int k = 0; k < kMaxKUnrolled; ++k) {
       dst[k] = (k < K) ? dest_pos[c0 + k] : -1;
-      wt[k] = (k < K) ? topk_w[c0 + k] : 0.0f;
+      wt[k] = (k < K) ? (WEIGHTED ? topk_w[c0 + k] : 1.0f) : 0.0f;
     }
     u32x4 *o = out + (size_t)s * vec_per_row;
     for (int base = blockIdx.y * kChunk; base < vec_per_row; base += gridDim.y * kChunk) {
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict
 }
 
 // Generic-K combine for K > kMaxKUnrolled: same arithmetic and order, one k at a time.
-template <bool BF16>
+template <bool BF16, bool WEIGHTED = true>
 __global__ __launch_bounds__(kRowThreads) void k_combine_anyk(const u32x4 *__restrict__ y_all,
                                                              const int32_t *__restrict__ dest_pos,
                                                              const float *__restrict__ topk_w,
@@ -145,10 +147,84 @@ __global__ __launch_bounds__(kRowThreads) void k_combine_anyk(const u32x4 *__res
         for (int k = 0; k < K; ++k) {
           const int d = dest_pos[c0 + k];
           if (d < 0) continue;
-          fma_row16<BF16>(acc, topk_w[c0 + k], y_all[(size_t)d * vec_per_row + v]);
+          fma_row16<BF16>(acc, WEIGHTED ? topk_w[c0 + k] : 1.0f,
+                          y_all[(size_t)d * vec_per_row + v]);
         }
         o[v] = round_row16<BF16>(acc);
       }
+    }
+  }
+}
+
+template <bool BF16>
+__device__ inline float dot_row16(u32x4 g, u32x4 y, float acc) {
+  if (BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc = __builtin_fmaf(bf16_lo(g[q]), bf16_lo(y[q]), acc);
+      acc = __builtin_fmaf(bf16_hi(g[q]), bf16_hi(y[q]), acc);
+    }
+  } else {
+    const f32x4 a = __builtin_bit_cast(f32x4, g), b = __builtin_bit_cast(f32x4, y);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_fmaf(a[q], b[q], acc);
+  }
+  return acc;
+}
+
+constexpr int kWgK = 8;  // copies whose gradients one pass over a token's gradient row serves
+
+// dw[s*K + k] = <dout[s], y_all[dest_pos[c]]>, c = (rank*S + s)*K + k (0 where dest_pos < 0).
+// grid (tokens); a block reads its token's output-gradient row once per group of kWgK copies
+// and each copy's expert-output row once.  Each thread sums its vectors in row order in fp32,
+// then a wave butterfly and the block's waves in index order: a fixed summation order, so the
+// result is deterministic.
+template <bool BF16>
+__global__ __launch_bounds__(kRowThreads) void k_combine_wgrad(const u32x4 *__restrict__ y_all,
+                                                              const int32_t *__restrict__ dest_pos,
+                                                              const u32x4 *__restrict__ dout,
+                                                              float *__restrict__ dw, int S, int K,
+                                                              int rank, int vec_per_row) {
+  __shared__ float part[kRowThreads / kWave][kWgK];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
+    const size_t c0 = ((size_t)rank * S + s) * K;
+    const u32x4 *g = dout + (size_t)s * vec_per_row;
+    for (int kb = 0; kb < K; kb += kWgK) {
+      int dst[kWgK];
+      float acc[kWgK];
+#pragma unroll
+      for (int k = 0; k < kWgK; ++k) {
+        dst[k] = (kb + k < K) ? dest_pos[c0 + kb + k] : -1;
+        acc[k] = 0.0f;
+      }
+      for (int v = threadIdx.x; v < vec_per_row; v += kRowThreads) {
+        const u32x4 gv = g[v];
+        u32x4 yv[kWgK];
+#pragma unroll
+        for (int k = 0; k < kWgK; ++k)
+          if (dst[k] >= 0) yv[k] = __builtin_nontemporal_load(y_all + (size_t)dst[k] * vec_per_row + v);
+#pragma unroll
+        for (int k = 0; k < kWgK; ++k)
+          if (dst[k] >= 0) acc[k] = dot_row16<BF16>(gv, yv[k], acc[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < kWgK; ++k) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) acc[k] += __shfl_xor(acc[k], off, kWave);
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < kWgK; ++k) part[wid][k] = acc[k];
+      }
+      __syncthreads();
+      if (threadIdx.x < kWgK && kb + (int)threadIdx.x < K) {
+        float t = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kRowThreads / kWave; ++w) t += part[w][threadIdx.x];
+        dw[(size_t)s * K + kb + threadIdx.x] = t;
+      }
+      __syncthreads();
     }
   }
 }
@@ -276,6 +352,58 @@ extern "C" moe_status_t moe_combine(const moe_dims *d, moe_dtype dtype, int64_t 
                          (const u32x4 *)y_all, dest_pos, topk_w, (u32x4 *)out, d->S, d->K, rank,
                          vec);
   }
+  return launch_status();
+}
+
+extern "C" moe_status_t moe_unpermute_reduce(const moe_dims *d, moe_dtype dtype, int64_t width,
+                                             int32_t rank, const void *dxp_all,
+                                             const int32_t *dest_pos, void *dx,
+                                             hipStream_t stream) {
+  if (!dims_ok(d) || !dxp_all || !dest_pos || !dx) return MOE_EINVAL;
+  if (rank < 0 || rank >= d->R) return MOE_EINVAL;
+  const int eb = elem_bytes(dtype);
+  if (!eb || width <= 0 || (width * eb) % 16 != 0 || width * eb / 16 > INT32_MAX) return MOE_EINVAL;
+  const int vec = (int)(width * eb / 16);
+  const dim3 grid(clamp_grid(d->S, kMaxGridX),
+                  clamp_grid(ceil_div(vec, kRowThreads * kCombU), kMaxGridY));
+  const bool bf = dtype == MOE_BF16;
+  const u32x4 *src = (const u32x4 *)dxp_all;
+  if (d->K <= kMaxKUnrolled) {
+    if (bf)
+      hipLaunchKernelGGL((k_combine<true, false>), grid, dim3(kRowThreads), 0, stream, src,
+                         dest_pos, nullptr, (u32x4 *)dx, d->S, d->K, rank, vec);
+    else
+      hipLaunchKernelGGL((k_combine<false, false>), grid, dim3(kRowThreads), 0, stream, src,
+                         dest_pos, nullptr, (u32x4 *)dx, d->S, d->K, rank, vec);
+  } else {
+    if (bf)
+      hipLaunchKernelGGL((k_combine_anyk<true, false>), grid, dim3(kRowThreads), 0, stream, src,
+                         dest_pos, nullptr, (u32x4 *)dx, d->S, d->K, rank, vec);
+    else
+      hipLaunchKernelGGL((k_combine_anyk<false, false>), grid, dim3(kRowThreads), 0, stream, src,
+                         dest_pos, nullptr, (u32x4 *)dx, d->S, d->K, rank, vec);
+  }
+  return launch_status();
+}
+
+extern "C" moe_status_t moe_combine_weight_grad(const moe_dims *d, moe_dtype dtype, int64_t width,
+                                                int32_t rank, const void *y_all,
+                                                const int32_t *dest_pos, const void *dout,
+                                                float *dw, hipStream_t stream) {
+  if (!dims_ok(d) || !y_all || !dest_pos || !dout || !dw) return MOE_EINVAL;
+  if (rank < 0 || rank >= d->R) return MOE_EINVAL;
+  const int eb = elem_bytes(dtype);
+  if (!eb || width <= 0 || (width * eb) % 16 != 0 || width * eb / 16 > INT32_MAX) return MOE_EINVAL;
+  const int vec = (int)(width * eb / 16);
+  const dim3 grid(clamp_grid(d->S, kMaxGridX));
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(k_combine_wgrad<true>, grid, dim3(kRowThreads), 0, stream,
+                       (const u32x4 *)y_all, dest_pos, (const u32x4 *)dout, dw, d->S, d->K, rank,
+                       vec);
+  else
+    hipLaunchKernelGGL(k_combine_wgrad<false>, grid, dim3(kRowThreads), 0, stream,
+                       (const u32x4 *)y_all, dest_pos, (const u32x4 *)dout, dw, d->S, d->K, rank,
+                       vec);
   return launch_status();
 }
 

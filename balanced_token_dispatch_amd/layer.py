@@ -9,7 +9,10 @@ Forward (rank r):  plan -> dispatch layout -> prefetch slot rows of both
 projections -> permute -> up GEMM -> down GEMM (written into rank r's
 slice of the all-ranks expert-output buffer) -> combine.
 Backward:          weighted permute of the output gradient (combine's
-adjoint) -> down DGRAD -> down WGRAD -> up DGRAD -> up WGRAD -> fold the
+adjoint for the expert outputs) -> router-weight gradient (combine's
+adjoint for the weights) -> down DGRAD -> down WGRAD -> up DGRAD (into rank
+r's slice of the all-ranks input-gradient buffer) -> up WGRAD -> un-permute
+reduce of the input gradients to the tokens (dispatch's adjoint) -> fold the
 replica rows of both weight gradients into their home experts.
 The activation between the projections is the identity.
 """
@@ -18,8 +21,9 @@ from dataclasses import dataclass
 import torch
 
 from . import (GEMM_DGRAD, GEMM_FWD, GEMM_WGRAD, dims as _mk_dims, dispatch_layout_workspace_bytes,
-               moe_combine, moe_dispatch_layout, moe_group_gemm, moe_permute, moe_plan,
-               moe_prefetch, moe_replica_grad_fold, plan_words, plan_workspace_bytes)
+               moe_combine, moe_combine_weight_grad, moe_dispatch_layout, moe_group_gemm,
+               moe_permute, moe_plan, moe_prefetch, moe_replica_grad_fold, moe_unpermute_reduce,
+               plan_words, plan_workspace_bytes)
 
 
 @dataclass
@@ -72,9 +76,20 @@ class LayerStep:
             self.dout_all = torch.zeros((s.R * s.S, s.H), **act)
             self.dy = torch.zeros((s.SK, s.H), **act)
             self.dz = torch.zeros((s.SK, s.Hp), **act)
-            self.dxp = torch.zeros((s.SK, s.H), **act)
+            # every rank's input-gradient rows in the layout's order; this rank's DGRAD writes
+            # its slice, the other slices stand in for the peers' (the un-permute reduce reads
+            # a token's K copies wherever they were processed)
+            self.dxp_all = torch.zeros((s.R * s.SK, s.H), **act)
+            self.dx = torch.zeros((s.S, s.H), **act)
+            self.dtopk_w = torch.zeros(s.SK, **f32)
             self.dw_up = torch.zeros((s.G, s.H, s.Hp), **f32)
             self.dw_down = torch.zeros((s.G, s.Hp, s.H), **f32)
+
+    @property
+    def dxp(self):
+        """This rank's slice of the input-gradient buffer (the up projection's DGRAD writes here)."""
+        r, SK = self.rank, self.s.SK
+        return self.dxp_all[r * SK:(r + 1) * SK]
 
     @property
     def y(self):
@@ -109,6 +124,8 @@ class LayerStep:
         s, r, c = self.s, self.rank, self._call
         c(timer, "permute_weighted", moe_permute, self.d, self.dout_all, self.src, self.dy,
           self.topk_w.view(-1))
+        c(timer, "combine_wgrad", moe_combine_weight_grad, self.d, r, self.y_all, self.dest,
+          self.dout_all[r * s.S:(r + 1) * s.S], self.dtopk_w)
         c(timer, "gemm_dgrad", moe_group_gemm, GEMM_DGRAD, self.dy, self.w_down, self.cu, self.dz,
           s.Hp, s.H)
         c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.z, self.dy, self.cu, self.dw_down,
@@ -117,6 +134,8 @@ class LayerStep:
           s.H, s.Hp)
         c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.xp, self.dz, self.cu, self.dw_up,
           s.H, s.Hp)
+        c(timer, "unpermute_reduce", moe_unpermute_reduce, self.d, r, self.dxp_all, self.dest,
+          self.dx)
         c(timer, "fold", moe_replica_grad_fold, self.d, r, self.plan, self.dw_up)
         c(timer, "fold", moe_replica_grad_fold, self.d, r, self.plan, self.dw_down)
 

@@ -60,7 +60,9 @@ KERNEL_SOURCES = {  # bench kernel name -> (rocprof name prefix, source files th
     "gemm_wgrad": ("moe::k_ggemm_bf16<2", ("group_gemm.hip", "common.hpp")),
     "permute": ("moe::k_permute<false>", ("rows.hip", "common.hpp")),
     "permute_weighted": ("moe::k_permute<true>", ("rows.hip", "common.hpp")),
-    "combine": ("moe::k_combine<true>", ("rows.hip", "common.hpp")),
+    "combine": ("moe::k_combine<true, true>", ("rows.hip", "common.hpp")),
+    "combine_wgrad": ("moe::k_combine_wgrad<true>", ("rows.hip", "common.hpp")),
+    "unpermute_reduce": ("moe::k_combine<true, false>", ("rows.hip", "common.hpp")),
     "fold": ("moe::k_fold", ("rows.hip", "common.hpp")),
     "prefetch": ("moe::k_prefetch", ("rows.hip", "common.hpp")),
 }
@@ -145,6 +147,8 @@ def algorithmic_work(shape, n_slots_used):
         "gemm_dgrad": ("mfma", gemm),
         "gemm_wgrad": ("mfma", gemm),
         "fold": ("hbm", 3.0 * n_slots_used * H * Hp * 4),
+        "combine_wgrad": ("hbm", SK * H * 2.0 + S * H * 2.0 + 8.0 * SK),
+        "unpermute_reduce": ("hbm", SK * H * 2.0 + S * H * 2.0 + 4.0 * SK),
     }
 
 
@@ -167,6 +171,7 @@ def setup_layer(wl, target, rank, placement="receiver0", layer=None):
         synth.fill_normal_(layer.y_all, 1.0, seed * 10 + 4)
         if layer.backward_enabled:
             synth.fill_normal_(layer.dout_all, 1.0, seed * 10 + 5)
+            synth.fill_normal_(layer.dxp_all, 1.0, seed * 10 + 6)
     layer.topk_idx.copy_(torch.from_numpy(idx))
     layer.topk_w.copy_(torch.from_numpy(w))
     torch.cuda.synchronize()
@@ -209,8 +214,9 @@ def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
 
     Timed on this host: the full plan and layout of all R ranks' routing, then permute,
     both projections forward, the weighted permute, both DGRADs and WGRADs on the first
-    ``rows_sample`` rows of rank r's buffer, the combine of ``tokens_sample`` tokens, and
-    the fold on 1/8 of each replica row.  Each part is scaled to the full step.
+    ``rows_sample`` rows of rank r's buffer, the combine, router-weight gradient and
+    un-permute reduce of ``tokens_sample`` tokens, and the fold on 1/8 of each replica row.
+    Each part is scaled to the full step.
     """
     import numpy as np
     import torch
@@ -263,8 +269,14 @@ def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
     ymap = np.full(s.R * s.SK, -1, np.int64)
     ymap[need] = np.arange(need.size)
     dest_l = np.where(dest >= 0, ymap[np.maximum(dest, 0)], -1)
+    g_tok = layer.dout_all[r * s.S:(r + 1) * s.S][torch.from_numpy(ts).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    g_full = np.zeros((s.S, s.H), np.uint16)
+    g_full[ts] = g_tok
+    dxp_rows = layer.dxp_all[torch.from_numpy(need.astype(np.int64)).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
     t0 = time.perf_counter()
     oracle.combine(y_rows, dest_l, w, r, s.S, s.K, tokens=ts)
+    oracle.combine_weight_grad(y_rows, dest_l, g_full, r, s.S, s.K, tokens=ts)
+    oracle.unpermute_reduce(dxp_rows, dest_l, r, s.S, s.K, tokens=ts)
     t["combine"] = time.perf_counter() - t0
     frac = 8
     dw = np.zeros((s.G, s.H * s.Hp // frac), np.float32)
@@ -404,7 +416,8 @@ def main():
                "kind": "oracle",
                "sample": (f"plan+layout of all {s.R} ranks' routing in full; permute, fwd up/down, "
                           f"weighted permute, dgrad x2, wgrad x2 on {n_rows} of {s.SK} rows; "
-                          f"combine of {n_tok} of {s.S} tokens; fold on 1/8 of each row; "
+                          f"combine, router-weight gradient and un-permute reduce of {n_tok} of "
+                          f"{s.S} tokens; fold on 1/8 of each row; "
                           f"each part scaled to the full step"),
                "seconds_measured": round(time.time() - t0, 1),
                "parts_s": {k: round(v, 3) for k, v in parts.items()}}

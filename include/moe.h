@@ -198,6 +198,36 @@ moe_status_t moe_combine(const moe_dims *dims, moe_dtype dtype, int64_t width, i
                          void *out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_unpermute_reduce -- dx[s] = sum_k dxp_all[dest_pos[c]], c = copy (rank,
+ * s, k): the backward of the dispatch, which copied each token row to K
+ * expert-grouped rows, so a token's input gradient is the sum of its copies'
+ * gradients.  fp32 accumulation in ascending k, one RNE rounding to the row
+ * type; copies with dest_pos < 0 add nothing.  [blog] "What This Does"
+ * (dispatch places a token's K copies) and "Real-World Use" (the training
+ * loop runs backward through the same path).
+ *   dxp_all [R*S*K, width] (rank q's input-gradient rows at q*S*K ..,
+ *   the layout's order), dest_pos from moe_dispatch_layout, dx [S, width],
+ *   width*elem % 16 == 0.
+ * ------------------------------------------------------------------------- */
+moe_status_t moe_unpermute_reduce(const moe_dims *dims, moe_dtype dtype, int64_t width,
+                                  int32_t rank, const void *dxp_all, const int32_t *dest_pos,
+                                  void *dx, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_combine_weight_grad -- dw[s*K + k] = sum_h dout[s, h] * y_all[dest_pos[c], h],
+ * c = copy (rank, s, k): the gradient of moe_combine with respect to rank
+ * `rank`'s router weights (the combine is linear in each weight).  Products
+ * and sums in fp32: each thread sums its 16-byte vectors of the row in row
+ * order, then a fixed-order reduction over the block, so the result is
+ * deterministic; 0 for copies with dest_pos < 0.  [blog] "Real-World Use".
+ *   y_all [R*S*K, width] as in moe_combine, dout [S, width] (this rank's
+ *   output-gradient rows), dw [S*K] fp32, width*elem % 16 == 0.
+ * ------------------------------------------------------------------------- */
+moe_status_t moe_combine_weight_grad(const moe_dims *dims, moe_dtype dtype, int64_t width,
+                                     int32_t rank, const void *y_all, const int32_t *dest_pos,
+                                     const void *dout, float *dw, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_replica_grad_fold -- fold rank `rank`'s replica weight-gradient rows
  * into their home expert rows: for each used slot j holding expert e,
  * dw[e] += dw[E+j] (fp32), then dw[E+j] = 0.  [ainovat] mechanism paragraph

@@ -119,3 +119,28 @@ def check_close(got_bits, ref_bits, dtype, tol=None, min_identical=0.98, what=""
     err = rel_inf(got, ref)
     assert err <= tol, f"{what}: max rel err {err:.3e} > {tol:.1e}"
     return err
+
+
+def router_grad_bound(y, dest, dout, rank, S, K, dtype, width, tokens=None):
+    """Error bound of the GPU router-weight gradient against the float64 definition.
+
+    Each GPU thread sums its 16-byte vectors of the row in order (ceil(vec/256) vectors of
+    8 bf16 or 4 fp32 products), then 6 butterfly levels and the 4 waves of the block add up
+    the partial sums: n = terms per thread + 8 fp32 roundings on any path, so
+    |err| <= n * 2^-24 * sum_h |g_h y_h|, plus half an ulp for the reference's own rounding
+    to float32.  Returns the [tokens, K] bound.
+    """
+    wide = (lambda a: oracle.bf16_bits_to_f64(a)) if dtype == "bf16" else (lambda a: np.asarray(a, np.float64))
+    per_vec = 8 if dtype == "bf16" else 4
+    vec = width // per_vec
+    n = ((vec + 255) // 256) * per_vec + 8
+    toks = np.arange(S) if tokens is None else np.asarray(tokens)
+    bound = np.zeros((toks.size, K))
+    dp = np.asarray(dest).reshape(-1)
+    for t, s_ in enumerate(toks):
+        gs = np.abs(wide(dout[int(s_)]))
+        for k in range(K):
+            dd = int(dp[(rank * S + int(s_)) * K + k])
+            if dd >= 0:
+                bound[t, k] = n * 2.0 ** -24 * float(np.dot(gs, np.abs(wide(y[dd]))))
+    return bound + 1e-30

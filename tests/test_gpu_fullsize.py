@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from gpu_common import check_close, log
+from gpu_common import check_close, log, router_grad_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -62,8 +62,9 @@ def _gpu():
 @pytest.mark.parametrize("name,target", WORKLOADS)
 def test_full_size_step(name, target):
     from balanced_token_dispatch_amd import (GEMM_DGRAD, GEMM_FWD, GEMM_WGRAD, moe_combine,
-                                             moe_dispatch_layout, moe_group_gemm, moe_permute,
-                                             moe_plan, moe_prefetch, moe_replica_grad_fold)
+                                             moe_combine_weight_grad, moe_dispatch_layout,
+                                             moe_group_gemm, moe_permute, moe_plan, moe_prefetch,
+                                             moe_replica_grad_fold, moe_unpermute_reduce)
     from balanced_token_dispatch_amd.layer import LayerStep, Shape
     wl = synth.WORKLOADS[name]
     d = wl.dims
@@ -78,6 +79,7 @@ def test_full_size_step(name, target):
     synth.fill_normal_(L.w_down, 0.02, seed * 10 + 3)
     synth.fill_normal_(L.y_all, 1.0, seed * 10 + 4)
     synth.fill_normal_(L.dout_all, 1.0, seed * 10 + 5)
+    synth.fill_normal_(L.dxp_all, 1.0, seed * 10 + 6)   # the peers' slices; rank 0's is recomputed
     L.topk_idx.copy_(torch.from_numpy(idx))
     L.topk_w.copy_(torch.from_numpy(w))
     SK, S, K, E, B, H, Hp, G = d.SK, d.S, d.K, d.E, d.B, d.H, d.Hp, d.G
@@ -215,6 +217,24 @@ def test_full_size_step(name, target):
                             torch.as_tensor(jj2, device="cuda")].cpu().numpy()
         assert np.abs(got2 - ent2).max() <= 1e-3 * max(1.0, np.abs(ent2).max()), (got2, ent2)
         log(f"  wgrad entries of segment {rho} ({hi - lo} rows) within tolerance")
+    # router-weight gradient and un-permute reduce of the sampled tokens, on the rows the
+    # GPU produced (rank 0's expert outputs and input gradients, the peers' staged rows)
+    moe_combine_weight_grad(L.d, rank, L.y_all, L.dest, L.dout_all[rank * S:(rank + 1) * S],
+                            L.dtopk_w)
+    moe_unpermute_reduce(L.d, rank, L.dxp_all, L.dest, L.dx)
+    torch.cuda.synchronize()
+    y_gpu = host_rows(L.y_all, need)
+    g_full = np.zeros((S, H), np.uint16)
+    g_full[tok_s] = host_rows(L.dout_all, rank * S + np.array(tok_s))
+    dw_ref = oracle.combine_weight_grad(y_gpu, dest_l, g_full, rank, S, K, "bf16", tokens=tok_s)
+    dw_got = L.dtopk_w.view(S, K)[torch.as_tensor(tok_s, device="cuda")].cpu().numpy()
+    bound = router_grad_bound(y_gpu, dest_l, g_full, rank, S, K, "bf16", H, tokens=tok_s)
+    err = np.abs(dw_got.astype(np.float64) - dw_ref.astype(np.float64))
+    assert (err <= bound + np.abs(dw_ref) * 2.0 ** -24).all(), (dw_got, dw_ref)
+    dx_ref = oracle.unpermute_reduce(host_rows(L.dxp_all, need), dest_l, rank, S, K, "bf16",
+                                     tokens=tok_s)
+    check_close(host_rows(L.dx, tok_s), dx_ref, "bf16", what="un-permute reduce tokens")
+    log(f"  router-weight gradient and un-permute reduce of {len(tok_s)} tokens within tolerance")
     # fold: home rows gain the slot rows, slot rows end zero (bitwise, on a sampled column block)
     cols = slice(0, 4096)
     before = {int(e): (L.dw_up[e].view(-1)[cols].cpu().numpy(),

@@ -14,6 +14,7 @@ import torch
 import oracle
 import synth
 from gpu_common import (GpuPlan, bits, check_close, check_plan_layout, from_bits, log, mod,
+                        router_grad_bound,
                         poisoned)
 
 pytestmark = pytest.mark.gpu
@@ -187,6 +188,78 @@ def test_combine_integer_exact():
     out = poisoned((S, W), torch.bfloat16)
     m.moe_combine(d, 1, from_bits(y), _dev(dest), _dev(w), out)
     assert (bits(out) == oracle.combine(y, dest, w, 1, S, K, "bf16")).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("K", [2, 8, 17])
+def test_unpermute_reduce(dtype, K):
+    R, S, E, B, W = 3, 200, 24, 2, 264
+    idx, pl = _plan_for(R, S, K, E, B, 7 + K)
+    m = mod()
+    d = m.dims(R, S, K, E, B)
+    _, dest, _ = oracle.layout(idx, pl, 0)
+    dest = dest.copy()
+    dest[5::41] = -1                         # copies without a destination add nothing
+    g = synth.host_normal(12, 2, (R * S * K, W))
+    g = synth.to_bf16_bits(g) if dtype == "bf16" else g
+    for rank in (0, R - 1):
+        dx = poisoned((S, W), torch.bfloat16 if dtype == "bf16" else torch.float32)
+        m.moe_unpermute_reduce(d, rank, from_bits(g), _dev(dest), dx)
+        ref = oracle.unpermute_reduce(g, dest, rank, S, K, dtype)
+        check_close(bits(dx), ref, dtype, what=f"unpermute reduce K={K} rank={rank}")
+
+
+def test_unpermute_reduce_integer_exact():
+    R, S, K, E, B, W = 4, 128, 8, 32, 4, 520
+    idx, pl = _plan_for(R, S, K, E, B, 22)
+    m = mod()
+    d = m.dims(R, S, K, E, B)
+    _, dest, _ = oracle.layout(idx, pl, 2)
+    g = synth.to_bf16_bits(synth.host_ternary(4, 3, (R * S * K, W)))
+    dx = poisoned((S, W), torch.bfloat16)
+    m.moe_unpermute_reduce(d, 2, from_bits(g), _dev(dest), dx)
+    assert (bits(dx) == oracle.unpermute_reduce(g, dest, 2, S, K, "bf16")).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("K,W", [(2, 264), (8, 1064), (17, 4104)])
+def test_combine_weight_grad(dtype, K, W):
+    R, S, E, B = 3, 150, 24, 2
+    idx, pl = _plan_for(R, S, K, E, B, 13 + K)
+    m = mod()
+    d = m.dims(R, S, K, E, B)
+    _, dest, _ = oracle.layout(idx, pl, 0)
+    dest = dest.copy()
+    dest[3::29] = -1
+    y = synth.host_normal(14, 2, (R * S * K, W))
+    gout = synth.host_normal(15, 3, (S, W))
+    if dtype == "bf16":
+        y, gout = synth.to_bf16_bits(y), synth.to_bf16_bits(gout)
+    for rank in (0, R - 1):
+        dw = poisoned((S * K,), torch.float32)
+        m.moe_combine_weight_grad(d, rank, from_bits(y), _dev(dest), from_bits(gout), dw)
+        got = dw.cpu().numpy().reshape(S, K)
+        ref = oracle.combine_weight_grad(y, dest, gout, rank, S, K, dtype)
+        none = np.asarray(dest).reshape(R, S, K)[rank] < 0
+        assert (got[none] == 0).all(), "copies without a destination get a zero gradient"
+        bound = router_grad_bound(y, dest, gout, rank, S, K, dtype, W)
+        err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+        # the oracle's float32 rounding of its float64 result adds half an ulp
+        assert (err <= bound + np.abs(ref) * 2.0 ** -24).all(), f"max excess {(err - bound).max()}"
+
+
+def test_combine_weight_grad_integer_exact():
+    R, S, K, E, B, W = 4, 96, 8, 32, 4, 2048
+    idx, pl = _plan_for(R, S, K, E, B, 23)
+    m = mod()
+    d = m.dims(R, S, K, E, B)
+    _, dest, _ = oracle.layout(idx, pl, 3)
+    y = synth.to_bf16_bits(synth.host_ternary(5, 3, (R * S * K, W)))
+    gout = synth.to_bf16_bits(synth.host_ternary(6, 4, (S, W)))
+    dw = poisoned((S * K,), torch.float32)
+    m.moe_combine_weight_grad(d, 3, from_bits(y), _dev(dest), from_bits(gout), dw)
+    ref = oracle.combine_weight_grad(y, dest, gout, 3, S, K, "bf16")
+    assert (dw.cpu().numpy().reshape(S, K) == ref).all()
 
 
 def test_fold_and_prefetch():

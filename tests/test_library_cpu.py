@@ -29,7 +29,8 @@ def mod():
 def test_header_declares_the_path():
     fns = declared_functions()
     for name in ("moe_plan", "moe_dispatch_layout", "moe_permute", "moe_group_gemm",
-                 "moe_combine", "moe_replica_grad_fold", "moe_prefetch"):
+                 "moe_combine", "moe_replica_grad_fold", "moe_prefetch", "moe_unpermute_reduce",
+                 "moe_combine_weight_grad"):
         assert name in fns
 
 
@@ -69,6 +70,12 @@ def test_host_validation_rejects_before_launch(mod):
     assert lib.moe_permute(by(d), mod.BF16, 12, P, P, None, P, None) == mod.MOE_EINVAL  # 24 B rows
     assert lib.moe_permute(by(d), 7, 16, P, P, None, P, None) == mod.MOE_EINVAL
     assert lib.moe_combine(by(d), mod.BF16, 16, -1, P, P, P, P, None) == mod.MOE_EINVAL
+    assert lib.moe_unpermute_reduce(by(d), mod.BF16, 16, 4, P, P, P, None) == mod.MOE_EINVAL
+    assert lib.moe_unpermute_reduce(by(d), mod.BF16, 12, 0, P, P, P, None) == mod.MOE_EINVAL
+    assert lib.moe_unpermute_reduce(by(d), mod.F32, 16, 0, None, P, P, None) == mod.MOE_EINVAL
+    assert lib.moe_combine_weight_grad(by(d), mod.BF16, 16, -1, P, P, P, P, None) == mod.MOE_EINVAL
+    assert lib.moe_combine_weight_grad(by(d), mod.F32, 6, 0, P, P, P, P, None) == mod.MOE_EINVAL
+    assert lib.moe_combine_weight_grad(by(d), mod.BF16, 16, 0, P, P, None, P, None) == mod.MOE_EINVAL
     assert lib.moe_replica_grad_fold(by(d), 0, P, P, 6, None) == mod.MOE_EINVAL
     assert lib.moe_prefetch(by(d), 0, P, P, 8, None) == mod.MOE_EINVAL
     gg = lib.moe_group_gemm
