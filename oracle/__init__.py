@@ -18,6 +18,9 @@ are listed per function in the tests:
   gradients, its input gradient and its router-weight gradient exactly on
   small-integer inputs; ``unpermute_reduce`` is also checked as the adjoint
   of ``permute``.
+* ``silu``, ``group_gemm_swiglu``, ``swiglu_backward`` (the gated variant):
+  scipy's logistic function, closed forms (silu(x) - silu(-x) = x), central
+  differences of the forward, and a dense gated MoE written copy by copy.
 * ``bf16``: torch's CPU cast on sampled bit patterns.
 
 Parity unpinned: any specific plan versus the original library's planner
@@ -26,7 +29,8 @@ Parity unpinned: any specific plan versus the original library's planner
 from .moe_ref import (  # noqa: F401
     STATUS_BAD_EXPERT_ID, STATUS_SLOT_OVERFLOW, HEADER_WORDS, Plan, Replica, maxvio, histogram,
     plan, plan_words, layout, layout_loops, permute, group_gemm, group_gemm_rows, wgrad_entries,
-    combine, replica_grad_fold, prefetch, unpermute_reduce, combine_weight_grad,
+    combine, replica_grad_fold, prefetch, unpermute_reduce, combine_weight_grad, silu,
+    group_gemm_swiglu, swiglu_backward,
 )
 from .bf16 import (  # noqa: F401
     bf16_bits_to_f32, bf16_bits_to_f64, f32_to_bf16_bits, f64_to_bf16_bits,

@@ -439,6 +439,57 @@ def group_gemm(op: str, a, b, cu, dtype="bf16", out=None):
     return res
 
 
+def silu(x64):
+    """x * sigma(x), sigma(x) = 1 / (1 + exp(-x)), in float64 (the SiLU / swish-1 function)."""
+    x64 = np.asarray(x64, np.float64)
+    with np.errstate(over="ignore"):
+        return x64 / (1.0 + np.exp(-x64))
+
+
+def group_gemm_swiglu(a, b, cu, dtype="bf16"):
+    """Gated (SwiGLU) up-projection over the grouped weight tensor.
+
+    The pages name no activation; a gated unit is the usual framework
+    variant.  READING: W[rho] has 2N' columns interleaved as (gate, up)
+    pairs; h = a[seg] @ W[rho] in float64 from exactly widened inputs;
+    z[:, j] = silu(h[:, 2j]) * h[:, 2j+1], both z and the pre-activation h
+    rounded once to the row type.  Returns (z [M, N'], h [M, 2N']); rows
+    outside every segment are zero.
+    """
+    cu = np.asarray(cu, np.int64)
+    G, M, N2 = cu.shape[0] - 1, a.shape[0], b.shape[2]
+    odt = np.uint16 if dtype == "bf16" else np.float32
+    z = np.zeros((M, N2 // 2), odt)
+    h = np.zeros((M, N2), odt)
+    for rho in range(G):
+        lo, hi = int(cu[rho]), int(cu[rho + 1])
+        if hi <= lo:
+            continue
+        h64 = _widen(a[lo:hi], dtype) @ _widen(b[rho], dtype)
+        z[lo:hi] = _narrow(silu(h64[:, 0::2]) * h64[:, 1::2], dtype)
+        h[lo:hi] = _narrow(h64, dtype)
+    return z, h
+
+
+def swiglu_backward(dz, h, dtype="bf16"):
+    """Gradient of the gated unit with respect to its pre-activation h (interleaved pairs).
+
+    READING: from the stored (rounded) pre-activation g = h[:, 2j],
+    u = h[:, 2j+1] and the output gradient dz[:, j], in float64:
+    dh[:, 2j] = dz * u * silu'(g), dh[:, 2j+1] = dz * silu(g), with
+    silu'(x) = sigma(x) * (1 + x * (1 - sigma(x))); one rounding.
+    """
+    hh = _widen(h, dtype)
+    g, u = hh[:, 0::2], hh[:, 1::2]
+    d = _widen(dz, dtype)
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-g))
+    out = np.empty(hh.shape, np.float64)
+    out[:, 0::2] = d * u * sg * (1.0 + g * (1.0 - sg))
+    out[:, 1::2] = d * g * sg
+    return _narrow(out, dtype)
+
+
 def group_gemm_rows(op: str, a, b, cu, rows, dtype="bf16"):
     """Selected output rows of ``group_gemm`` ("fwd"/"dgrad"), computed one row at a time.
 
