@@ -25,7 +25,8 @@ GEMM_FWD, GEMM_DGRAD, GEMM_WGRAD = 0, 1, 2
 EXPORTS = ("moe_status_string", "moe_plan_words", "moe_plan_workspace_bytes", "moe_plan",
            "moe_dispatch_layout_workspace_bytes", "moe_dispatch_layout", "moe_prefetch",
            "moe_permute", "moe_group_gemm", "moe_combine", "moe_replica_grad_fold",
-           "moe_unpermute_reduce", "moe_combine_weight_grad")
+           "moe_unpermute_reduce", "moe_combine_weight_grad", "moe_group_gemm_swiglu",
+           "moe_swiglu_backward")
 
 
 class MoeDims(ctypes.Structure):
@@ -52,6 +53,9 @@ _lib.moe_combine.argtypes = [_D, ctypes.c_int, _I64, _I32, _P, _P, _P, _P, _P]
 _lib.moe_replica_grad_fold.argtypes = [_D, _I32, _P, _P, _I64, _P]
 _lib.moe_unpermute_reduce.argtypes = [_D, ctypes.c_int, _I64, _I32, _P, _P, _P, _P]
 _lib.moe_combine_weight_grad.argtypes = [_D, ctypes.c_int, _I64, _I32, _P, _P, _P, _P, _P]
+_lib.moe_group_gemm_swiglu.argtypes = [ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
+                                       _P]
+_lib.moe_swiglu_backward.argtypes = [ctypes.c_int, _I64, _I64, _P, _P, _P, _P]
 for _n in EXPORTS[3:]:
     if _n.endswith("_bytes"):
         continue
@@ -134,6 +138,19 @@ def moe_group_gemm(op, a, b, cu_seqlens, out, Kd, N, stream=None):
     G = cu_seqlens.numel() - 1
     _check(_lib.moe_group_gemm(op, _dtype(a), G, a.shape[0], Kd, N, _ptr(a), _ptr(b),
                                _ptr(cu_seqlens), _ptr(out), _stream(stream)), "moe_group_gemm")
+
+
+def moe_group_gemm_swiglu(a, b, cu_seqlens, z, h, Kd, N, stream=None):
+    """Gated up-projection: z = silu(gate) * up over (gate, up) column pairs of W; h optional."""
+    G = cu_seqlens.numel() - 1
+    _check(_lib.moe_group_gemm_swiglu(_dtype(a), G, a.shape[0], Kd, N, _ptr(a), _ptr(b),
+                                      _ptr(cu_seqlens), _ptr(z), _ptr(h), _stream(stream)),
+           "moe_group_gemm_swiglu")
+
+
+def moe_swiglu_backward(h, dz, dh, stream=None):
+    _check(_lib.moe_swiglu_backward(_dtype(h), dz.shape[0], dz.shape[1], _ptr(h), _ptr(dz),
+                                    _ptr(dh), _stream(stream)), "moe_swiglu_backward")
 
 
 def moe_combine(d, rank, y_all, dest_pos, topk_w, out, stream=None):

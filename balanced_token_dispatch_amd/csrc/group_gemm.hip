@@ -126,16 +126,15 @@ __device__ inline void dma_issue(const DmaOp &d, uint32_t lds_op, uint32_t wave_
     // has no register result (nothing in flight can overwrite a VGPR); the "memory"
     // clobber keeps LDS accesses on their side of it; completion is ordered only by the
     // explicit vmcnt waits and barriers of the K loop.
-    // M0 is written inside the same asm, one wait state ahead of the load: on this
-    // architecture family an LDS-DMA load must not read M0 in the cycle after a scalar
-    // write to it (the compiler pads its own LDS-DMA loads the same way).
+    // M0 is set by the compiler from the "{m0}" operand; the asm starts with one wait
+    // state, because on this architecture family an LDS-DMA load must not read M0 in the
+    // cycle after a scalar write to it (the compiler pads its own LDS-DMA loads the same way).
     const uint32_t m0 = lds_op + wave_off + u * kWaves * 1024;
     asm volatile(
-        "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
         "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off),
-        "s"(rs), "s"(m0)
-        : "memory", "m0");
+        "s"(rs), "{m0}"(m0)
+        : "memory");
   }
 }
 
@@ -393,10 +392,47 @@ __device__ inline void epilogue_bf16(uint16_t *lds, const f32x16 (&acc)[TM][TN],
   __syncthreads();
 }
 
+// Gated (SwiGLU) output: W's columns come in (gate, up) pairs, so each lane's 4 consecutive
+// accumulator columns hold two pairs and z = silu(gate) * up is register-local.  The 256 x 128
+// z tile (64 KB bf16) leaves through LDS like the bf16 epilogue: chunk (8 z values) c of row i
+// at c ^ (i & 15), then 16-byte row segments, 256 B per row.  cols (valid z columns of the
+// tile) is a multiple of 8.
+constexpr int kOpSwiglu = 3;  // internal op: FWD main loop, gated epilogue
+
+__device__ inline float silu_f32(float x) { return x / (1.0f + __expf(-x)); }
+
+__device__ inline void epilogue_swiglu(uint16_t *lds, const f32x16 (&acc)[TM][TN], uint16_t *o,
+                                       long long ld, int rows, int cols, int wi, int wj,
+                                       int lane) {
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int i = wi + tm * 32 + (lane & 31);
+        const int jz = (wj + tn * 32 + g * 8 + (lane >> 5) * 4) >> 1;  // even z column
+        const f32x16 &a = acc[tm][tn];
+        const uint32_t v = pack_bf16x2(silu_f32(a[4 * g + 0]) * a[4 * g + 1],
+                                       silu_f32(a[4 * g + 2]) * a[4 * g + 3]);
+        *(uint32_t *)(lds + i * 128 + ((jz >> 3) ^ (i & 15)) * 8 + (jz & 7)) = v;
+      }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {  // 512 threads: 32 rows x 16 chunks per pass
+    const int i = (threadIdx.x >> 4) + 32 * r;
+    const int c = threadIdx.x & 15;
+    const u32x4 v = *(const u32x4 *)(lds + i * 128 + (c ^ (i & 15)) * 8);
+    if (i < rows && c * 8 < cols) *(u32x4 *)(o + i * ld + c * 8) = v;
+  }
+  __syncthreads();
+}
+
 template <int OP, bool RAGGED>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
-    const int32_t *__restrict__ cu, void *__restrict__ out, int G, int M_total, int Kd, int N) {
+    const int32_t *__restrict__ cu, void *__restrict__ out, void *__restrict__ out2, int G,
+    int M_total, int Kd, int N) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * STAGE_ELEMS];
   __shared__ int sCu[kMaxG + 1], sStart[kMaxG + 1];
   const bool wgrad = OP == MOE_GEMM_WGRAD;
@@ -423,7 +459,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
       const uint16_t *w = b + (size_t)rho * Kd * N;
       TileArgs ta;
       ta.wave_off = wave_off;
-      if (OP == MOE_GEMM_FWD) {
+      if (OP == MOE_GEMM_FWD || OP == kOpSwiglu) {
         dma_init<true>(ta.a, a + (size_t)m0 * Kd, (long long)rows * Kd * 2, Kd, rows);
         dma_init<false>(ta.b, w + j0, ((long long)Kd * N - j0) * 2, N, N - j0);
         ta.c_len = Kd;
@@ -433,12 +469,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
         ta.c_len = N;
       }
       ta.nk = (ta.c_len + BK - 1) / BK;
-      if (OP == MOE_GEMM_FWD)
+      if (OP == MOE_GEMM_FWD || OP == kOpSwiglu)
         tile_mma<true, false, RAGGED>(lds, ta, acc);
       else
         tile_mma<true, true, RAGGED>(lds, ta, acc);
-      epilogue_bf16(lds, acc, (uint16_t *)out + (size_t)m0 * ncols + j0, ncols, rows,
-                    ncols - j0, wi, wj, lane, wid);
+      if (OP == kOpSwiglu) {
+        // out = z [M, N/2], out2 = pre-activation h [M, N] (optional)
+        if (out2)
+          epilogue_bf16(lds, acc, (uint16_t *)out2 + (size_t)m0 * N + j0, N, rows, N - j0, wi,
+                        wj, lane, wid);
+        epilogue_swiglu(lds, acc, (uint16_t *)out + (size_t)m0 * (N / 2) + j0 / 2, N / 2, rows,
+                        (N - j0) / 2, wi, wj, lane);
+      } else {
+        epilogue_bf16(lds, acc, (uint16_t *)out + (size_t)m0 * ncols + j0, ncols, rows,
+                      ncols - j0, wi, wj, lane, wid);
+      }
     } else {
       const int per_seg = n_it * n_ct;
       const int sidx = (int)(t / per_seg);
@@ -580,22 +625,42 @@ extern "C" moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t 
     case MOE_GEMM_FWD:
       if (Kd % BK)
         hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_FWD, true>), dim3(grid), dim3(kGemmThreads), 0,
-                           stream, a16, b16, cu_seqlens, out, G, M_total, Kd, N);
+                           stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
       else
         hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_FWD, false>), dim3(grid), dim3(kGemmThreads),
-                           0, stream, a16, b16, cu_seqlens, out, G, M_total, Kd, N);
+                           0, stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
       break;
     case MOE_GEMM_DGRAD:
       if (N % BK)
         hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_DGRAD, true>), dim3(grid), dim3(kGemmThreads),
-                           0, stream, a16, b16, cu_seqlens, out, G, M_total, Kd, N);
+                           0, stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
       else
         hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_DGRAD, false>), dim3(grid), dim3(kGemmThreads),
-                           0, stream, a16, b16, cu_seqlens, out, G, M_total, Kd, N);
+                           0, stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
       break;
     default:
       hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_WGRAD, false>), dim3(grid), dim3(kGemmThreads), 0,
-                         stream, a16, b16, cu_seqlens, out, G, M_total, Kd, N);
+                         stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
   }
+  return launch_status();
+}
+
+extern "C" moe_status_t moe_group_gemm_swiglu(moe_dtype dtype, int32_t G, int32_t M_total,
+                                              int32_t Kd, int32_t N, const void *a,
+                                              const void *b, const int32_t *cu_seqlens,
+                                              void *z, void *h, hipStream_t stream) {
+  if (!a || !b || !cu_seqlens || !z) return MOE_EINVAL;
+  if (dtype != MOE_BF16) return MOE_EINVAL;
+  if (G < 1 || G > kMaxG || M_total < 0 || Kd < 8 || N < 16 || Kd % 8 || N % 16) return MOE_EINVAL;
+  if ((long long)M_total * (Kd > N ? Kd : N) >= (1LL << 40)) return MOE_EINVAL;
+  if (M_total == 0) return MOE_OK;
+  const int grid = device_cu_count();
+  const uint16_t *a16 = (const uint16_t *)a, *b16 = (const uint16_t *)b;
+  if (Kd % BK)
+    hipLaunchKernelGGL((k_ggemm_bf16<kOpSwiglu, true>), dim3(grid), dim3(kGemmThreads), 0, stream,
+                       a16, b16, cu_seqlens, z, h, G, M_total, Kd, N);
+  else
+    hipLaunchKernelGGL((k_ggemm_bf16<kOpSwiglu, false>), dim3(grid), dim3(kGemmThreads), 0, stream,
+                       a16, b16, cu_seqlens, z, h, G, M_total, Kd, N);
   return launch_status();
 }

@@ -229,6 +229,55 @@ __global__ __launch_bounds__(kRowThreads) void k_combine_wgrad(const u32x4 *__re
   }
 }
 
+// Gated-unit backward, elementwise over (gate, up) pairs: with g, u the stored pre-activation
+// pair and d the output gradient, dh_gate = d * u * silu'(g), dh_up = d * silu(g), in fp32,
+// one rounding.  The arrays are flat (row-major, no padding): output-gradient vector v (8
+// bf16 or 4 fp32 pairs) goes with pre-activation vectors 2v and 2v+1.  One-shot grid.
+template <bool BF16>
+__global__ __launch_bounds__(kRowThreads) void k_swiglu_bwd(const u32x4 *__restrict__ h,
+                                                           const u32x4 *__restrict__ dz,
+                                                           u32x4 *__restrict__ dh, long long n_vec) {
+  constexpr int kChunk = kRowThreads * kStreamU;
+  for (long long base = (long long)blockIdx.x * kChunk; base < n_vec;
+       base += (long long)gridDim.x * kChunk) {
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+      const long long v = base + u * kRowThreads + threadIdx.x;
+      if (v >= n_vec) break;
+      const u32x4 d = dz[v], h0 = h[2 * v], h1 = h[2 * v + 1];
+      u32x4 o0, o1;
+      if (BF16) {
+        // pair q of d (q = 0..7) is (gate, up) = word q of the 16-value h pair h0|h1
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t hw = q < 4 ? h0[q] : h1[q - 4];
+          const float g = bf16_lo(hw), up = bf16_hi(hw);
+          const float dd = (q & 1) ? bf16_hi(d[q >> 1]) : bf16_lo(d[q >> 1]);
+          const float sg = 1.0f / (1.0f + __expf(-g));
+          const uint32_t r = pack_bf16x2(dd * up * sg * (1.0f + g * (1.0f - sg)), dd * g * sg);
+          if (q < 4) o0[q] = r; else o1[q - 4] = r;
+        }
+      } else {
+        const f32x4 df = __builtin_bit_cast(f32x4, d);
+        const f32x4 a = __builtin_bit_cast(f32x4, h0), b = __builtin_bit_cast(f32x4, h1);
+        f32x4 r0, r1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float g = q < 2 ? a[2 * q] : b[2 * (q - 2)];
+          const float up = q < 2 ? a[2 * q + 1] : b[2 * (q - 2) + 1];
+          const float sg = 1.0f / (1.0f + __expf(-g));
+          const float dg = df[q] * up * sg * (1.0f + g * (1.0f - sg)), du = df[q] * g * sg;
+          if (q < 2) { r0[2 * q] = dg; r0[2 * q + 1] = du; } else { r1[2 * (q - 2)] = dg; r1[2 * (q - 2) + 1] = du; }
+        }
+        o0 = __builtin_bit_cast(u32x4, r0);
+        o1 = __builtin_bit_cast(u32x4, r1);
+      }
+      __builtin_nontemporal_store(o0, dh + 2 * v);
+      __builtin_nontemporal_store(o1, dh + 2 * v + 1);
+    }
+  }
+}
+
 // dw[e] += dw[E+j]; dw[E+j] = 0 for every used slot j of `rank`.  grid (chunks, B);
 // a block covers kRowThreads*kStreamU vectors of one slot row.
 __global__ __launch_bounds__(kRowThreads) void k_fold(const int32_t *__restrict__ plan,
@@ -433,5 +482,24 @@ extern "C" moe_status_t moe_prefetch(const moe_dims *d, int32_t rank, const int3
                   d->B);
   hipLaunchKernelGGL(k_prefetch, grid, dim3(kRowThreads), 0, stream, plan, (u32x4 *)w, d->E,
                      d->R, d->B, rank, vec);
+  return launch_status();
+}
+
+extern "C" moe_status_t moe_swiglu_backward(moe_dtype dtype, int64_t rows, int64_t n_pairs,
+                                            const void *h, const void *dz, void *dh,
+                                            hipStream_t stream) {
+  if (!h || !dz || !dh || rows < 0 || n_pairs <= 0) return MOE_EINVAL;
+  const int eb = elem_bytes(dtype);
+  if (!eb || (n_pairs * eb) % 16 != 0) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  const long long n_vec = rows * n_pairs * eb / 16;
+  const dim3 grid(clamp_grid((n_vec + kRowThreads * kStreamU - 1) / (kRowThreads * kStreamU),
+                             kMaxGridX));
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(k_swiglu_bwd<true>, grid, dim3(kRowThreads), 0, stream, (const u32x4 *)h,
+                       (const u32x4 *)dz, (u32x4 *)dh, n_vec);
+  else
+    hipLaunchKernelGGL(k_swiglu_bwd<false>, grid, dim3(kRowThreads), 0, stream,
+                       (const u32x4 *)h, (const u32x4 *)dz, (u32x4 *)dh, n_vec);
   return launch_status();
 }

@@ -186,6 +186,35 @@ moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t G, int32_t 
                             const int32_t *cu_seqlens, void *out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_group_gemm_swiglu -- the FWD grouped GEMM with a gated (SwiGLU) epilogue:
+ * h = a @ W[rho] per segment as in moe_group_gemm(FWD), W's N columns taken as
+ * (gate, up) pairs (column 2j is gate j, 2j+1 is up j), and
+ * z[:, j] = silu(h[:, 2j]) * h[:, 2j+1], silu(x) = x / (1 + exp(-x)), computed in
+ * fp32 from the fp32 accumulators and rounded once (RNE).  The pages name no
+ * activation ([ainovat] contract names only the two projections); the gated
+ * unit is the usual framework variant and the interleaved pairs keep it local
+ * to the accumulators.  bf16 only.
+ *   a [M_total, Kd], b = W [G, Kd, N] (N % 16 == 0), cu_seqlens as in
+ *   moe_group_gemm, z [M_total, N/2] bf16, h [M_total, N] bf16 or NULL (the
+ *   pre-activation, rounded once, kept for moe_swiglu_backward).
+ * ------------------------------------------------------------------------- */
+moe_status_t moe_group_gemm_swiglu(moe_dtype dtype, int32_t G, int32_t M_total, int32_t Kd,
+                                   int32_t N, const void *a, const void *b,
+                                   const int32_t *cu_seqlens, void *z, void *h,
+                                   hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_swiglu_backward -- gradient of the gated unit with respect to its
+ * pre-activation, elementwise over pairs: with (g, u) = (h[:, 2j], h[:, 2j+1])
+ * and d = dz[:, j], dh[:, 2j] = d * u * silu'(g) and dh[:, 2j+1] = d * silu(g),
+ * silu'(x) = s(x) (1 + x (1 - s(x))), s the logistic function; fp32, one RNE.
+ *   h [rows, 2 n_pairs], dz [rows, n_pairs], dh [rows, 2 n_pairs], all of the
+ *   given dtype, row-major without padding; n_pairs * elem % 16 == 0.
+ * ------------------------------------------------------------------------- */
+moe_status_t moe_swiglu_backward(moe_dtype dtype, int64_t rows, int64_t n_pairs, const void *h,
+                                 const void *dz, void *dh, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_combine -- out[s] = sum_k topk_w[c] * y_all[dest_pos[c]], c = copy
  * (rank, s, k), fp32 accumulation in ascending k, one RNE rounding; copies
  * with dest_pos < 0 add nothing.  [blog] "What This Does" / "Real-World

@@ -144,3 +144,19 @@ def router_grad_bound(y, dest, dout, rank, S, K, dtype, width, tokens=None):
             if dd >= 0:
                 bound[t, k] = n * 2.0 ** -24 * float(np.dot(gs, np.abs(wide(y[dd]))))
     return bound + 1e-30
+
+
+def within_one_bf16_ulp(got_bits, ref_bits, what=""):
+    """Every element within one bf16 rounding step of the reference.
+
+    For results computed in fp32 (relative error ~1e-6, far below bf16's half-ulp of 2^-9)
+    and rounded once, the rounded values can differ only where the exact value sits next to
+    a rounding boundary, and then by one unit in the last place.
+    """
+    g = oracle.bf16_bits_to_f64(np.asarray(got_bits))
+    r = oracle.bf16_bits_to_f64(np.asarray(ref_bits))
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    mag = np.maximum(np.abs(g), np.abs(r))
+    ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-300))) - 7), 0.0)
+    bad = np.abs(g - r) > ulp + 1e-30
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond one ulp, e.g. {g[bad][:4]} vs {r[bad][:4]}"

@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 from gpu_common import (GpuPlan, bits, check_close, check_plan_layout, from_bits, log, mod,
-                        router_grad_bound,
+                        router_grad_bound, within_one_bf16_ulp,
                         poisoned)
 
 pytestmark = pytest.mark.gpu
@@ -431,3 +431,125 @@ def test_tiny_f32_workload_end_to_end():
     Y_ref[rank * d.SK:(rank + 1) * d.SK] = y_ref
     out_ref = oracle.combine(Y_ref, dest, topk_w, rank, d.S, d.K, "f32")
     check_close(out.cpu().numpy(), out_ref, "f32", what="tiny combine")
+
+
+# ------------------------------------------------------------------------------------------
+# gated (SwiGLU) variant
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G,M,Kd,N", [(5, 700, 64, 256), (6, 1000, 136, 400), (3, 2100, 520, 528),
+                                      (9, 257, 1408, 4096)])
+def test_group_gemm_swiglu(G, M, Kd, N):
+    rng = np.random.default_rng(G * 1000 + N)
+    m = mod()
+    cu = _segments(rng, G, M)
+    a = synth.to_bf16_bits(rng.standard_normal((M, Kd)).astype(np.float32))
+    W = synth.to_bf16_bits((rng.standard_normal((G, Kd, N)) * (2.0 / np.sqrt(Kd))).astype(np.float32))
+    z = poisoned((M, N // 2), torch.bfloat16)
+    h = poisoned((M, N), torch.bfloat16)
+    m.moe_group_gemm_swiglu(from_bits(a), from_bits(W), _dev(cu), z, h, Kd, N)
+    z_ref, h_ref = oracle.group_gemm_swiglu(a, W, cu, "bf16")
+    rows = np.arange(cu[0], cu[-1])
+    check_close(bits(h)[rows], h_ref[rows], "bf16", what=f"swiglu pre-activation {G},{M},{Kd},{N}")
+    # normwise bf16 tolerance as for every GEMM output: a per-element bound does not hold where
+    # the gate or up pre-activation is a near-cancelling sum (fp32 vs float64 accumulation)
+    check_close(bits(z)[rows], z_ref[rows], "bf16", min_identical=0.95,
+                what=f"swiglu z {G},{M},{Kd},{N}")
+    # z alone (no pre-activation output) gives the same z
+    z2 = poisoned((M, N // 2), torch.bfloat16)
+    m.moe_group_gemm_swiglu(from_bits(a), from_bits(W), _dev(cu), z2, None, Kd, N)
+    assert (bits(z2)[rows] == bits(z)[rows]).all()
+
+
+def test_group_gemm_swiglu_integer_preactivation():
+    """On ternary inputs the pre-activation is exact, so it must match the FWD GEMM bit for bit."""
+    rng = np.random.default_rng(3)
+    G, M, Kd, N = 4, 900, 256, 512
+    m = mod()
+    cu = _segments(rng, G, M)
+    a = synth.to_bf16_bits(synth.host_ternary(1, 1, (M, Kd)))
+    W = synth.to_bf16_bits(synth.host_ternary(1, 2, (G, Kd, N)))
+    z = poisoned((M, N // 2), torch.bfloat16)
+    h = poisoned((M, N), torch.bfloat16)
+    m.moe_group_gemm_swiglu(from_bits(a), from_bits(W), _dev(cu), z, h, Kd, N)
+    z_ref, h_ref = oracle.group_gemm_swiglu(a, W, cu, "bf16")
+    rows = np.arange(cu[0], cu[-1])
+    assert (bits(h)[rows] == h_ref[rows]).all()
+    # the pre-activation is exact here, so z differs from the oracle only by fp32 SiLU and
+    # one rounding: within one bf16 unit in the last place everywhere
+    within_one_bf16_ulp(bits(z)[rows], z_ref[rows], what="swiglu z on ternary inputs")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_swiglu_backward(dtype):
+    rng = np.random.default_rng(11)
+    M, Np = 1000, 264
+    h = (rng.standard_normal((M, 2 * Np)) * 2.5).astype(np.float32)
+    dz = rng.standard_normal((M, Np)).astype(np.float32)
+    if dtype == "bf16":
+        h, dz = synth.to_bf16_bits(h), synth.to_bf16_bits(dz)
+    m = mod()
+    dh = poisoned((M, 2 * Np), torch.bfloat16 if dtype == "bf16" else torch.float32)
+    m.moe_swiglu_backward(from_bits(h), from_bits(dz), dh)
+    ref = oracle.swiglu_backward(dz, h, dtype)
+    check_close(bits(dh), ref, dtype, tol=2e-2 if dtype == "bf16" else 1e-5,
+                min_identical=0.95, what=f"swiglu backward {dtype}")
+
+
+def test_gated_layer_step_against_oracle():
+    """Tiny gated layer on rank 0: dispatch, gated up, down, combine, and the backward through
+    the gated unit (down DGRAD, swiglu backward, up DGRAD, both WGRADs), stage by stage."""
+    R, S, K, E, B, H, Hp = 4, 96, 2, 16, 2, 64, 48
+    idx, pl = _plan_for(R, S, K, E, B, 33)
+    m = mod()
+    d = m.dims(R, S, K, E, B)
+    G, SK, rank = E + B, S * K, 0
+    cu, dest, src = oracle.layout(idx, pl, rank)
+    rng = np.random.default_rng(4)
+    x = synth.to_bf16_bits(rng.standard_normal((R * S, H)).astype(np.float32))
+    Wu = synth.to_bf16_bits((rng.standard_normal((G, H, 2 * Hp)) * 0.25).astype(np.float32))
+    Wd = synth.to_bf16_bits((rng.standard_normal((G, Hp, H)) * 0.25).astype(np.float32))
+    dout = synth.to_bf16_bits(rng.standard_normal((R * S, H)).astype(np.float32))
+    w = rng.random(R * S * K).astype(np.float32)
+    Wu_d, Wd_d = from_bits(Wu), from_bits(Wd)
+    plan_d = _dev(pl.to_blob())
+    m.moe_prefetch(d, rank, plan_d, Wu_d)
+    m.moe_prefetch(d, rank, plan_d, Wd_d)
+    Wu_r, Wd_r = oracle.prefetch(Wu, pl, rank), oracle.prefetch(Wd, pl, rank)
+    xp = poisoned((SK, H), torch.bfloat16)
+    m.moe_permute(d, from_bits(x), _dev(src), xp)
+    z = poisoned((SK, Hp), torch.bfloat16)
+    hpre = poisoned((SK, 2 * Hp), torch.bfloat16)
+    cu_d = _dev(cu)
+    m.moe_group_gemm_swiglu(xp, Wu_d, cu_d, z, hpre, H, 2 * Hp)
+    y = poisoned((SK, H), torch.bfloat16)
+    m.moe_group_gemm(m.GEMM_FWD, z, Wd_d, cu_d, y, Hp, H)
+    xp_r = oracle.permute(x, src, K)
+    assert (bits(xp) == xp_r).all()
+    z_r, h_r = oracle.group_gemm_swiglu(xp_r, Wu_r, cu, "bf16")
+    check_close(bits(hpre), h_r, "bf16", what="gated layer pre-activation")
+    check_close(bits(z), z_r, "bf16", min_identical=0.95, what="gated layer z")
+    # downstream stages take the GPU's own z so each comparison tests one kernel
+    y_r = oracle.group_gemm("fwd", bits(z), Wd_r, cu, "bf16")
+    check_close(bits(y), y_r, "bf16", what="gated layer down projection")
+    dy = poisoned((SK, H), torch.bfloat16)
+    m.moe_permute(d, from_bits(dout), _dev(src), dy, row_scale=_dev(w))
+    dz = poisoned((SK, Hp), torch.bfloat16)
+    m.moe_group_gemm(m.GEMM_DGRAD, dy, Wd_d, cu_d, dz, Hp, H)
+    dh = poisoned((SK, 2 * Hp), torch.bfloat16)
+    m.moe_swiglu_backward(hpre, dz, dh)
+    dxp = poisoned((SK, H), torch.bfloat16)
+    m.moe_group_gemm(m.GEMM_DGRAD, dh, Wu_d, cu_d, dxp, H, 2 * Hp)
+    dWu = torch.zeros((G, H, 2 * Hp), dtype=torch.float32, device="cuda")
+    m.moe_group_gemm(m.GEMM_WGRAD, xp, dh, cu_d, dWu, H, 2 * Hp)
+    dy_r = oracle.permute(dout, src, K, row_scale=w)
+    assert (bits(dy) == dy_r).all()
+    dz_r = oracle.group_gemm("dgrad", dy_r, Wd_r, cu, "bf16")
+    check_close(bits(dz), dz_r, "bf16", what="gated layer down dgrad")
+    dh_r = oracle.swiglu_backward(bits(dz), bits(hpre), "bf16")
+    check_close(bits(dh), dh_r, "bf16", min_identical=0.95, what="gated layer swiglu backward")
+    dxp_r = oracle.group_gemm("dgrad", bits(dh), Wu_r, cu, "bf16")
+    check_close(bits(dxp), dxp_r, "bf16", what="gated layer up dgrad")
+    dWu_r = oracle.group_gemm("wgrad", xp_r, bits(dh), cu, "bf16",
+                              out=np.zeros((G, H, 2 * Hp), np.float32))
+    check_close(dWu.cpu().numpy(), dWu_r, "f32", tol=1e-4, what="gated layer up wgrad")

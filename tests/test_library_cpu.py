@@ -30,7 +30,7 @@ def test_header_declares_the_path():
     fns = declared_functions()
     for name in ("moe_plan", "moe_dispatch_layout", "moe_permute", "moe_group_gemm",
                  "moe_combine", "moe_replica_grad_fold", "moe_prefetch", "moe_unpermute_reduce",
-                 "moe_combine_weight_grad"):
+                 "moe_combine_weight_grad", "moe_group_gemm_swiglu", "moe_swiglu_backward"):
         assert name in fns
 
 
@@ -83,6 +83,12 @@ def test_host_validation_rejects_before_launch(mod):
     assert gg(mod.GEMM_FWD, mod.BF16, 0, 256, 16, 16, P, P, P, P, None) == mod.MOE_EINVAL
     assert gg(5, mod.BF16, 18, 256, 16, 16, P, P, P, P, None) == mod.MOE_EINVAL
     assert gg(mod.GEMM_FWD, mod.BF16, 18, 256, 16, 16, None, P, P, P, None) == mod.MOE_EINVAL
+    sw = lib.moe_group_gemm_swiglu
+    assert sw(mod.BF16, 18, 256, 16, 24, P, P, P, P, None, None) == mod.MOE_EINVAL  # N%16
+    assert sw(mod.F32, 18, 256, 16, 32, P, P, P, P, None, None) == mod.MOE_EINVAL   # bf16 only
+    assert sw(mod.BF16, 18, 256, 16, 32, P, P, P, None, None, None) == mod.MOE_EINVAL
+    assert lib.moe_swiglu_backward(mod.BF16, 4, 4, P, P, P, None) == mod.MOE_EINVAL  # 8 B rows
+    assert lib.moe_swiglu_backward(mod.F32, 4, 8, None, P, P, None) == mod.MOE_EINVAL
     assert lib.moe_status_string(mod.MOE_ENOSPACE).startswith(b"workspace")
 
 
