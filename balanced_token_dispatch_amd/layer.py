@@ -14,7 +14,11 @@ adjoint for the weights) -> down DGRAD -> down WGRAD -> up DGRAD (into rank
 r's slice of the all-ranks input-gradient buffer) -> up WGRAD -> un-permute
 reduce of the input gradients to the tokens (dispatch's adjoint) -> fold the
 replica rows of both weight gradients into their home experts.
-The activation between the projections is the identity.
+The activation between the projections is the identity, or, with
+``activation="swiglu"``, the gated linear unit: the up projection then has
+2H' columns holding (gate, up) pairs, its GEMM writes both the pre-activation
+h and z = silu(gate) * up, and the backward turns dz into dh with the gated
+unit's derivative before the up projection's DGRAD and WGRAD.
 """
 from dataclasses import dataclass
 
@@ -22,8 +26,8 @@ import torch
 
 from . import (GEMM_DGRAD, GEMM_FWD, GEMM_WGRAD, dims as _mk_dims, dispatch_layout_workspace_bytes,
                moe_combine, moe_combine_weight_grad, moe_dispatch_layout, moe_group_gemm,
-               moe_permute, moe_plan, moe_prefetch, moe_replica_grad_fold, moe_unpermute_reduce,
-               plan_words, plan_workspace_bytes)
+               moe_group_gemm_swiglu, moe_permute, moe_plan, moe_prefetch, moe_replica_grad_fold,
+               moe_swiglu_backward, moe_unpermute_reduce, plan_words, plan_workspace_bytes)
 
 
 @dataclass
@@ -47,9 +51,14 @@ class Shape:
 
 class LayerStep:
     def __init__(self, shape: Shape, rank: int = 0, dtype=torch.bfloat16, device="cuda",
-                 backward: bool = True):
+                 backward: bool = True, activation: str = "identity"):
         s = shape
+        if activation not in ("identity", "swiglu"):
+            raise ValueError(f"activation {activation!r}")
         self.s, self.rank, self.dtype, self.device = s, rank, dtype, device
+        self.activation = activation
+        # gated: the up projection has 2H' columns, (gate, up) pairs interleaved
+        self.up_cols = 2 * s.Hp if activation == "swiglu" else s.Hp
         self.d = _mk_dims(s.R, s.S, s.K, s.E, s.B)
         i32 = dict(dtype=torch.int32, device=device)
         f32 = dict(dtype=torch.float32, device=device)
@@ -65,10 +74,12 @@ class LayerStep:
         self.dest = torch.zeros(s.R * s.SK, **i32)
         self.src = torch.zeros(s.SK, **i32)
         self.x_all = torch.zeros((s.R * s.S, s.H), **act)
-        self.w_up = torch.zeros((s.G, s.H, s.Hp), **act)
+        self.w_up = torch.zeros((s.G, s.H, self.up_cols), **act)
         self.w_down = torch.zeros((s.G, s.Hp, s.H), **act)
         self.xp = torch.zeros((s.SK, s.H), **act)
         self.z = torch.zeros((s.SK, s.Hp), **act)
+        # gated: the pre-activation, kept for the backward
+        self.hpre = torch.zeros((s.SK, self.up_cols), **act) if activation == "swiglu" else None
         self.y_all = torch.zeros((s.R * s.SK, s.H), **act)
         self.out = torch.zeros((s.S, s.H), **act)
         self.backward_enabled = backward
@@ -76,13 +87,14 @@ class LayerStep:
             self.dout_all = torch.zeros((s.R * s.S, s.H), **act)
             self.dy = torch.zeros((s.SK, s.H), **act)
             self.dz = torch.zeros((s.SK, s.Hp), **act)
+            self.dh = torch.zeros((s.SK, self.up_cols), **act) if activation == "swiglu" else None
             # every rank's input-gradient rows in the layout's order; this rank's DGRAD writes
             # its slice, the other slices stand in for the peers' (the un-permute reduce reads
             # a token's K copies wherever they were processed)
             self.dxp_all = torch.zeros((s.R * s.SK, s.H), **act)
             self.dx = torch.zeros((s.S, s.H), **act)
             self.dtopk_w = torch.zeros(s.SK, **f32)
-            self.dw_up = torch.zeros((s.G, s.H, s.Hp), **f32)
+            self.dw_up = torch.zeros((s.G, s.H, self.up_cols), **f32)
             self.dw_down = torch.zeros((s.G, s.Hp, s.H), **f32)
 
     @property
@@ -113,8 +125,12 @@ class LayerStep:
         c(timer, "prefetch", moe_prefetch, self.d, r, self.plan, self.w_up)
         c(timer, "prefetch", moe_prefetch, self.d, r, self.plan, self.w_down)
         c(timer, "permute", moe_permute, self.d, self.x_all, self.src, self.xp)
-        c(timer, "gemm_fwd", moe_group_gemm, GEMM_FWD, self.xp, self.w_up, self.cu, self.z, s.H,
-          s.Hp)
+        if self.activation == "swiglu":
+            c(timer, "gemm_fwd_swiglu", moe_group_gemm_swiglu, self.xp, self.w_up, self.cu, self.z,
+              self.hpre, s.H, self.up_cols)
+        else:
+            c(timer, "gemm_fwd", moe_group_gemm, GEMM_FWD, self.xp, self.w_up, self.cu, self.z,
+              s.H, s.Hp)
         c(timer, "gemm_fwd", moe_group_gemm, GEMM_FWD, self.z, self.w_down, self.cu, self.y, s.Hp,
           s.H)
         c(timer, "combine", moe_combine, self.d, r, self.y_all, self.dest,
@@ -130,10 +146,14 @@ class LayerStep:
           s.Hp, s.H)
         c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.z, self.dy, self.cu, self.dw_down,
           s.Hp, s.H)
-        c(timer, "gemm_dgrad", moe_group_gemm, GEMM_DGRAD, self.dz, self.w_up, self.cu, self.dxp,
-          s.H, s.Hp)
-        c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.xp, self.dz, self.cu, self.dw_up,
-          s.H, s.Hp)
+        dup = self.dz
+        if self.activation == "swiglu":
+            c(timer, "swiglu_bwd", moe_swiglu_backward, self.hpre, self.dz, self.dh)
+            dup = self.dh
+        c(timer, "gemm_dgrad", moe_group_gemm, GEMM_DGRAD, dup, self.w_up, self.cu, self.dxp,
+          s.H, self.up_cols)
+        c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.xp, dup, self.cu, self.dw_up,
+          s.H, self.up_cols)
         c(timer, "unpermute_reduce", moe_unpermute_reduce, self.d, r, self.dxp_all, self.dest,
           self.dx)
         c(timer, "fold", moe_replica_grad_fold, self.d, r, self.plan, self.dw_up)

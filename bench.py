@@ -12,7 +12,11 @@ entry of the dominant kernel (HIP events around every launch in the timed region
 step at maxvio 0 and 1 (per-rank time flatness), and the CPU oracle timed on a bounded sample
 of the same step on this host.
 
+With --activation swiglu the up projection is the gated unit (2H' columns as (gate, up)
+pairs, silu(gate)*up in the GEMM epilogue, its derivative in a row kernel in the backward).
+
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-sweep]
+                       [--activation identity|swiglu]
 """
 import argparse
 import json
@@ -58,6 +62,7 @@ KERNEL_SOURCES = {  # bench kernel name -> (rocprof name prefix, source files th
     "gemm_fwd": ("moe::k_ggemm_bf16<0", ("group_gemm.hip", "common.hpp")),
     "gemm_dgrad": ("moe::k_ggemm_bf16<1", ("group_gemm.hip", "common.hpp")),
     "gemm_wgrad": ("moe::k_ggemm_bf16<2", ("group_gemm.hip", "common.hpp")),
+    "gemm_fwd_swiglu": ("moe::k_ggemm_bf16<3", ("group_gemm.hip", "common.hpp")),
     "permute": ("moe::k_permute<false>", ("rows.hip", "common.hpp")),
     "permute_weighted": ("moe::k_permute<true>", ("rows.hip", "common.hpp")),
     "combine": ("moe::k_combine<true, true>", ("rows.hip", "common.hpp")),
@@ -65,6 +70,7 @@ KERNEL_SOURCES = {  # bench kernel name -> (rocprof name prefix, source files th
     "unpermute_reduce": ("moe::k_combine<true, false>", ("rows.hip", "common.hpp")),
     "fold": ("moe::k_fold", ("rows.hip", "common.hpp")),
     "prefetch": ("moe::k_prefetch", ("rows.hip", "common.hpp")),
+    "swiglu_bwd": ("moe::k_swiglu_bwd<true>", ("rows.hip", "common.hpp")),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_skew8_fwdbwd.md")
 COPY_BYTES = 1 << 30          # calibration copy: reads and writes exactly this many bytes
@@ -131,28 +137,37 @@ def render_traffic(fetch_csv, write_csv):
     print("\n".join(out))
 
 
-def algorithmic_work(shape, n_slots_used):
-    """Minimum bytes (or flops) per launch of each kernel of the step."""
+def algorithmic_work(shape, n_slots_used, gated=False):
+    """Minimum bytes (or flops) per launch of each kernel of the step.
+
+    Kernels launched once per projection (prefetch, fold, DGRAD, WGRAD) report the mean over
+    the step's launches; with the gated unit the up projection is twice as wide as the down.
+    """
     R, S, K, E, H, Hp = shape.R, shape.S, shape.K, shape.E, shape.H, shape.Hp
     SK = S * K
     gemm = 2.0 * SK * H * Hp
+    up = 2.0 if gated else 1.0
+    both = (1.0 + up) / 2.0
     return {
         "plan": ("hbm", 4.0 * R * SK + 4.0 * R * E),
         "dispatch_layout": ("hbm", 8.0 * R * SK + 4.0 * SK),
-        "prefetch": ("hbm", 2.0 * n_slots_used * H * Hp * 2),
+        "prefetch": ("hbm", 2.0 * n_slots_used * H * Hp * 2 * both),
         "permute": ("hbm", 2.0 * SK * H * 2 + 4.0 * SK),
         "gemm_fwd": ("mfma", gemm),
+        "gemm_fwd_swiglu": ("mfma", 2.0 * gemm),
         "combine": ("hbm", SK * H * 2.0 + S * H * 2.0 + 8.0 * SK),
         "permute_weighted": ("hbm", 2.0 * SK * H * 2 + 8.0 * SK),
-        "gemm_dgrad": ("mfma", gemm),
-        "gemm_wgrad": ("mfma", gemm),
-        "fold": ("hbm", 3.0 * n_slots_used * H * Hp * 4),
+        "gemm_dgrad": ("mfma", gemm * both),
+        "gemm_wgrad": ("mfma", gemm * both),
+        "fold": ("hbm", 3.0 * n_slots_used * H * Hp * 4 * both),
         "combine_wgrad": ("hbm", SK * H * 2.0 + S * H * 2.0 + 8.0 * SK),
         "unpermute_reduce": ("hbm", SK * H * 2.0 + S * H * 2.0 + 4.0 * SK),
+        # reads h [SK, 2H'] and dz [SK, H'], writes dh [SK, 2H'] (bf16)
+        "swiglu_bwd": ("hbm", SK * Hp * 2.0 * 5),
     }
 
 
-def setup_layer(wl, target, rank, placement="receiver0", layer=None):
+def setup_layer(wl, target, rank, placement="receiver0", layer=None, activation="identity"):
     import numpy as np
     import torch
     import synth
@@ -163,7 +178,8 @@ def setup_layer(wl, target, rank, placement="receiver0", layer=None):
     idx, w = synth.routing(d, zipf, wl.base_seed, placement)
     log(f"routing {wl.name} maxvio target {target}: zipf s={zipf:.4f}, {time.time() - t0:.1f}s")
     if layer is None:
-        layer = LayerStep(Shape(d.R, d.S, d.K, d.E, d.B, d.H, d.Hp), rank=rank)
+        layer = LayerStep(Shape(d.R, d.S, d.K, d.E, d.B, d.H, d.Hp), rank=rank,
+                          activation=activation)
         seed = wl.base_seed
         synth.fill_normal_(layer.x_all, 1.0, seed * 10 + 1)
         synth.fill_normal_(layer.w_up, 0.02, seed * 10 + 2)
@@ -213,8 +229,8 @@ def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
     """The oracle as it stands, on a bounded sample of the same step, scaled to tokens/s.
 
     Timed on this host: the full plan and layout of all R ranks' routing, then permute,
-    both projections forward, the weighted permute, both DGRADs and WGRADs on the first
-    ``rows_sample`` rows of rank r's buffer, the combine, router-weight gradient and
+    both projections forward (with the gated unit, when the layer has it), the weighted
+    permute, both DGRADs and WGRADs on the first ``rows_sample`` rows of rank r's buffer, the combine, router-weight gradient and
     un-permute reduce of ``tokens_sample`` tokens, and the fold on 1/8 of each replica row.
     Each part is scaled to the full step.
     """
@@ -247,14 +263,19 @@ def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
         if cu_s[rho + 1] > cu_s[rho]:
             wu[rho], wd[rho]
     t0 = time.perf_counter()
+    gated = layer.activation == "swiglu"
     xp = oracle.permute(x_rows, src_l.astype(np.int32), s.K)
-    z = oracle.group_gemm("fwd", xp, wu, cu_s)
+    if gated:
+        z, h = oracle.group_gemm_swiglu(xp, wu, cu_s)
+    else:
+        z = oracle.group_gemm("fwd", xp, wu, cu_s)
     oracle.group_gemm("fwd", z, wd, cu_s)
     dy = oracle.permute(g_rows, src_l.astype(np.int32), s.K, row_scale=w_flat)
     dz = oracle.group_gemm("dgrad", dy, wd, cu_s)
-    oracle.group_gemm("dgrad", dz, wu, cu_s)
+    dup = oracle.swiglu_backward(dz, h) if gated else dz
+    oracle.group_gemm("dgrad", dup, wu, cu_s)
     act = [rho for rho in range(s.G) if cu_s[rho + 1] > cu_s[rho]]
-    for a, b, K_, N_ in ((z, dy, s.Hp, s.H), (xp, dz, s.H, s.Hp)):
+    for a, b, K_, N_ in ((z, dy, s.Hp, s.H), (xp, dup, s.H, layer.up_cols)):
         for rho in act:                          # wgrad of the sampled segments only
             lo, hi = cu_s[rho], cu_s[rho + 1]
             sub = np.array([0, hi - lo])
@@ -279,10 +300,11 @@ def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
     oracle.unpermute_reduce(dxp_rows, dest_l, r, s.S, s.K, tokens=ts)
     t["combine"] = time.perf_counter() - t0
     frac = 8
-    dw = np.zeros((s.G, s.H * s.Hp // frac), np.float32)
+    dw_u = np.zeros((s.G, s.H * layer.up_cols // frac), np.float32)
+    dw_d = np.zeros((s.G, s.H * s.Hp // frac), np.float32)
     t0 = time.perf_counter()
-    oracle.replica_grad_fold(dw, pl, r)
-    oracle.replica_grad_fold(dw, pl, r)
+    oracle.replica_grad_fold(dw_u, pl, r)
+    oracle.replica_grad_fold(dw_d, pl, r)
     t["fold"] = (time.perf_counter() - t0) * frac
     est = (t["plan"] + t["layout"] + t["rows"] * s.SK / max(n, 1)
            + t["combine"] * s.S / max(len(ts), 1) + t["fold"])
@@ -309,6 +331,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32768)
     ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--activation", choices=("identity", "swiglu"), default="identity",
+                    help="activation between the projections (swiglu: gated up projection)")
     ap.add_argument("--probe", action="store_true",
                     help="one warm-up step, a 1 GiB calibration copy, one step (for --pmc runs)")
     ap.add_argument("--render-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -330,7 +354,7 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     target = wl.maxvio_targets[-1] if wl.maxvio_targets[-1] is not None else None
-    layer, idx, w, info = setup_layer(wl, target, args.rank)
+    layer, idx, w, info = setup_layer(wl, target, args.rank, activation=args.activation)
     s = layer.s
     if args.probe:
         layer.step()
@@ -356,7 +380,7 @@ def main():
     ms_step = elapsed * 1000.0 / args.steps
     value = s.S * args.steps / elapsed
 
-    work = algorithmic_work(s, n_slots)
+    work = algorithmic_work(s, n_slots, gated=args.activation == "swiglu")
     kernels = {}
     totals = {}
     for name, times in timer.ms().items():
@@ -429,7 +453,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "R": s.R, "S": s.S, "K": s.K, "E": s.E, "B": s.B,
-                   "H": s.H, "H_prime": s.Hp, "rank": args.rank, "step": "forward+backward",
+                   "H": s.H, "H_prime": s.Hp, "activation": args.activation,
+                   "rank": args.rank, "step": "forward+backward",
                    "maxvio": round(info["maxvio"], 3), "zipf_s": info["zipf_s"],
                    "plan_status": status, "replica_slots_used_on_rank": n_slots},
         "roofline": roof,

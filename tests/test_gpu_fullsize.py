@@ -252,3 +252,101 @@ def test_full_size_step(name, target):
     del L
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def test_full_size_gated_step():
+    """The gated layer at the headline shape (H=7168, H'=2048, up projection 7168 x 4096),
+    run as the benchmark runs it (LayerStep.forward + backward, activation="swiglu"); the
+    pre-activation, z, y, dz, dh, dxp rows and up-WGRAD entries are checked on sampled rows,
+    each recomputed by the oracle from the generated inputs alone."""
+    from balanced_token_dispatch_amd.layer import LayerStep, Shape
+    wl = synth.WORKLOADS["skew8_large_fwdbwd"]
+    d = wl.dims
+    rank = 0
+    idx, w = synth.routing(d, synth.zipf_for(wl, 8.0), wl.base_seed)
+    log(f"full size gated step maxvio={synth.realised_maxvio(idx, d.E):.3f}")
+    L = LayerStep(Shape(d.R, d.S, d.K, d.E, d.B, d.H, d.Hp), rank=rank, activation="swiglu")
+    seed = wl.base_seed
+    synth.fill_normal_(L.x_all, 1.0, seed * 10 + 1)
+    synth.fill_normal_(L.w_up, 0.02, seed * 10 + 2)
+    synth.fill_normal_(L.w_down, 0.02, seed * 10 + 3)
+    synth.fill_normal_(L.y_all, 1.0, seed * 10 + 4)
+    synth.fill_normal_(L.dout_all, 1.0, seed * 10 + 5)
+    synth.fill_normal_(L.dxp_all, 1.0, seed * 10 + 6)
+    L.topk_idx.copy_(torch.from_numpy(idx))
+    L.topk_w.copy_(torch.from_numpy(w))
+    SK, S, K, E, B, H, Hp, G = d.SK, d.S, d.K, d.E, d.B, d.H, d.Hp, d.G
+    L.forward()
+    L.dw_up.zero_()
+    L.dw_down.zero_()
+    L.backward()
+    torch.cuda.synchronize()
+    pl = oracle.plan(idx, E, B)
+    cu, dest, src = oracle.layout(idx, pl, rank)
+    assert (L.cu.cpu().numpy() == cu).all() and (L.src.cpu().numpy() == src).all()
+    Wu, Wd = HostWeights(L.w_up, pl, rank), HostWeights(L.w_down, pl, rank)
+    assert Wu.shape == (G, H, 2 * Hp)
+    se, _, _ = pl.slot_table()
+    homes = {int(e) for e in se[rank] if e >= 0}
+    rng = np.random.default_rng(seed + 1)
+    act = [rho for rho in range(G) if cu[rho + 1] > cu[rho]]
+    slots = [rho for rho in act if rho >= E]
+    plain = [rho for rho in act if rho < E and rho not in homes]
+    pick = sorted(set(rng.choice(plain, size=min(2, len(plain)), replace=False).tolist())
+                  | set(slots[:1]))
+    rows = []
+    for rho in pick:
+        lo, hi = int(cu[rho]), int(cu[rho + 1])
+        rows += [lo, hi - 1] + rng.integers(lo, hi, size=4).tolist()
+    rows = np.array(sorted(set(rows)), np.int64)
+    seg = np.searchsorted(cu, rows, side="right") - 1
+    cu_c = compact_cu(seg, G)
+    toks = src[rows] // K
+    x_rows = host_rows(L.x_all, toks)
+    z_ref, h_ref = oracle.group_gemm_swiglu(x_rows, Wu, cu_c, "bf16")
+    check_close(host_rows(L.hpre, rows), h_ref, "bf16", what="gated pre-activation rows")
+    check_close(host_rows(L.z, rows), z_ref, "bf16", min_identical=0.95, what="gated z rows")
+    _, y_ref = oracle.group_gemm_rows("fwd", z_ref, Wd, cu_c, np.arange(rows.size))
+    check_close(host_rows(L.y, rows), y_ref, "bf16", what="down projection rows (gated)")
+    g_rows = host_rows(L.dout_all, toks)
+    src_l = (np.arange(rows.size) * K + src[rows] % K).astype(np.int32)
+    rs = np.zeros(rows.size * K, np.float32)
+    rs[src_l] = w.reshape(-1)[src[rows]]
+    dy_ref = oracle.permute(g_rows, src_l, K, row_scale=rs)
+    assert (host_rows(L.dy, rows) == dy_ref).all(), "weighted permute rows"
+    _, dz_ref = oracle.group_gemm_rows("dgrad", dy_ref, Wd, cu_c, np.arange(rows.size))
+    check_close(host_rows(L.dz, rows), dz_ref, "bf16", what="down dgrad rows (gated)")
+    dh_ref = oracle.swiglu_backward(dz_ref, h_ref, "bf16")
+    # dh compounds the last-place differences of dz, gate and up: fewer identical elements
+    check_close(host_rows(L.dh, rows), dh_ref, "bf16", min_identical=0.85,
+                what="gated backward rows")
+    _, dxp_ref = oracle.group_gemm_rows("dgrad", dh_ref, Wu, cu_c, np.arange(rows.size))
+    # its input dh already differs in the last place from the GPU's in up to 15% of elements,
+    # so the rounded sums agree less often; the normwise bound is the same
+    check_close(host_rows(L.dxp, rows), dxp_ref, "bf16", min_identical=0.95,
+                what="up dgrad rows (gated)")
+    log(f"  gated forward/backward rows within tolerance ({rows.size} rows, segments {pick})")
+    # up-WGRAD entries of the smallest sampled home-expert segment (no fold touches it)
+    rho = min([r_ for r_ in pick if r_ < E], key=lambda r_: cu[r_ + 1] - cu[r_])
+    lo, hi = int(cu[rho]), int(cu[rho + 1])
+    if hi - lo <= 4096:
+        seg_rows = np.arange(lo, hi)
+        stoks = src[seg_rows] // K
+        xs = host_rows(L.x_all, stoks)
+        cu1 = np.array([0] * (rho + 1) + [hi - lo] * (G - rho), np.int64)
+        _, hs = oracle.group_gemm_swiglu(xs, Wu, cu1, "bf16")
+        gs = host_rows(L.dout_all, stoks)
+        dys = oracle.permute(gs, (np.arange(hi - lo) * K).astype(np.int32), K,
+                             row_scale=np.repeat(w.reshape(-1)[src[seg_rows]], K).astype(np.float32))
+        _, dzs = oracle.group_gemm_rows("dgrad", dys, Wd, cu1, np.arange(hi - lo))
+        dhs = oracle.swiglu_backward(dzs, hs, "bf16")
+        ii = rng.integers(0, H, 8)
+        jj = rng.integers(0, 2 * Hp, 8)
+        ent = oracle.wgrad_entries(xs, dhs, np.array([0, hi - lo]), 0, ii, jj, "bf16")
+        got = L.dw_up[rho][torch.as_tensor(ii, device="cuda"),
+                           torch.as_tensor(jj, device="cuda")].cpu().numpy()
+        assert np.abs(got - ent).max() <= 1e-3 * max(1.0, np.abs(ent).max()), (got, ent)
+        log(f"  gated up-WGRAD entries of segment {rho} ({hi - lo} rows) within tolerance")
+    del L
+    gc.collect()
+    torch.cuda.empty_cache()
