@@ -11,7 +11,10 @@ are listed per function in the tests:
   (tests/golden), invariants on random and adversarial routings, brute-force
   optimal replica counts on tiny inputs, and special cases that reduce to a
   stable argsort / bincount (one rank) or to plain expert parallelism
-  (balanced routing).
+  (balanced routing).  The relay fallback inside ``plan``: hand-worked relay
+  and switch chains, exhaustive search on tiny routings (it finds a plan
+  within B slots whenever one exists there) and a mixed-integer feasibility
+  check on medium ones.
 * ``permute``, ``group_gemm``, ``combine``, ``replica_grad_fold``,
   ``unpermute_reduce``, ``combine_weight_grad``: a simulation of every rank
   that must reproduce the dense MoE definition, its per-expert weight

@@ -107,9 +107,10 @@ class Plan:
     n_donors: int
     n_receivers: int
     n_pieces: int
-    max_needed: int             # most replicas any one rank was asked to host
+    max_needed: int             # most replicas any one rank was asked to host by the walk
     rep_first: np.ndarray = field(default=None)
     rep_n: np.ndarray = field(default=None)
+    n_relayed: int = 0          # walk replicas placed by the relay fallback
 
     @property
     def E_loc(self):
@@ -155,7 +156,7 @@ class Plan:
         """int32 words: header, T, keep, rep_first, rep_n, replica list, slot tables.
 
         header = [status, n_replicas, max_needed, n_donors, n_receivers,
-        n_pieces, 0, 0]; the replica list holds E+R entries of each of
+        n_pieces, n_relayed, 0]; the replica list holds E+R entries of each of
         (expert, rank, slot, start, count), unused entries (-1, -1, -1, 0, 0);
         the slot tables are [R*B] each of (expert, start, count).
         """
@@ -167,7 +168,7 @@ class Plan:
             re[i], rq[i], rs[i], rst[i], rc[i] = m.expert, m.rank, m.slot, m.start, m.count
         se, ss, sc = self.slot_table()
         hdr = np.array([self.status, len(self.replicas), self.max_needed, self.n_donors,
-                        self.n_receivers, self.n_pieces, 0, 0], np.int64)
+                        self.n_receivers, self.n_pieces, self.n_relayed, 0], np.int64)
         blob = np.concatenate([hdr, self.T, self.keep, self.rep_first, self.rep_n,
                                re, rq, rs, rst, rc, se.ravel(), ss.ravel(), sc.ravel()])
         assert blob.size == plan_words(R, E, B)
@@ -201,8 +202,10 @@ def plan(topk_idx: np.ndarray, E: int, B: int) -> Plan:
          receiver carrying x = min(piece left, deficit left) copies, taken
          from e's copy order starting at keep_e + (part of the piece already
          emitted); whichever runs out advances
-      6. replicas on a receiver take slots 0, 1, ... in emission order; a
-         replica beyond slot B-1 is dropped and STATUS_SLOT_OVERFLOW is set
+      6. replicas on a receiver take slots 0, 1, ... in emission order; when
+         a receiver would need more than B slots the relay fallback
+         (``relay_fallback``) re-places the walk's replicas; a replica it
+         cannot place is dropped and STATUS_SLOT_OVERFLOW is set
     """
     R, S, K = topk_idx.shape
     SK = S * K
@@ -259,8 +262,11 @@ def plan(topk_idx: np.ndarray, E: int, B: int) -> Plan:
         m.slot = hosted[m.rank] if hosted[m.rank] < B else -1
         hosted[m.rank] += 1
     max_needed = max(hosted) if R else 0
+    n_relayed = 0
     if max_needed > B:
-        status |= STATUS_SLOT_OVERFLOW
+        replicas, keep, n_relayed, dropped = relay_fallback(replicas, keep, E_loc, R, B)
+        if dropped:
+            status |= STATUS_SLOT_OVERFLOW
 
     rep_first = np.zeros(E, np.int64)
     rep_n = np.zeros(E, np.int64)
@@ -271,7 +277,117 @@ def plan(topk_idx: np.ndarray, E: int, B: int) -> Plan:
 
     return Plan(R=R, S=S, K=K, E=E, B=B, status=status, counts=C, T=T, keep=keep,
                 replicas=replicas, n_donors=len(donors), n_receivers=len(receivers),
-                n_pieces=len(pieces), max_needed=max_needed, rep_first=rep_first, rep_n=rep_n)
+                n_pieces=len(pieces), max_needed=max_needed, rep_first=rep_first, rep_n=rep_n,
+                n_relayed=n_relayed)
+
+
+def relay_fallback(walk, keep, E_loc: int, R: int, B: int):
+    """Re-place the walk's replicas when a receiver would need more than B slots.
+
+    [ainovat] invariant paragraph: every rank gets exactly S*K copies
+    whatever the skew; the donor-to-receiver walk alone cannot always keep
+    within B slots per rank.  READING (the pages give no algorithm; a
+    one-hop relay through a donor):
+
+    The walk's replicas (expert f, receiver q, x copies) are taken again in
+    emission order.  "Place n copies of e on rank a" means: add them to
+    keep_e if a is e's home; else add them to the replica of e that a
+    already hosts; else open a replica of e on a in a's next free slot;
+    else it fails.  For each walk replica:
+      1. place the x copies of f on q directly;
+      2. otherwise (q is full) relay through q: for q's replicas (e, c) in
+         slot order, the first with keep_e >= x whose home A can take x
+         copies of f: q's replica of e grows by x (taken from keep_e), and A
+         takes the x copies of f instead of q;
+      3. otherwise switch: for q's replicas (e, c) in slot order, the first
+         with keep_f >= c whose home-of-f F can take c copies of e: that
+         replica becomes a replica of f with c + x copies (c of them taken
+         from keep_f), and F takes the c copies of e;
+      4. otherwise the replica is dropped (slot -1, its copies get no
+         destination).
+    Every step keeps each rank's load and each expert's total, so a plan
+    with nothing dropped gives every rank exactly S*K copies.  Relays land
+    only on donors (homes of pieced experts).  Each walk replica gives at
+    most one new entry, so the list never outgrows the walk's.
+
+    Afterwards the entries of each expert are gathered together (experts in
+    the order of their first entry, entries of one expert in pass order),
+    and an expert's copies are tiled home first, then its entries in that
+    order: start = keep_e + the counts of its earlier entries.  When
+    nothing overflows the walk's list is returned unchanged.
+    Returns (replicas, keep, number of relayed or switched replicas,
+    number dropped).
+    """
+    keep = keep.copy()
+    out = []                               # entries in pass order
+    on_rank = [[] for _ in range(R)]       # indices into out, in slot order
+
+    def home(e):
+        return e // E_loc
+
+    def entry_of(a, e):
+        for i in on_rank[a]:
+            if out[i].expert == e:
+                return i
+        return -1
+
+    def can_place(e, a):
+        return a == home(e) or entry_of(a, e) >= 0 or len(on_rank[a]) < B
+
+    def place(e, a, n):
+        if a == home(e):
+            keep[e] += n
+            return
+        i = entry_of(a, e)
+        if i >= 0:
+            out[i].count += n
+            return
+        assert len(on_rank[a]) < B
+        out.append(Replica(expert=e, rank=a, start=0, count=n, slot=len(on_rank[a])))
+        on_rank[a].append(len(out) - 1)
+
+    relayed = dropped = 0
+    for m in walk:
+        f, q, x = m.expert, m.rank, m.count
+        if can_place(f, q):                                       # 1
+            place(f, q, x)
+            continue
+        done = False
+        for i in list(on_rank[q]):                                # 2
+            e = out[i].expert
+            if keep[e] >= x and can_place(f, home(e)):
+                out[i].count += x
+                keep[e] -= x
+                place(f, home(e), x)
+                done = True
+                break
+        if not done:
+            for i in list(on_rank[q]):                            # 3
+                e, c = out[i].expert, out[i].count
+                if keep[f] >= c and can_place(e, home(f)):
+                    out[i].expert = f
+                    out[i].count = c + x
+                    keep[f] -= c
+                    place(e, home(f), c)
+                    done = True
+                    break
+        if done:
+            relayed += 1
+        else:                                                     # 4
+            out.append(Replica(expert=f, rank=q, start=0, count=x, slot=-1))
+            dropped += 1
+
+    # gather each expert's entries, then tile its copies: home first, entries in order
+    first = {}
+    for i, r in enumerate(out):
+        first.setdefault(r.expert, i)
+    order = sorted(range(len(out)), key=lambda i: (first[out[i].expert], i))
+    grouped = [out[i] for i in order]
+    pos = {}
+    for r in grouped:
+        r.start = int(keep[r.expert]) + pos.get(r.expert, 0)
+        pos[r.expert] = pos.get(r.expert, 0) + r.count
+    return grouped, keep, relayed, dropped
 
 
 # --------------------------------------------------------------------------------------------

@@ -33,7 +33,7 @@ def _check_case(g, idx, B, case):
     got = [dict(expert=m.expert, rank=m.rank, start=m.start, count=m.count, slot=m.slot)
            for m in pl.replicas]
     assert got == case["replicas"]
-    for k in ("n_donors", "n_receivers", "n_pieces", "max_needed"):
+    for k in ("n_donors", "n_receivers", "n_pieces", "max_needed", "n_relayed"):
         if k in case:
             assert getattr(pl, k) == case[k], k
     if "counts" in case:
