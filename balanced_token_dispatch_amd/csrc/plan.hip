@@ -15,7 +15,10 @@
 //   k_plan_solve   one 1024-thread workgroup: loads, donor/receiver order,
 //                  pieces, the piece/receiver walk and slots, all as
 //                  counting ranks and block scans in LDS (no serial loop
-//                  over ranks or experts).
+//                  over ranks or experts).  Only when some receiver would
+//                  need more than B slots, one thread then re-places the
+//                  walk's replicas with the relay fallback (relay_pass) and
+//                  the block regroups the list by expert.
 #include "common.hpp"
 
 namespace moe {
@@ -92,6 +95,94 @@ __device__ int block_scan_excl(int v, int *tmp /* >= 17 ints */, int *total) {
   return base + x - v;
 }
 
+// Relay fallback state, all in LDS: the replica list (edited in place: the
+// pass writes entry w while reading walk entry m >= w, each walk entry giving
+// at most one new entry), copies kept home, and per rank its slot count and
+// its replicas as a chain in slot order.
+struct RelayState {
+  int *rexp, *rrank, *rcount, *rslot;
+  int *keep, *hosted, *chain_first, *chain_last, *chain_next;
+  int E_loc, B;
+  int w;
+
+  __device__ int entry_of(int a, int e) const {
+    for (int i = chain_first[a]; i >= 0; i = chain_next[i])
+      if (rexp[i] == e) return i;
+    return -1;
+  }
+  __device__ bool can_place(int e, int a) const {
+    return a == e / E_loc || entry_of(a, e) >= 0 || hosted[a] < B;
+  }
+  __device__ void append(int e, int a, int n, int slot) {
+    rexp[w] = e;
+    rrank[w] = a;
+    rcount[w] = n;
+    rslot[w] = slot;
+    if (slot >= 0) {
+      chain_next[w] = -1;
+      if (chain_last[a] >= 0) chain_next[chain_last[a]] = w; else chain_first[a] = w;
+      chain_last[a] = w;
+      ++hosted[a];
+    }
+    ++w;
+  }
+  // n copies of e onto rank a: home, an existing replica, or a new slot
+  __device__ void place(int e, int a, int n) {
+    if (a == e / E_loc) {
+      keep[e] += n;
+      return;
+    }
+    const int i = entry_of(a, e);
+    if (i >= 0) rcount[i] += n; else append(e, a, n, hosted[a]);
+  }
+};
+
+// One thread.  For each walk replica (f, q, x) in emission order: place it on
+// q; else relay through one of q's replicas (e, c) in slot order (q takes x
+// more copies of e from keep_e, e's home takes the x copies of f); else
+// switch one of them (it becomes f with c + x copies, c taken from keep_f,
+// and f's home takes the c copies of e); else drop it.  Returns the number
+// of relayed or switched replicas; *dropped counts the dropped ones.
+__device__ int relay_pass(RelayState &st, int nWalk, int *dropped) {
+  int relayed = 0, nd = 0;
+  st.w = 0;
+  for (int m = 0; m < nWalk; ++m) {
+    const int f = st.rexp[m], q = st.rrank[m], x = st.rcount[m];
+    if (st.can_place(f, q)) {
+      st.place(f, q, x);
+      continue;
+    }
+    bool done = false;
+    for (int i = st.chain_first[q]; i >= 0 && !done; i = st.chain_next[i]) {
+      const int e = st.rexp[i], A = e / st.E_loc;
+      if (st.keep[e] >= x && st.can_place(f, A)) {
+        st.rcount[i] += x;
+        st.keep[e] -= x;
+        st.place(f, A, x);
+        done = true;
+      }
+    }
+    for (int i = st.chain_first[q]; i >= 0 && !done; i = st.chain_next[i]) {
+      const int e = st.rexp[i], c = st.rcount[i], F = f / st.E_loc;
+      if (st.keep[f] >= c && st.can_place(e, F)) {
+        st.rexp[i] = f;
+        st.rcount[i] = c + x;
+        st.keep[f] -= c;
+        st.place(e, F, c);
+        done = true;
+      }
+    }
+    if (done) {
+      ++relayed;
+    } else {
+      st.append(f, q, x, -1);
+      ++nd;
+    }
+  }
+  *dropped = nd;
+  return relayed;
+}
+
 __global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__restrict__ counts,
                                                               const int32_t *__restrict__ bad,
                                                               int32_t *__restrict__ plan,
@@ -108,8 +199,11 @@ __global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__r
   __shared__ int sRecvFirst[kMaxR], sRecvN[kMaxR];
   // replica list
   __shared__ int sRexp[kMaxL], sRrank[kMaxL], sRstart[kMaxL], sRcount[kMaxL], sRslot[kMaxL];
+  // relay fallback: per-rank slot chains, and the regrouped list
+  __shared__ int sHosted[kMaxR], sChainFirst[kMaxR], sChainLast[kMaxR], sChainNext[kMaxL];
+  __shared__ int tExp[kMaxL], tRank[kMaxL], tCount[kMaxL], tSlot[kMaxL];
   __shared__ int sTmp[32];
-  __shared__ int sNDonor, sNRecv, sMaxNeeded, sOverflow, sBad;
+  __shared__ int sNDonor, sNRecv, sMaxNeeded, sOverflow, sBad, sNOut, sRelayed, sDropped;
 
   const int tid = threadIdx.x, nt = blockDim.x;
   const int E_loc = E / R;
@@ -122,6 +216,8 @@ __global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__r
     sMaxNeeded = 0;
     sOverflow = 0;
     sBad = 0;
+    sRelayed = 0;
+    sDropped = 0;
   }
   __syncthreads();
   // T_e and the bad-id flag
@@ -137,6 +233,9 @@ __global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__r
     sNP[p] = 0;
     sRecvFirst[p] = -1;
     sRecvN[p] = 0;
+    sHosted[p] = 0;
+    sChainFirst[p] = -1;
+    sChainLast[p] = -1;
   }
   __syncthreads();
   // home loads and excess
@@ -297,16 +396,74 @@ __global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__r
     }
   }
   __syncthreads();
+  int nOut = nRep;
+  if (sOverflow) {  // uniform: the walk does not fit in B slots somewhere
+    if (tid == 0) {
+      RelayState st{sRexp, sRrank, sRcount, sRslot, sKeep, sHosted, sChainFirst, sChainLast,
+                    sChainNext, E_loc, B, 0};
+      int nd = 0;
+      sRelayed = relay_pass(st, nRep, &nd);
+      sDropped = nd;
+      sNOut = st.w;
+    }
+    // sSrank (per expert) is free now: first list index of each expert
+    for (int e = tid; e < E; e += nt) {
+      sSrank[e] = 0x7fffffff;
+      sRepFirst[e] = 0;
+      sRepN[e] = 0;
+    }
+    __syncthreads();
+    nOut = sNOut;
+    for (int m = tid; m < nOut; m += nt) atomicMin(&sSrank[sRexp[m]], m);
+    __syncthreads();
+    // gather each expert's entries: experts by first entry, entries in pass order
+    for (int m = tid; m < nOut; m += nt) {
+      const int e = sRexp[m], fi = sSrank[e];
+      int pos = 0;
+      for (int k = 0; k < nOut; ++k) {
+        const int ek = sRexp[k];
+        pos += (sSrank[ek] < fi) || (ek == e && k < m);
+      }
+      tExp[pos] = e;
+      tRank[pos] = sRrank[m];
+      tCount[pos] = sRcount[m];
+      tSlot[pos] = sRslot[m];
+    }
+    __syncthreads();
+    for (int m = tid; m < nOut; m += nt) {
+      sRexp[m] = tExp[m];
+      sRrank[m] = tRank[m];
+      sRcount[m] = tCount[m];
+      sRslot[m] = tSlot[m];
+    }
+    __syncthreads();
+    // tile each expert's copies: home first, then its entries in order
+    for (int m = tid; m < nOut; m += nt) {
+      const int e = sRexp[m];
+      int st = sKeep[e], k = m - 1;
+      for (; k >= 0 && sRexp[k] == e; --k) st += sRcount[k];
+      sRstart[m] = st;
+      if (k == m - 1) {
+        int n = 1;
+        while (m + n < nOut && sRexp[m + n] == e) ++n;
+        sRepFirst[e] = m;
+        sRepN[e] = n;
+      }
+    }
+  } else {
+    for (int q = tid; q < R; q += nt) sHosted[q] = sRecvN[q];
+  }
+  __syncthreads();
   // write the blob, each word exactly once
-  const int status = (sBad ? MOE_DEV_BAD_EXPERT_ID : 0) | (sOverflow ? MOE_DEV_SLOT_OVERFLOW : 0);
+  const int status = (sBad ? MOE_DEV_BAD_EXPERT_ID : 0) | (sDropped ? MOE_DEV_SLOT_OVERFLOW : 0);
   if (tid == 0) {
     plan[0] = status;
-    plan[1] = nRep;
+    plan[1] = nOut;
     plan[2] = sMaxNeeded;
     plan[3] = nDonor;
     plan[4] = nRecv;
     plan[5] = nPieces;
-    plan[6] = 0;
+    plan[6] = sRelayed;
     plan[7] = 0;
     if (dev_status) *dev_status = (uint32_t)status;
   }
@@ -317,20 +474,28 @@ __global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__r
     plan[L.off_rep_n + e] = sRepN[e];
   }
   for (int m = tid; m < E + R; m += nt) {
-    const bool used = m < nRep;
+    const bool used = m < nOut;
     plan[L.off_rexp + m] = used ? sRexp[m] : -1;
     plan[L.off_rrank + m] = used ? sRrank[m] : -1;
     plan[L.off_rslot + m] = used ? sRslot[m] : -1;
     plan[L.off_rstart + m] = used ? sRstart[m] : 0;
     plan[L.off_rcount + m] = used ? sRcount[m] : 0;
   }
+  // slot tables: slots 0..hosted-1 of a rank are written by their entries,
+  // the rest are empty
+  for (int m = tid; m < nOut; m += nt) {
+    const int j = sRslot[m];
+    if (j < 0) continue;
+    const int w = sRrank[m] * B + j;
+    plan[L.off_sexp + w] = sRexp[m];
+    plan[L.off_sstart + w] = sRstart[m];
+    plan[L.off_scount + w] = sRcount[m];
+  }
   for (int w = tid; w < R * B; w += nt) {
-    const int q = w / B, j = w % B;
-    const int f = sRecvFirst[q];
-    const bool used = f >= 0 && j < min(sRecvN[q], B);
-    plan[L.off_sexp + w] = used ? sRexp[f + j] : -1;
-    plan[L.off_sstart + w] = used ? sRstart[f + j] : 0;
-    plan[L.off_scount + w] = used ? sRcount[f + j] : 0;
+    if (w % B < sHosted[w / B]) continue;
+    plan[L.off_sexp + w] = -1;
+    plan[L.off_sstart + w] = 0;
+    plan[L.off_scount + w] = 0;
   }
 }
 

@@ -91,20 +91,31 @@ const char *moe_status_string(moe_status_t s);
  * experts taken by (T_e desc, e asc) until the excess is gone; the pieces
  * are dealt out, in order, to receivers (d_r < 0) ordered by (-d_r desc,
  * r asc), each replica carrying min(piece left, deficit left) copies; a
- * receiver's replicas take slots 0, 1, ... in order, those beyond B-1 are
- * dropped with MOE_DEV_SLOT_OVERFLOW.  Afterwards every rank processes
- * exactly S*K copies (absent overflow and bad ids).
+ * receiver's replicas take slots 0, 1, ... in order.  When some receiver
+ * would need more than B slots, a relay fallback re-places the walk's
+ * replicas in order: a full receiver instead takes more copies of an expert
+ * it already hosts while that expert's home (a donor) takes the piece, or one
+ * of its replicas switches to the new expert while the new expert's home
+ * takes the switched-out copies (first fit over the receiver's slots; a
+ * "place" goes to the home's keep, an existing replica, or a free slot).
+ * A replica neither can place is dropped with MOE_DEV_SLOT_OVERFLOW.  The
+ * list is then gathered by expert (experts by first entry, entries in pass
+ * order) and each expert's copies are tiled home first, then its entries.
+ * Plans the walk fits are the walk's.  Afterwards every rank processes
+ * exactly S*K copies (absent overflow and bad ids).  The fallback is one
+ * thread's loop (fast when few replicas need it; it runs only on overflow).
  *
  *   topk_idx   [R*S*K] int32, router top-K expert ids of every rank.
  *   counts     [R*E] int32 out, C[p][e] (ids outside [0,E) not counted).
  *   plan       [moe_plan_words(dims)] int32 out:
- *                [0] status bits  [1] replicas emitted  [2] most replicas
- *                asked of one rank  [3] donors  [4] receivers  [5] pieces
- *                [6..7] 0
+ *                [0] status bits  [1] replicas in the list  [2] most
+ *                replicas the walk asked of one rank  [3] donors
+ *                [4] receivers  [5] pieces  [6] replicas relayed or
+ *                switched by the fallback  [7] 0
  *                T[E]  keep[E] (copies of e staying home)
  *                rep_first[E] rep_n[E] (e's replicas in the list; 0,0 if none)
  *                replica list, E+R entries each of expert[] rank[] slot[]
- *                  start[] count[] in emission order; the replica takes the
+ *                  start[] count[], an expert's entries together; the replica takes the
  *                  copies of its expert at positions [start, start+count) of
  *                  that expert's copy-id order; unused entries -1,-1,-1,0,0;
  *                  slot -1 = dropped

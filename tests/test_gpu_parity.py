@@ -89,6 +89,51 @@ def test_plan_layout_random(case):
         check_plan_layout(gp, idx, r, pl)
 
 
+RELAY_CASES = [
+    # R, S, K, E, B, skew: routings whose walk needs more than B slots on some rank
+    (4, 64, 2, 8, 1, 0.3),           # one relay
+    (8, 200, 2, 16, 1, 0.3),
+    (8, 50, 1, 8, 1, 0.5),
+    (16, 100, 4, 32, 1, 0.2),        # relays, and some replicas still dropped
+    (32, 256, 8, 256, 1, 0.1),       # the same at 32 ranks
+    (64, 64, 4, 128, 1, 0.1),        # 13 relays over 64 ranks
+]
+
+
+@pytest.mark.parametrize("case", RELAY_CASES)
+def test_plan_layout_relay(case):
+    """The relay fallback (walk replicas re-placed through donors) matches the oracle bit for
+    bit: plan blob, cu_seqlens, dest_pos and src_flat."""
+    R, S, K, E, B, skew = case
+    rng = np.random.default_rng(R * 1000 + S)
+    with np.errstate(divide="ignore"):
+        idx = _random_routing(rng, R, S, K, E, skew)
+    pl = oracle.plan(idx, E, B)
+    assert pl.max_needed > B and pl.n_relayed > 0
+    gp = GpuPlan(R, S, K, E, B)
+    for r in sorted({0, 1, R // 2, R - 1}):
+        log(f"relay plan case={case} rank={r} status={pl.status} relayed={pl.n_relayed}")
+        gp.run(_dev(idx), r)
+        check_plan_layout(gp, idx, r, pl)
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_plan_layout_relay_chain(B):
+    """Five donors with excess 1 and one receiver with deficit 5: chains of relays (B=2) and
+    of switches (B=1) re-place every piece; all ranks checked."""
+    R, K, S, E = 6, 1, 5, 6
+    flat = []
+    for r in range(1, R):
+        flat += [r] * (S + 1)
+    idx = np.array(flat, np.int32).reshape(R, S, K)
+    pl = oracle.plan(idx, E, B)
+    assert pl.status == 0 and pl.n_relayed > 0
+    gp = GpuPlan(R, S, K, E, B)
+    for r in range(R):
+        gp.run(_dev(idx), r)
+        check_plan_layout(gp, idx, r, pl)
+
+
 def test_plan_layout_bad_ids():
     rng = np.random.default_rng(11)
     R, S, K, E, B = 4, 700, 3, 16, 3
