@@ -7,19 +7,20 @@
 // (experts are addressed by row index, so the tensor must be contiguous).
 //
 // bf16 path (MFMA, gfx950):
-//   * persistent grid of one 512-thread workgroup per CU; every workgroup
-//     rebuilds the tile table from cu_seqlens in LDS (no host sync, the
-//     grid is sized from the machine, not from the routing);
-//   * 256x256 output tile, K step 32, 8 waves in 2x4, each wave 128x64 as
-//     4x2 v_mfma_f32_32x32x16_bf16 blocks (fp32 accumulators);
+//   * persistent grid of one workgroup per CU; every workgroup rebuilds the
+//     tile table from cu_seqlens in LDS (no host sync, the grid is sized from
+//     the machine, not from the routing);
+//   * 256x256 output tile, K step 32, v_mfma_f32_32x32x16_bf16 blocks with
+//     fp32 accumulators; FWD and DGRAD run 4 waves (one per SIMD) of 128x128,
+//     WGRAD and the gated FWD 8 waves of 128x64;
 //   * operands go global -> LDS with direct-to-LDS buffer loads (no register
 //     staging) into a 4-stage ring, XOR-swizzled by 16-byte chunks so the
 //     fragment reads are conflict-free; an operand whose contraction index is
 //     contiguous is read with ds_read_b128, one whose contraction index is
 //     strided (the weight in FWD, both operands in WGRAD) with the
 //     transposing ds_read_b64_tr_b16;
-//   * ping-pong K loop: the two waves sharing a SIMD alternate between an
-//     MFMA half step and a memory half step (see tile_mma);
+//   * interleaved K loop: each wave issues one fragment read or load behind
+//     each MFMA (see tile_mma);
 //   * the MFMA is issued as (column-side x row-side) so each lane ends with
 //     4 consecutive output columns: 8-byte bf16 / 16-byte fp32 stores;
 //   * blockIdx is remapped so the 32 workgroups of one XCD work on
@@ -34,14 +35,23 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int BM = 256, BN = 256, BK = 32;
-// 8 waves (two per SIMD, so one wave's MFMAs overlap the other's waits), laid out 2 x 4 over
-// the 256x256 tile: each wave owns 128 x 64 = 4 x 2 blocks of 32x32.
-constexpr int kWavesM = 2, kWavesN = 4, kWaves = kWavesM * kWavesN;
-constexpr int kGemmThreads = 64 * kWaves;
-constexpr int TM = BM / (32 * kWavesM), TN = BN / (32 * kWavesN);
 constexpr int kMaxG = 1088;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
+
+// Wave layouts of the 256x256 output tile (2 waves along rows, WN along columns).
+//   Waves<2>: 4 waves, one per SIMD, each 128 x 128 = 4 x 4 blocks of 32x32 (fp32
+//             accumulators in the accumulation registers); FWD and DGRAD.
+//   Waves<4>: 8 waves, two per SIMD, each 128 x 64 = 4 x 2 blocks; WGRAD and the gated FWD,
+//             whose epilogues need the registers the larger wave tile takes.
+template <int WN>
+struct Waves {
+  static constexpr int M = 2, N = WN, n = M * N, threads = 64 * n;
+  static constexpr int TM = BM / (32 * M), TN = BN / (32 * N);
+  static constexpr int blk = 16 / n;    // 1-KB blocks per wave per operand per K step
+  static constexpr int loads = 2 * blk; // direct-to-LDS loads per wave per K step
+};
+constexpr int kMaxBlk = 4;
 
 // Buffer resource over [base, base + bytes): loads past the end return zero.
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, long long bytes) {
@@ -62,8 +72,8 @@ constexpr int OP_ELEMS = 256 * BK;            // one operand of one stage
 constexpr int STAGE_ELEMS = 2 * OP_ELEMS;
 
 // Direct-to-LDS loads of one operand tile (256 rows x BK contraction per K step).  Each
-// wave instruction writes 64 lanes x 16 B = 1 KB of LDS contiguously; each wave issues two
-// per operand per K step.
+// wave instruction writes 64 lanes x 16 B = 1 KB of LDS contiguously; the 16 blocks of an
+// operand tile are shared out over the waves.
 //  contiguous source (row r, contraction c at base[r*ld + c]): LDS is [256][BK], 64 B per row;
 //    16-byte chunk k of row r sits at position k ^ ((r >> 2) & 3);
 //  strided source (row r, contraction c at base[c*ld + r]): LDS is [BK][256], 512 B per
@@ -79,11 +89,11 @@ struct DmaOp {
   const char *base;  // byte address of element (row 0, contraction 0) of the tile
   long long bytes;   // bytes readable from base
   long long step;    // bytes per K step
-  int voff[2];       // per-lane byte offset of this wave's two blocks, or kOOB
-  int kc[2];         // contraction index of each block's chunk within a K step
+  int voff[kMaxBlk]; // per-lane byte offset of this wave's blocks, or kOOB
+  int kc[kMaxBlk];   // contraction index of each block's chunk within a K step
 };
 
-template <bool CONTIG>
+template <class W, bool CONTIG>
 __device__ inline void dma_init(DmaOp &d, const uint16_t *base, long long bytes, int ld,
                                 int row_lim) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -91,8 +101,8 @@ __device__ inline void dma_init(DmaOp &d, const uint16_t *base, long long bytes,
   d.bytes = bytes;
   d.step = CONTIG ? BK * 2 : (long long)BK * ld * 2;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int blk = u * kWaves + wid;              // 1-KB block of the 16-KB tile
+  for (int u = 0; u < W::blk; ++u) {
+    const int blk = u * W::n + wid;                // 1-KB block of the 16-KB tile
     const int o = blk * 1024 + lane * 16;          // this lane's LDS byte offset
     if (CONTIG) {
       const int r = o >> 6, p = (o >> 4) & 3;
@@ -108,34 +118,35 @@ __device__ inline void dma_init(DmaOp &d, const uint16_t *base, long long bytes,
   }
 }
 
-// Issue this wave's two loads of K step kt into the operand's LDS region at byte address
-// `lds_op` (+ this wave's block offset `wave_off`).
-template <bool CONTIG, bool RAGGED>
-__device__ inline void dma_issue(const DmaOp &d, uint32_t lds_op, uint32_t wave_off, int kt,
-                                 int nk, int c_lim) {
+// Buffer resource of K step kt of an operand (a zero-byte resource past the last step).
+__device__ inline __amdgpu_buffer_rsrc_t dma_rsrc(const DmaOp &d, int kt, int nk) {
   const long long c0b = (long long)kt * d.step;
   const long long rem = d.bytes - c0b;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(d.base + c0b, (kt < nk && rem > 0) ? rem : 0);
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    int off = d.voff[u];
-    if (CONTIG && RAGGED) off = kt * BK + d.kc[u] < c_lim ? off : kOOB;
-    // buffer_load_dwordx4 ... lds: 16 bytes per lane straight into LDS at M0 + 16 * lane.
-    // Written as asm so the compiler does not track it: its alias analysis cannot tell the
-    // ping-pong groups' stages apart and would drain every load at each barrier.  The load
-    // has no register result (nothing in flight can overwrite a VGPR); the "memory"
-    // clobber keeps LDS accesses on their side of it; completion is ordered only by the
-    // explicit vmcnt waits and barriers of the K loop.
-    // M0 is set by the compiler from the "{m0}" operand; the asm starts with one wait
-    // state, because on this architecture family an LDS-DMA load must not read M0 in the
-    // cycle after a scalar write to it (the compiler pads its own LDS-DMA loads the same way).
-    const uint32_t m0 = lds_op + wave_off + u * kWaves * 1024;
-    asm volatile(
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off),
-        "s"(rs), "{m0}"(m0)
-        : "memory");
-  }
+  return make_rsrc(d.base + c0b, (kt < nk && rem > 0) ? rem : 0);
+}
+
+// This wave's load u of K step kt into the operand's LDS region at byte address `lds_op`
+// (+ this wave's block offset `wave_off`).
+template <class W, bool CONTIG, bool RAGGED>
+__device__ inline void dma_one(const DmaOp &d, __amdgpu_buffer_rsrc_t rs, uint32_t lds_op,
+                               uint32_t wave_off, int kt, int c_lim, int u) {
+  int off = d.voff[u];
+  if (CONTIG && RAGGED) off = kt * BK + d.kc[u] < c_lim ? off : kOOB;
+  // buffer_load_dwordx4 ... lds: 16 bytes per lane straight into LDS at M0 + 16 * lane.
+  // Written as asm so the compiler does not track it: its alias analysis cannot tell the
+  // ring's stages apart and would drain every load at each barrier.  The load has no
+  // register result (nothing in flight can overwrite a VGPR); the "memory" clobber keeps
+  // LDS accesses on their side of it; completion is ordered only by the explicit vmcnt
+  // waits and barriers of the K loop.  M0 is set by the compiler from the "{m0}" operand;
+  // the asm starts with one wait state, because on this architecture family an LDS-DMA
+  // load must not read M0 in the cycle after a scalar write to it (the compiler pads its
+  // own LDS-DMA loads the same way).
+  const uint32_t m0 = lds_op + wave_off + u * W::n * 1024;
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off),
+      "s"(rs), "{m0}"(m0)
+      : "memory");
 }
 
 // MFMA operand t of lane `lane` (rows wbase + 32t .. +31 for a contiguous operand) at
@@ -165,8 +176,6 @@ __device__ inline bf16x8 read_operand(const uint16_t *src, int wbase, int t, int
   }
 }
 
-constexpr int kLoadsPerStep = 2 * (16 / kWaves);  // direct-to-LDS loads per thread per K step
-
 template <int N>
 __device__ inline void waitcnt_vm() {
   // s_waitcnt vmcnt(N), expcnt and lgkmcnt at their maximum (no wait on them);
@@ -175,25 +184,20 @@ __device__ inline void waitcnt_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// One contraction sub-step (16) of this wave's MFMA operands.
+template <class W>
 struct Frags {
-  bf16x8 a[TM], b[TN];
+  bf16x8 a[W::TM], b[W::TN];
 };
 
-template <bool A_CONTIG, bool B_CONTIG>
-__device__ inline void read_frags(Frags &f, const uint16_t *stage, int wi, int wj, int lane,
+template <class W, bool A_CONTIG, bool B_CONTIG>
+__device__ inline void read_frags(Frags<W> &f, const uint16_t *stage, int wi, int wj, int lane,
                                   int ks) {
 #pragma unroll
-  for (int t = 0; t < TM; ++t) f.a[t] = read_operand<A_CONTIG>(stage, wi, t, lane, ks);
+  for (int t = 0; t < W::TM; ++t) f.a[t] = read_operand<A_CONTIG>(stage, wi, t, lane, ks);
 #pragma unroll
-  for (int t = 0; t < TN; ++t) f.b[t] = read_operand<B_CONTIG>(stage + OP_ELEMS, wj, t, lane, ks);
-}
-
-__device__ inline void mma16(f32x16 (&acc)[TM][TN], const Frags &f) {
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tm][tn], 0, 0, 0);
+  for (int t = 0; t < W::TN; ++t)
+    f.b[t] = read_operand<B_CONTIG>(stage + OP_ELEMS, wj, t, lane, ks);
 }
 
 struct TileArgs {
@@ -203,85 +207,96 @@ struct TileArgs {
 };
 
 // This wave's loads of K step kt (both operands) into LDS stage `stage`.
-template <bool A_CONTIG, bool B_CONTIG, bool RAGGED>
+template <class W, bool A_CONTIG, bool B_CONTIG, bool RAGGED>
 __device__ inline void dma_step(const uint16_t *lds, int stage, const TileArgs &ta, int kt) {
   const uint32_t st = (uint32_t)(uintptr_t)(lds_vptr)(lds + stage * STAGE_ELEMS);
-  dma_issue<A_CONTIG, RAGGED>(ta.a, st, ta.wave_off, kt, ta.nk, ta.c_len);
-  dma_issue<B_CONTIG, RAGGED>(ta.b, st + OP_ELEMS * 2, ta.wave_off, kt, ta.nk, ta.c_len);
+  const __amdgpu_buffer_rsrc_t ra = dma_rsrc(ta.a, kt, ta.nk);
+  const __amdgpu_buffer_rsrc_t rb = dma_rsrc(ta.b, kt, ta.nk);
+#pragma unroll
+  for (int u = 0; u < W::blk; ++u)
+    dma_one<W, A_CONTIG, RAGGED>(ta.a, ra, st, ta.wave_off, kt, ta.c_len, u);
+#pragma unroll
+  for (int u = 0; u < W::blk; ++u)
+    dma_one<W, B_CONTIG, RAGGED>(ta.b, rb, st + OP_ELEMS * 2, ta.wave_off, kt, ta.c_len, u);
 }
 
 // One 256x256 output tile: out_tile[i][j] = sum_c Aop(i, c) * Bop(j, c), BK = 32 per K
 // step, K step k in LDS stage k % 4.
 //
-// Ping-pong schedule.  Waves w and w+4 share a SIMD; waves 0-3 form group X, waves 4-7
-// group Y.  The loop runs in half steps separated by barriers, and in each half step one
-// group issues the 16 MFMAs of a K step while the other reads its fragments of a K step
-// from LDS and issues its share of the direct-to-LDS loads.  A wave issues in order, so
-// a load stalled on a full address queue only delays the memory-phase wave, never the
-// MFMAs of the SIMD's other wave.  Numbering half steps h = 0, 1, ...:
-//   X reads step k at h = 2k and runs its MFMAs at h = 2k+1;
-//   Y reads step k at h = 2k+1 and runs its MFMAs at h = 2k+2;
-//   each memory phase of either group issues its loads for step k+3 into stage
-//   (k+3) % 4, whose previous occupant, step k-1, was last read at h = 2k-1, and then
-//   waits until at most two steps of its own loads are in flight, so step k+1 has landed
-//   before the barrier that precedes its first read.
-// The prologue issues steps 0-2 and waits for steps 0 and 1.  Loads of steps past the
-// last have every offset out of range and write zeros into stages no later read uses.
-template <bool A_CONTIG, bool B_CONTIG, bool RAGGED>
-__device__ __attribute__((always_inline)) inline void mem_phase(const uint16_t *lds,
-                                                                const TileArgs &ta, int k_read,
-                                                                int k_dma, Frags (&f)[2], int wi,
-                                                                int wj, int lane) {
-  const uint16_t *src = lds + (k_read & 3) * STAGE_ELEMS;
-  read_frags<A_CONTIG, B_CONTIG>(f[0], src, wi, wj, lane, 0);
-  read_frags<A_CONTIG, B_CONTIG>(f[1], src, wi, wj, lane, 1);
-  dma_step<A_CONTIG, B_CONTIG, RAGGED>(lds, k_dma & 3, ta, k_dma);
-}
-
-template <bool A_CONTIG, bool B_CONTIG, bool RAGGED>
-__device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta, f32x16 (&acc)[TM][TN]) {
+// A K step is two half steps, one per contraction sub-step of 16, each of TM*TN MFMAs;
+// behind each MFMA the wave issues at most one memory operation for later, so the matrix
+// unit is fed while reads and loads are in flight:
+//   half A of step k: MFMAs on sub-step 0 (registers F0); reads sub-step 1 of step k into
+//                     F1; issues its loads of the row-side operand of step k+3 into stage
+//                     (k+3) % 4;
+//   wait until at most the loads of step k+2 and the row-side loads of step k+3 are in
+//   flight (so step k+1 has landed), barrier;
+//   half B of step k: MFMAs on sub-step 1 (F1); reads sub-step 0 of step k+1 into F0;
+//                     issues its loads of the column-side operand of step k+3.
+// Stage (k+3) % 4 last held step k-1, whose reads every wave finished before the barrier in
+// the middle of step k-1 (the barrier waits for this wave's LDS reads), and the barrier in
+// the middle of step k follows every wave's wait for step k+1, which half B then reads.
+// The prologue issues steps 0-2 and waits for step 0.  Loads of steps past the last have
+// every offset out of range and write zeros into stages no later read uses.
+template <class W, bool A_CONTIG, bool B_CONTIG, bool RAGGED>
+__device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta,
+                                f32x16 (&acc)[W::TM][W::TN]) {
+  constexpr int TM = W::TM, TN = W::TN, NB = W::blk;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wi = (wid / kWavesN) * (32 * TM), wj = (wid % kWavesN) * (32 * TN);
+  const int wi = (wid / W::N) * (32 * TM), wj = (wid % W::N) * (32 * TN);
   const int nk = ta.nk;
-  // (wid is wave-uniform; reading it through readfirstlane makes the compiler restructure
-  // the loop and spill, so the branch below is left to the divergent-branch lowering,
-  // whose skip-if-no-lane-active jumps make it uniform at run time.)
-  const bool X = wid < kWaves / 2;
-
 #pragma unroll
   for (int a = 0; a < TM; ++a)
 #pragma unroll
     for (int b = 0; b < TN; ++b) acc[a][b] = (f32x16){};
 
-  Frags f[2];
+  Frags<W> F0, F1;
 #pragma unroll
-  for (int kt = 0; kt < 3; ++kt) dma_step<A_CONTIG, B_CONTIG, RAGGED>(lds, kt, ta, kt);
-  waitcnt_vm<kLoadsPerStep>();
+  for (int kt = 0; kt < 3; ++kt) dma_step<W, A_CONTIG, B_CONTIG, RAGGED>(lds, kt, ta, kt);
+  waitcnt_vm<2 * W::loads>();
   __syncthreads();
-  if (X) {  // h = 0
-    mem_phase<A_CONTIG, B_CONTIG, RAGGED>(lds, ta, 0, 3, f, wi, wj, lane);
-    waitcnt_vm<2 * kLoadsPerStep>();
-  }
-  __syncthreads();
+  read_frags<W, A_CONTIG, B_CONTIG>(F0, lds, wi, wj, lane, 0);
   for (int k = 0; k < nk; ++k) {
-    if (X) {
+    const uint16_t *cur = lds + (k & 3) * STAGE_ELEMS;
+    const uint16_t *nxt = lds + ((k + 1) & 3) * STAGE_ELEMS;
+    const uint32_t st = (uint32_t)(uintptr_t)(lds_vptr)(lds + ((k + 3) & 3) * STAGE_ELEMS);
+    __amdgpu_buffer_rsrc_t ra, rb;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TM * TN; ++i) {  // half A
+      const int tm = i / TN, tn = i % TN;
+      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F0.b[tn], F0.a[tm], acc[tm][tn], 0,
+                                                            0, 0);
+      if (i < TM)
+        F1.a[i] = read_operand<A_CONTIG>(cur, wi, i, lane, 1);
+      else if (i < TM + TN)
+        F1.b[i - TM] = read_operand<B_CONTIG>(cur + OP_ELEMS, wj, i - TM, lane, 1);
+      if (i == 1) ra = dma_rsrc(ta.a, k + 3, nk);
+      if (i == 2) rb = dma_rsrc(ta.b, k + 3, nk);
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (i == (u + 1) * TM * TN / (NB + 1))
+          dma_one<W, A_CONTIG, RAGGED>(ta.a, ra, st, ta.wave_off, k + 3, ta.c_len, u);
       __builtin_amdgcn_sched_barrier(0);
-      mma16(acc, f[0]);  // h = 2k+1
-      mma16(acc, f[1]);
+    }
+    waitcnt_vm<W::loads + NB>();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TM * TN; ++i) {  // half B
+      const int tm = i / TN, tn = i % TN;
+      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F1.b[tn], F1.a[tm], acc[tm][tn], 0,
+                                                            0, 0);
+      if (i < TM)
+        F0.a[i] = read_operand<A_CONTIG>(nxt, wi, i, lane, 0);
+      else if (i < TM + TN)
+        F0.b[i - TM] = read_operand<B_CONTIG>(nxt + OP_ELEMS, wj, i - TM, lane, 0);
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (i == (u + 1) * TM * TN / (NB + 1))
+          dma_one<W, B_CONTIG, RAGGED>(ta.b, rb, st + OP_ELEMS * 2, ta.wave_off, k + 3,
+                                       ta.c_len, u);
       __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      mem_phase<A_CONTIG, B_CONTIG, RAGGED>(lds, ta, k + 1, k + 4, f, wi, wj, lane);  // h = 2k+2
-      waitcnt_vm<2 * kLoadsPerStep>();
-      __syncthreads();
-    } else {
-      mem_phase<A_CONTIG, B_CONTIG, RAGGED>(lds, ta, k, k + 3, f, wi, wj, lane);  // h = 2k+1
-      waitcnt_vm<2 * kLoadsPerStep>();
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      mma16(acc, f[0]);  // h = 2k+2
-      mma16(acc, f[1]);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
     }
   }
   waitcnt_vm<0>();  // the trailing out-of-range loads land before the stages are reused
@@ -306,15 +321,16 @@ __device__ inline int logical_block() {
 }
 
 // Segment table: sCu[rho] (clamped to [0, M_total]) and sStart[rho] = first row tile of rho.
+template <class W>
 __device__ inline int build_tiles(const int32_t *cu, int G, int M_total, int *sCu, int *sStart,
                                   bool wgrad) {
-  __shared__ int tmp[kWaves];
+  __shared__ int tmp[W::n];
   __shared__ int carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  for (int i = tid; i <= G; i += kGemmThreads) sCu[i] = min(max(cu[i], 0), M_total);
+  for (int i = tid; i <= G; i += W::threads) sCu[i] = min(max(cu[i], 0), M_total);
   if (tid == 0) carry_s = 0;
   __syncthreads();
-  for (int base = 0; base < G; base += kGemmThreads) {
+  for (int base = 0; base < G; base += W::threads) {
     const int rho = base + tid;
     int v = 0;
     if (rho < G) {
@@ -331,7 +347,7 @@ __device__ inline int build_tiles(const int32_t *cu, int G, int M_total, int *sC
     __syncthreads();
     int before = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < W::n; ++w) {
       before += w < wid ? tmp[w] : 0;
       tot += tmp[w];
     }
@@ -364,13 +380,14 @@ __device__ inline int find_seg(const int *sStart, int G, int t) {
 // 512 B of one row per 32 lanes.  16-byte LDS chunks are XOR-swizzled by row so the
 // fragment writes spread over the banks and the row reads are conflict-free.  Rows >= rows
 // and columns >= cols of the tile are not written (cols is a multiple of 8).
-__device__ inline void epilogue_bf16(uint16_t *lds, const f32x16 (&acc)[TM][TN], uint16_t *o,
-                                     long long ld, int rows, int cols, int wi, int wj,
-                                     int lane, int wid) {
+template <class W>
+__device__ inline void epilogue_bf16(uint16_t *lds, const f32x16 (&acc)[W::TM][W::TN],
+                                     uint16_t *o, long long ld, int rows, int cols, int wi,
+                                     int wj, int lane, int wid) {
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
+  for (int tm = 0; tm < W::TM; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
+    for (int tn = 0; tn < W::TN; ++tn)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int i = wi + tm * 32 + (lane & 31);
@@ -382,9 +399,10 @@ __device__ inline void epilogue_bf16(uint16_t *lds, const f32x16 (&acc)[TM][TN],
         *(uint2 *)(lds + i * 256 + (c ^ (i & 31)) * 8 + (lane >> 5) * 4) = v;
       }
   __syncthreads();
+  constexpr int kRows = BM / W::n;  // rows stored by one wave, two per instruction
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {  // wave wid: rows 32 wid .. +31, two per instruction
-    const int i = wid * 32 + 2 * r + (lane >> 5);
+  for (int r = 0; r < kRows / 2; ++r) {
+    const int i = wid * kRows + 2 * r + (lane >> 5);
     const int c = lane & 31;
     const u32x4 v = *(const u32x4 *)(lds + i * 256 + (c ^ (i & 31)) * 8);
     if (i < rows && c * 8 < cols) *(u32x4 *)(o + i * ld + c * 8) = v;
@@ -401,13 +419,14 @@ constexpr int kOpSwiglu = 3;  // internal op: FWD main loop, gated epilogue
 
 __device__ inline float silu_f32(float x) { return x / (1.0f + __expf(-x)); }
 
-__device__ inline void epilogue_swiglu(uint16_t *lds, const f32x16 (&acc)[TM][TN], uint16_t *o,
-                                       long long ld, int rows, int cols, int wi, int wj,
-                                       int lane) {
+template <class W>
+__device__ inline void epilogue_swiglu(uint16_t *lds, const f32x16 (&acc)[W::TM][W::TN],
+                                       uint16_t *o, long long ld, int rows, int cols, int wi,
+                                       int wj, int lane) {
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
+  for (int tm = 0; tm < W::TM; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
+    for (int tn = 0; tn < W::TN; ++tn)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int i = wi + tm * 32 + (lane & 31);
@@ -418,9 +437,10 @@ __device__ inline void epilogue_swiglu(uint16_t *lds, const f32x16 (&acc)[TM][TN
         *(uint32_t *)(lds + i * 128 + ((jz >> 3) ^ (i & 15)) * 8 + (jz & 7)) = v;
       }
   __syncthreads();
+  constexpr int kPass = W::threads / 16;  // rows per pass, 16 chunks each
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {  // 512 threads: 32 rows x 16 chunks per pass
-    const int i = (threadIdx.x >> 4) + 32 * r;
+  for (int r = 0; r < BM / kPass; ++r) {
+    const int i = (threadIdx.x >> 4) + kPass * r;
     const int c = threadIdx.x & 15;
     const u32x4 v = *(const u32x4 *)(lds + i * 128 + (c ^ (i & 15)) * 8);
     if (i < rows && c * 8 < cols) *(u32x4 *)(o + i * ld + c * 8) = v;
@@ -428,15 +448,17 @@ __device__ inline void epilogue_swiglu(uint16_t *lds, const f32x16 (&acc)[TM][TN
   __syncthreads();
 }
 
-template <int OP, bool RAGGED>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
+template <int OP, bool RAGGED, int WN>
+__global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
     const int32_t *__restrict__ cu, void *__restrict__ out, void *__restrict__ out2, int G,
     int M_total, int Kd, int N) {
+  using W = Waves<WN>;
+  constexpr int TM = W::TM, TN = W::TN;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * STAGE_ELEMS];
   __shared__ int sCu[kMaxG + 1], sStart[kMaxG + 1];
   const bool wgrad = OP == MOE_GEMM_WGRAD;
-  const int n_rt_total = build_tiles(cu, G, M_total, sCu, sStart, wgrad);
+  const int n_rt_total = build_tiles<W>(cu, G, M_total, sCu, sStart, wgrad);
   // FWD: i = rows, j = n in [0,N), c = kd.  DGRAD: i = rows, j = kd, c = n.
   // WGRAD: i = kd, j = n, c = rows of the segment (per active segment: n_it x n_jt tiles).
   const int ncols = OP == MOE_GEMM_DGRAD ? Kd : N;
@@ -444,7 +466,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
   const int n_it = (Kd + BM - 1) / BM;
   const long long total = wgrad ? (long long)n_rt_total * n_it * n_ct : (long long)n_rt_total * n_ct;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wi = (wid / kWavesN) * (32 * TM), wj = (wid % kWavesN) * (32 * TN);
+  const int wi = (wid / W::N) * (32 * TM), wj = (wid % W::N) * (32 * TN);
   const uint32_t wave_off = __builtin_amdgcn_readfirstlane(wid) * 1024;
 
   for (long long t = logical_block(); t < total; t += gridDim.x) {
@@ -460,29 +482,29 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
       TileArgs ta;
       ta.wave_off = wave_off;
       if (OP == MOE_GEMM_FWD || OP == kOpSwiglu) {
-        dma_init<true>(ta.a, a + (size_t)m0 * Kd, (long long)rows * Kd * 2, Kd, rows);
-        dma_init<false>(ta.b, w + j0, ((long long)Kd * N - j0) * 2, N, N - j0);
+        dma_init<W, true>(ta.a, a + (size_t)m0 * Kd, (long long)rows * Kd * 2, Kd, rows);
+        dma_init<W, false>(ta.b, w + j0, ((long long)Kd * N - j0) * 2, N, N - j0);
         ta.c_len = Kd;
       } else {
-        dma_init<true>(ta.a, a + (size_t)m0 * N, (long long)rows * N * 2, N, rows);
-        dma_init<true>(ta.b, w + (size_t)j0 * N, (long long)(Kd - j0) * N * 2, N, Kd - j0);
+        dma_init<W, true>(ta.a, a + (size_t)m0 * N, (long long)rows * N * 2, N, rows);
+        dma_init<W, true>(ta.b, w + (size_t)j0 * N, (long long)(Kd - j0) * N * 2, N, Kd - j0);
         ta.c_len = N;
       }
       ta.nk = (ta.c_len + BK - 1) / BK;
       if (OP == MOE_GEMM_FWD || OP == kOpSwiglu)
-        tile_mma<true, false, RAGGED>(lds, ta, acc);
+        tile_mma<W, true, false, RAGGED>(lds, ta, acc);
       else
-        tile_mma<true, true, RAGGED>(lds, ta, acc);
+        tile_mma<W, true, true, RAGGED>(lds, ta, acc);
       if (OP == kOpSwiglu) {
         // out = z [M, N/2], out2 = pre-activation h [M, N] (optional)
         if (out2)
-          epilogue_bf16(lds, acc, (uint16_t *)out2 + (size_t)m0 * N + j0, N, rows, N - j0, wi,
-                        wj, lane, wid);
-        epilogue_swiglu(lds, acc, (uint16_t *)out + (size_t)m0 * (N / 2) + j0 / 2, N / 2, rows,
-                        (N - j0) / 2, wi, wj, lane);
+          epilogue_bf16<W>(lds, acc, (uint16_t *)out2 + (size_t)m0 * N + j0, N, rows, N - j0,
+                           wi, wj, lane, wid);
+        epilogue_swiglu<W>(lds, acc, (uint16_t *)out + (size_t)m0 * (N / 2) + j0 / 2, N / 2,
+                           rows, (N - j0) / 2, wi, wj, lane);
       } else {
-        epilogue_bf16(lds, acc, (uint16_t *)out + (size_t)m0 * ncols + j0, ncols, rows,
-                      ncols - j0, wi, wj, lane, wid);
+        epilogue_bf16<W>(lds, acc, (uint16_t *)out + (size_t)m0 * ncols + j0, ncols, rows,
+                         ncols - j0, wi, wj, lane, wid);
       }
     } else {
       const int per_seg = n_it * n_ct;
@@ -494,11 +516,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_ggemm_bf16(
       const int i0 = it * BM, j0 = ct * BN;
       TileArgs ta;
       ta.wave_off = wave_off;
-      dma_init<false>(ta.a, a + (size_t)m0 * Kd + i0, ((long long)len * Kd - i0) * 2, Kd, Kd - i0);
-      dma_init<false>(ta.b, b + (size_t)m0 * N + j0, ((long long)len * N - j0) * 2, N, N - j0);
+      dma_init<W, false>(ta.a, a + (size_t)m0 * Kd + i0, ((long long)len * Kd - i0) * 2, Kd,
+                         Kd - i0);
+      dma_init<W, false>(ta.b, b + (size_t)m0 * N + j0, ((long long)len * N - j0) * 2, N, N - j0);
       ta.c_len = len;
       ta.nk = (len + BK - 1) / BK;
-      tile_mma<false, false, false>(lds, ta, acc);
+      tile_mma<W, false, false, false>(lds, ta, acc);
       // fp32 += straight from registers: staging this epilogue through LDS (as the bf16 one
       // is) measured slower, and so did starting the accumulator from the old values.
       float *o = (float *)out + ((size_t)rho * Kd + i0) * N + j0;
@@ -619,27 +642,30 @@ extern "C" moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t 
   }
   const int grid = device_cu_count();
   const uint16_t *a16 = (const uint16_t *)a, *b16 = (const uint16_t *)b;
-  // A contiguous operand whose contraction length is not a multiple of the K step needs a
-  // per-lane column test in its last K step; every other shape runs the test-free loop.
+  // FWD and DGRAD run 4 waves of 128x128, WGRAD 8 waves of 128x64 (its fp32
+  // read-modify-write epilogue needs the registers).  A contiguous operand whose contraction
+  // length is not a multiple of the K step needs a per-lane column test in its last K step;
+  // every other shape runs the test-free loop.
+  constexpr int T4 = Waves<2>::threads, T8 = Waves<4>::threads;
   switch (op) {
     case MOE_GEMM_FWD:
       if (Kd % BK)
-        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_FWD, true>), dim3(grid), dim3(kGemmThreads), 0,
+        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_FWD, true, 2>), dim3(grid), dim3(T4), 0,
                            stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
       else
-        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_FWD, false>), dim3(grid), dim3(kGemmThreads),
-                           0, stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
+        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_FWD, false, 2>), dim3(grid), dim3(T4), 0,
+                           stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
       break;
     case MOE_GEMM_DGRAD:
       if (N % BK)
-        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_DGRAD, true>), dim3(grid), dim3(kGemmThreads),
-                           0, stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
+        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_DGRAD, true, 2>), dim3(grid), dim3(T4), 0,
+                           stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
       else
-        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_DGRAD, false>), dim3(grid), dim3(kGemmThreads),
-                           0, stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
+        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_DGRAD, false, 2>), dim3(grid), dim3(T4), 0,
+                           stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
       break;
     default:
-      hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_WGRAD, false>), dim3(grid), dim3(kGemmThreads), 0,
+      hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_WGRAD, false, 4>), dim3(grid), dim3(T8), 0,
                          stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
   }
   return launch_status();
@@ -656,11 +682,13 @@ extern "C" moe_status_t moe_group_gemm_swiglu(moe_dtype dtype, int32_t G, int32_
   if (M_total == 0) return MOE_OK;
   const int grid = device_cu_count();
   const uint16_t *a16 = (const uint16_t *)a, *b16 = (const uint16_t *)b;
+  // 8 waves: the gated epilogue needs the registers the 128x128 wave tile would take
+  constexpr int T8 = Waves<4>::threads;
   if (Kd % BK)
-    hipLaunchKernelGGL((k_ggemm_bf16<kOpSwiglu, true>), dim3(grid), dim3(kGemmThreads), 0, stream,
-                       a16, b16, cu_seqlens, z, h, G, M_total, Kd, N);
+    hipLaunchKernelGGL((k_ggemm_bf16<kOpSwiglu, true, 4>), dim3(grid), dim3(T8), 0, stream, a16,
+                       b16, cu_seqlens, z, h, G, M_total, Kd, N);
   else
-    hipLaunchKernelGGL((k_ggemm_bf16<kOpSwiglu, false>), dim3(grid), dim3(kGemmThreads), 0, stream,
-                       a16, b16, cu_seqlens, z, h, G, M_total, Kd, N);
+    hipLaunchKernelGGL((k_ggemm_bf16<kOpSwiglu, false, 4>), dim3(grid), dim3(T8), 0, stream, a16,
+                       b16, cu_seqlens, z, h, G, M_total, Kd, N);
   return launch_status();
 }
