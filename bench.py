@@ -7,10 +7,11 @@ the whole hot path on rank 0, forward and backward:
   combine; weighted permute, down/up DGRAD and WGRAD, replica-gradient folds.
 value = input tokens of rank 0 per second (S / step time), inputs resident in HBM.
 
-Also printed in the same JSON line: per-kernel times and roofline fractions, the roofline
-entry of the dominant kernel (HIP events around every launch in the timed region), the same
-step at maxvio 0 and 1 (per-rank time flatness), and the CPU oracle timed on a bounded sample
-of the same step on this host.
+Also printed in the same JSON line: routed copies/s, the forward alone, per-kernel times and
+roofline fractions, the roofline entry of the dominant kernel (HIP events around every launch
+in the timed region), the same step at maxvio 0 and 1 with every rank's share timed at each
+point (flatness of rank 0's time and of the slowest rank's time across skews), and the CPU
+oracle timed on a bounded sample of the same step on this host.
 
 With --activation swiglu the up projection is the gated unit (2H' columns as (gate, up)
 pairs, silu(gate)*up in the GEMM epilogue, its derivative in a row kernel in the backward).
@@ -196,16 +197,29 @@ def setup_layer(wl, target, rank, placement="receiver0", layer=None, activation=
     return layer, idx, w, info
 
 
-def run_steps(layer, steps, warmup, timer=None):
+def run_steps(layer, steps, warmup, timer=None, forward_only=False):
     import torch
+    fn = layer.forward if forward_only else layer.step
     for _ in range(warmup):
-        layer.step()
+        fn()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        layer.step(timer)
+        fn(timer)
     torch.cuda.synchronize()
     return time.perf_counter() - t0
+
+
+def per_rank_ms(layer, reps=3, warmup=1):
+    """Step time of every rank's share (same routing), ms: each rank processes exactly S*K
+    copies, so the times should be flat across ranks as well as across skews."""
+    orig = layer.rank
+    out = []
+    for r in range(layer.s.R):
+        layer.rank = r
+        out.append(run_steps(layer, reps, warmup) * 1000.0 / reps)
+    layer.rank = orig
+    return out
 
 
 class _LazyRows:
@@ -412,11 +426,19 @@ def main():
         roof["traffic_unit"] = "bytes per launch (HBM, FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
     log(f"main: {ms_step:.3f} ms/step, {value:.0f} tokens/s, status {status}, slots used {n_slots}")
 
+    fwd_ms = run_steps(layer, args.steps, 2, forward_only=True) * 1000.0 / args.steps
+    log(f"forward only: {fwd_ms:.3f} ms/step")
+
     sweep = {}
     if not args.no_sweep and wl.name == "skew8_large_fwdbwd":
+        def rank_stats():
+            t = per_rank_ms(layer)
+            return {"max_ms": round(max(t), 4), "min_ms": round(min(t), 4),
+                    "argmax_rank": int(np.argmax(t))}
         sweep[f"{info['maxvio']:.2f}"] = {"ms_per_step": round(ms_step, 4),
                                           "tokens_per_s": round(value, 1),
-                                          "home_load_ratio": round(info["home_load_ratio"], 3)}
+                                          "home_load_ratio": round(info["home_load_ratio"], 3),
+                                          "every_rank": rank_stats()}
         for t in (0.0, 1.0):
             wl_t = synth.WORKLOADS["skew1_large"]
             layer, idx_t, _, info_t = setup_layer(wl_t, t, args.rank, layer=layer)
@@ -425,12 +447,16 @@ def main():
             sweep[f"{info_t['maxvio']:.2f}"] = {
                 "ms_per_step": round(ms_t, 4), "tokens_per_s": round(s.S / (ms_t * 1e-3), 1),
                 "home_load_ratio": round(info_t["home_load_ratio"], 3),
-                "status": int(layer.status.item())}
-            log(f"sweep maxvio {info_t['maxvio']:.2f}: {ms_t:.3f} ms/step")
+                "status": int(layer.status.item()), "every_rank": rank_stats()}
+            key = f"{info_t['maxvio']:.2f}"
+            log(f"sweep maxvio {key}: {ms_t:.3f} ms/step, every rank {sweep[key]['every_rank']}")
         # restore the headline routing for the CPU baseline below
         layer, idx, w, info = setup_layer(wl, target, args.rank, layer=layer)
-        t_all = [v["ms_per_step"] for v in sweep.values()]
+        pts = [v for v in sweep.values() if isinstance(v, dict)]
+        t_all = [v["ms_per_step"] for v in pts]
         sweep["flatness_max_over_min"] = round(max(t_all) / min(t_all), 4)
+        t_max = [v["every_rank"]["max_ms"] for v in pts]
+        sweep["flatness_of_slowest_rank"] = round(max(t_max) / min(t_max), 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -451,6 +477,9 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "copies_per_s": round(s.SK * args.steps / elapsed, 1),
+        "forward_only": {"ms_per_step": round(fwd_ms, 4),
+                         "tokens_per_s": round(s.S / (fwd_ms * 1e-3), 1)},
         "data": "synthetic",
         "config": {"workload": wl.name, "R": s.R, "S": s.S, "K": s.K, "E": s.E, "B": s.B,
                    "H": s.H, "H_prime": s.Hp, "activation": args.activation,

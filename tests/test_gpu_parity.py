@@ -373,6 +373,8 @@ GEMM_SHAPES = [
     (18, 600, 256, 512),
     (3, 2100, 520, 264),
     (9, 257, 1408, 2048),
+    (1, 300, 96, 96),         # one segment, one partial tile
+    (1088, 3000, 64, 128),    # the largest G: ~3 rows per segment, many empty
 ]
 
 
