@@ -7,7 +7,8 @@ the whole hot path on rank 0, forward and backward:
   combine; weighted permute, down/up DGRAD and WGRAD, replica-gradient folds.
 value = input tokens of rank 0 per second (S / step time), inputs resident in HBM.
 
-Also printed in the same JSON line: routed copies/s, the forward alone, per-kernel times and
+Also printed in the same JSON line: routed copies/s, the forward alone, the step replayed from
+a HIP graph (captured once; --no-graph skips it), per-kernel times and
 roofline fractions, the roofline entry of the dominant kernel (HIP events around every launch
 in the timed region), the same step at maxvio 0 and 1 with every rank's share timed at each
 point (flatness of rank 0's time and of the slowest rank's time across skews), and the CPU
@@ -210,6 +211,29 @@ def run_steps(layer, steps, warmup, timer=None, forward_only=False):
     return time.perf_counter() - t0
 
 
+def graph_replay_ms(layer, steps):
+    """The same step captured once in a HIP graph and replayed: ms per replay."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.step()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    del g
+    return ms
+
+
 def per_rank_ms(layer, reps=3, warmup=1):
     """Step time of every rank's share (same routing), ms: each rank processes exactly S*K
     copies, so the times should be flat across ranks as well as across skews."""
@@ -345,6 +369,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32768)
     ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay figure")
     ap.add_argument("--activation", choices=("identity", "swiglu"), default="identity",
                     help="activation between the projections (swiglu: gated up projection)")
     ap.add_argument("--probe", action="store_true",
@@ -428,6 +453,14 @@ def main():
 
     fwd_ms = run_steps(layer, args.steps, 2, forward_only=True) * 1000.0 / args.steps
     log(f"forward only: {fwd_ms:.3f} ms/step")
+    graph = None
+    if not args.no_graph:
+        try:
+            g_ms = graph_replay_ms(layer, args.steps)
+            graph = {"ms_per_step": round(g_ms, 4), "tokens_per_s": round(s.S / (g_ms * 1e-3), 1)}
+            log(f"graph replay: {g_ms:.3f} ms/step")
+        except Exception as exc:  # reported, not fatal: the eager figures stand
+            graph = {"error": str(exc)[:200]}
 
     sweep = {}
     if not args.no_sweep and wl.name == "skew8_large_fwdbwd":
@@ -480,6 +513,7 @@ def main():
         "copies_per_s": round(s.SK * args.steps / elapsed, 1),
         "forward_only": {"ms_per_step": round(fwd_ms, 4),
                          "tokens_per_s": round(s.S / (fwd_ms * 1e-3), 1)},
+        "graph_replay": graph,
         "data": "synthetic",
         "config": {"workload": wl.name, "R": s.R, "S": s.S, "K": s.K, "E": s.E, "B": s.B,
                    "H": s.H, "H_prime": s.Hp, "activation": args.activation,
