@@ -181,7 +181,7 @@ def setup_layer(wl, target, rank, placement="receiver0", layer=None, activation=
     log(f"routing {wl.name} maxvio target {target}: zipf s={zipf:.4f}, {time.time() - t0:.1f}s")
     if layer is None:
         layer = LayerStep(Shape(d.R, d.S, d.K, d.E, d.B, d.H, d.Hp), rank=rank,
-                          activation=activation)
+                          activation=activation, backward=wl.backward)
         seed = wl.base_seed
         synth.fill_normal_(layer.x_all, 1.0, seed * 10 + 1)
         synth.fill_normal_(layer.w_up, 0.02, seed * 10 + 2)
@@ -276,6 +276,7 @@ def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
     import torch
     import oracle
     s, r = layer.s, layer.rank
+    bwd = layer.backward_enabled
     t = {}
     t0 = time.perf_counter()
     pl = oracle.plan(idx, s.E, s.B)
@@ -290,7 +291,8 @@ def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
     cu_s = np.minimum(cu, n)
     toks = np.unique(src[:n] // s.K)
     x_rows = layer.x_all[torch.from_numpy(toks).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
-    g_rows = layer.dout_all[torch.from_numpy(toks).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    if bwd:
+        g_rows = layer.dout_all[torch.from_numpy(toks).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
     remap = {int(tk): i for i, tk in enumerate(toks)}
     src_l = np.array([remap[int(c) // s.K] * s.K + int(c) % s.K for c in src[:n]], np.int64)
     w_flat = np.zeros(len(toks) * s.K, np.float32)
@@ -308,17 +310,18 @@ def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
     else:
         z = oracle.group_gemm("fwd", xp, wu, cu_s)
     oracle.group_gemm("fwd", z, wd, cu_s)
-    dy = oracle.permute(g_rows, src_l.astype(np.int32), s.K, row_scale=w_flat)
-    dz = oracle.group_gemm("dgrad", dy, wd, cu_s)
-    dup = oracle.swiglu_backward(dz, h) if gated else dz
-    oracle.group_gemm("dgrad", dup, wu, cu_s)
-    act = [rho for rho in range(s.G) if cu_s[rho + 1] > cu_s[rho]]
-    for a, b, K_, N_ in ((z, dy, s.Hp, s.H), (xp, dup, s.H, layer.up_cols)):
-        for rho in act:                          # wgrad of the sampled segments only
-            lo, hi = cu_s[rho], cu_s[rho + 1]
-            sub = np.array([0, hi - lo])
-            oracle.group_gemm("wgrad", a[lo:hi], b[lo:hi], sub,
-                              out=np.zeros((1, K_, N_), np.float32))
+    if bwd:
+        dy = oracle.permute(g_rows, src_l.astype(np.int32), s.K, row_scale=w_flat)
+        dz = oracle.group_gemm("dgrad", dy, wd, cu_s)
+        dup = oracle.swiglu_backward(dz, h) if gated else dz
+        oracle.group_gemm("dgrad", dup, wu, cu_s)
+        act = [rho for rho in range(s.G) if cu_s[rho + 1] > cu_s[rho]]
+        for a, b, K_, N_ in ((z, dy, s.Hp, s.H), (xp, dup, s.H, layer.up_cols)):
+            for rho in act:                      # wgrad of the sampled segments only
+                lo, hi = cu_s[rho], cu_s[rho + 1]
+                sub = np.array([0, hi - lo])
+                oracle.group_gemm("wgrad", a[lo:hi], b[lo:hi], sub,
+                                  out=np.zeros((1, K_, N_), np.float32))
     t["rows"] = time.perf_counter() - t0
     # combine: tokens_sample tokens of rank r, expert outputs gathered from a staged buffer
     ts = np.arange(min(tokens_sample, s.S))
@@ -328,22 +331,26 @@ def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
     ymap = np.full(s.R * s.SK, -1, np.int64)
     ymap[need] = np.arange(need.size)
     dest_l = np.where(dest >= 0, ymap[np.maximum(dest, 0)], -1)
-    g_tok = layer.dout_all[r * s.S:(r + 1) * s.S][torch.from_numpy(ts).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
-    g_full = np.zeros((s.S, s.H), np.uint16)
-    g_full[ts] = g_tok
-    dxp_rows = layer.dxp_all[torch.from_numpy(need.astype(np.int64)).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    if bwd:
+        g_tok = layer.dout_all[r * s.S:(r + 1) * s.S][torch.from_numpy(ts).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+        g_full = np.zeros((s.S, s.H), np.uint16)
+        g_full[ts] = g_tok
+        dxp_rows = layer.dxp_all[torch.from_numpy(need.astype(np.int64)).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
     t0 = time.perf_counter()
     oracle.combine(y_rows, dest_l, w, r, s.S, s.K, tokens=ts)
-    oracle.combine_weight_grad(y_rows, dest_l, g_full, r, s.S, s.K, tokens=ts)
-    oracle.unpermute_reduce(dxp_rows, dest_l, r, s.S, s.K, tokens=ts)
+    if bwd:
+        oracle.combine_weight_grad(y_rows, dest_l, g_full, r, s.S, s.K, tokens=ts)
+        oracle.unpermute_reduce(dxp_rows, dest_l, r, s.S, s.K, tokens=ts)
     t["combine"] = time.perf_counter() - t0
     frac = 8
-    dw_u = np.zeros((s.G, s.H * layer.up_cols // frac), np.float32)
-    dw_d = np.zeros((s.G, s.H * s.Hp // frac), np.float32)
-    t0 = time.perf_counter()
-    oracle.replica_grad_fold(dw_u, pl, r)
-    oracle.replica_grad_fold(dw_d, pl, r)
-    t["fold"] = (time.perf_counter() - t0) * frac
+    t["fold"] = 0.0
+    if bwd:
+        dw_u = np.zeros((s.G, s.H * layer.up_cols // frac), np.float32)
+        dw_d = np.zeros((s.G, s.H * s.Hp // frac), np.float32)
+        t0 = time.perf_counter()
+        oracle.replica_grad_fold(dw_u, pl, r)
+        oracle.replica_grad_fold(dw_d, pl, r)
+        t["fold"] = (time.perf_counter() - t0) * frac
     est = (t["plan"] + t["layout"] + t["rows"] * s.SK / max(n, 1)
            + t["combine"] * s.S / max(len(ts), 1) + t["fold"])
     return est, t, n, len(ts)
@@ -497,11 +504,14 @@ def main():
         est, parts, n_rows, n_tok = cpu_baseline(layer, idx, w, args.cpu_rows, args.cpu_tokens)
         cpu = {"value": round(s.S / est, 2), "unit": "tokens/s", "cores": blas_threads(),
                "kind": "oracle",
-               "sample": (f"plan+layout of all {s.R} ranks' routing in full; permute, fwd up/down, "
-                          f"weighted permute, dgrad x2, wgrad x2 on {n_rows} of {s.SK} rows; "
-                          f"combine, router-weight gradient and un-permute reduce of {n_tok} of "
-                          f"{s.S} tokens; fold on 1/8 of each row; "
-                          f"each part scaled to the full step"),
+               "sample": ((f"plan+layout of all {s.R} ranks' routing in full; permute, fwd up/down, "
+                           f"weighted permute, dgrad x2, wgrad x2 on {n_rows} of {s.SK} rows; "
+                           f"combine, router-weight gradient and un-permute reduce of {n_tok} of "
+                           f"{s.S} tokens; fold on 1/8 of each row; "
+                           f"each part scaled to the full step") if layer.backward_enabled else
+                          (f"plan+layout of all {s.R} ranks' routing in full; permute, fwd up/down "
+                           f"on {n_rows} of {s.SK} rows; combine of {n_tok} of {s.S} tokens; "
+                           f"each part scaled to the full forward")),
                "seconds_measured": round(time.time() - t0, 1),
                "parts_s": {k: round(v, 3) for k, v in parts.items()}}
         log(f"cpu baseline: {cpu['value']} tokens/s ({cpu['seconds_measured']} s)")
@@ -517,7 +527,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "R": s.R, "S": s.S, "K": s.K, "E": s.E, "B": s.B,
                    "H": s.H, "H_prime": s.Hp, "activation": args.activation,
-                   "rank": args.rank, "step": "forward+backward",
+                   "rank": args.rank,
+                   "step": "forward+backward" if layer.backward_enabled else "forward",
                    "maxvio": round(info["maxvio"], 3), "zipf_s": info["zipf_s"],
                    "plan_status": status, "replica_slots_used_on_rank": n_slots},
         "roofline": roof,
