@@ -161,7 +161,8 @@ def algorithmic_work(shape, n_slots_used, gated=False):
         "permute_weighted": ("hbm", 2.0 * SK * H * 2 + 8.0 * SK),
         "gemm_dgrad": ("mfma", gemm * both),
         "gemm_wgrad": ("mfma", gemm * both),
-        "fold": ("hbm", 3.0 * n_slots_used * H * Hp * 4 * both),
+        # home row read and written, slot row read and zeroed (fp32)
+        "fold": ("hbm", 4.0 * n_slots_used * H * Hp * 4 * both),
         "combine_wgrad": ("hbm", SK * H * 2.0 + S * H * 2.0 + 8.0 * SK),
         "unpermute_reduce": ("hbm", SK * H * 2.0 + S * H * 2.0 + 4.0 * SK),
         # reads h [SK, 2H'] and dz [SK, H'], writes dh [SK, 2H'] (bf16)
