@@ -22,7 +22,9 @@
 //   * interleaved K loop: each wave issues one fragment read or load behind
 //     each MFMA (see tile_mma);
 //   * the MFMA is issued as (column-side x row-side) so each lane ends with
-//     4 consecutive output columns: 8-byte bf16 / 16-byte fp32 stores;
+//     4 consecutive output columns; output tiles leave through LDS so that
+//     global memory sees whole rows (bf16 stores; WGRAD's fp32
+//     read-modify-write, see wgrad_rmw_full);
 //   * blockIdx is remapped so the 32 workgroups of one XCD work on
 //     neighbouring tiles (shared weight and activation panels in that XCD's
 //     L2); tiles are walked in groups of 8 row-tiles.
@@ -448,6 +450,68 @@ __device__ inline void epilogue_swiglu(uint16_t *lds, const f32x16 (&acc)[W::TM]
   __syncthreads();
 }
 
+// WGRAD epilogue of a tile inside the output (every element in range): fp32 out += acc, staged
+// through LDS (free once the K loop has drained) so that global memory sees whole rows.  Two
+// passes; in pass p every wave writes its row blocks tm = 2p, 2p+1 into LDS (tile rows
+// 64p .. 64p+63 and 128+64p .. 128+64p+63: 128 rows x 1 KB) and issues its loads of the old
+// values, then after a barrier every thread adds and stores 16 chunks of 16 bytes, a wave
+// instruction covering one whole 1-KB row.  Compared with read-modify-writes straight from
+// the accumulator layout (32 bytes of each of 32 rows per instruction) this sends 8x fewer
+// requests to L2 for the same bytes; the old values are read and written non-temporally
+// (each is touched once per call).  LDS rows are padded to kRmwLd floats, which spreads the
+// 32 rows a wave writes per instruction over all banks.
+constexpr int kRmwLd = 260;
+constexpr int kRmwLdsElems = 2 * 128 * kRmwLd;  // bf16 elements of the staging area
+constexpr int kNonTemporal = 2;                 // cache-policy bit of buffer loads and stores
+
+template <class W>
+__device__ inline void wgrad_rmw_full(float *o, int N, const f32x16 (&acc)[W::TM][W::TN],
+                                      uint16_t *lds_raw, int wi, int wj, int lane) {
+  constexpr int TN = W::TN;
+  static_assert(W::threads == 512 && W::TM == 4, "8 waves of 128-row blocks");
+  float *L = (float *)lds_raw;  // 128 rows x kRmwLd floats
+  const int c = threadIdx.x & 63, r0 = threadIdx.x >> 6;  // chunk, first staged row (+8 q)
+  // one resource over the tile's 256 rows; per-lane offset of (row r0, chunk c), the row of
+  // each load and store in the (wave-uniform) scalar offset
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(o, (long long)BM * N * 4);
+  const int voff = (r0 * N + c * 4) * 4;
+  float *wr = L + ((wi >> 1) + (lane & 31)) * kRmwLd + wj + (lane >> 5) * 4;
+  const float *rd = L + r0 * kRmwLd + c * 4;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16 &a = acc[2 * p + b][tn];
+          const f32x4 v = {a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+          *(f32x4 *)(wr + b * 32 * kRmwLd + tn * 32 + g * 8) = v;
+        }
+    // staged row r0 + 8q is tile row 64p + r0 + 8q (q < 8) or 128 + 64p + r0 + 8(q - 8)
+    u32x4 old[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      old[q] = __builtin_amdgcn_raw_buffer_load_b128(
+          rs, voff, ((q < 8 ? 64 * p : 64 + 64 * p) + 8 * q) * N * 4, kNonTemporal);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const f32x4 a = *(const f32x4 *)(rd + 8 * q * kRmwLd);
+      f32x4 v = __builtin_bit_cast(f32x4, old[q]);
+      v[0] += a[0];
+      v[1] += a[1];
+      v[2] += a[2];
+      v[3] += a[3];
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff,
+                                             ((q < 8 ? 64 * p : 64 + 64 * p) + 8 * q) * N * 4,
+                                             kNonTemporal);
+    }
+    __syncthreads();
+  }
+}
+
 template <int OP, bool RAGGED, int WN>
 __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
@@ -455,7 +519,11 @@ __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
     int M_total, int Kd, int N) {
   using W = Waves<WN>;
   constexpr int TM = W::TM, TN = W::TN;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * STAGE_ELEMS];
+  // the K loop's ring; the 8-wave WGRAD epilogue stages through a slightly larger area
+  constexpr int kLdsElems = OP == MOE_GEMM_WGRAD && kRmwLdsElems > kStages * STAGE_ELEMS
+                                ? kRmwLdsElems
+                                : kStages * STAGE_ELEMS;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
   __shared__ int sCu[kMaxG + 1], sStart[kMaxG + 1];
   const bool wgrad = OP == MOE_GEMM_WGRAD;
   const int n_rt_total = build_tiles<W>(cu, G, M_total, sCu, sStart, wgrad);
@@ -522,9 +590,15 @@ __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
       ta.c_len = len;
       ta.nk = (len + BK - 1) / BK;
       tile_mma<W, false, false, false>(lds, ta, acc);
-      // fp32 += straight from registers: staging this epilogue through LDS (as the bf16 one
-      // is) measured slower, and so did starting the accumulator from the old values.
       float *o = (float *)out + ((size_t)rho * Kd + i0) * N + j0;
+      if constexpr (OP == MOE_GEMM_WGRAD && WN == 4) {
+        if (i0 + BM <= Kd && j0 + BN <= N) {
+          wgrad_rmw_full<W>(o, N, acc, lds, wi, wj, lane);
+          continue;
+        }
+      }
+      // a tile cut by the edge of the output: fp32 += straight from registers, one row block
+      // at a time (column and row tests per 16-byte element)
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         const int i = wi + tm * 32 + (lane & 31);
