@@ -512,20 +512,142 @@ __device__ inline void wgrad_rmw_full(float *o, int N, const f32x16 (&acc)[W::TM
   }
 }
 
+// Per-workgroup constants of the tile loops.
+struct TileCtx {
+  int lane, wid, wi, wj;
+  uint32_t wave_off;  // this wave's 1-KB block offset within an operand tile (wave-uniform)
+};
+
+template <class W>
+__device__ inline TileCtx tile_ctx() {
+  TileCtx c;
+  c.lane = threadIdx.x & 63;
+  c.wid = threadIdx.x >> 6;
+  c.wi = (c.wid / W::N) * (32 * W::TM);
+  c.wj = (c.wid % W::N) * (32 * W::TN);
+  c.wave_off = __builtin_amdgcn_readfirstlane(c.wid) * 1024;
+  return c;
+}
+
+// Output tile t of the row-operand GEMMs (FWD, DGRAD, gated FWD): rows of one segment x 256
+// output columns.  FWD: out[m, j] = sum_c a[m, c] W[rho][c, j], c < Kd.  DGRAD: out[m, j] =
+// sum_c a[m, c] W[rho][j, c], c < N, j < Kd.  n_rt_total row tiles (sStart: first row tile
+// of each segment), n_ct column tiles.
+template <int OP, bool RAGGED, class W>
+__device__ inline void rows_tile(const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
+                                 void *__restrict__ out, void *__restrict__ out2, int G, int Kd,
+                                 int N, int n_rt_total, int n_ct, const int *sCu,
+                                 const int *sStart, uint16_t *lds, int t, const TileCtx &cx) {
+  f32x16 acc[W::TM][W::TN];
+  const int ncols = OP == MOE_GEMM_DGRAD ? Kd : N;
+  int rt, ct;
+  swizzle(t, n_rt_total, n_ct, &rt, &ct);
+  const int rho = find_seg(sStart, G, rt);
+  const int m0 = sCu[rho] + (rt - sStart[rho]) * BM;
+  const int rows = min(BM, sCu[rho + 1] - m0);
+  const int j0 = ct * BN;
+  const uint16_t *w = b + (size_t)rho * Kd * N;
+  TileArgs ta;
+  ta.wave_off = cx.wave_off;
+  if (OP == MOE_GEMM_FWD || OP == kOpSwiglu) {
+    dma_init<W, true>(ta.a, a + (size_t)m0 * Kd, (long long)rows * Kd * 2, Kd, rows);
+    dma_init<W, false>(ta.b, w + j0, ((long long)Kd * N - j0) * 2, N, N - j0);
+    ta.c_len = Kd;
+  } else {
+    dma_init<W, true>(ta.a, a + (size_t)m0 * N, (long long)rows * N * 2, N, rows);
+    dma_init<W, true>(ta.b, w + (size_t)j0 * N, (long long)(Kd - j0) * N * 2, N, Kd - j0);
+    ta.c_len = N;
+  }
+  ta.nk = (ta.c_len + BK - 1) / BK;
+  if (OP == MOE_GEMM_FWD || OP == kOpSwiglu)
+    tile_mma<W, true, false, RAGGED>(lds, ta, acc);
+  else
+    tile_mma<W, true, true, RAGGED>(lds, ta, acc);
+  if (OP == kOpSwiglu) {
+    // out = z [M, N/2], out2 = pre-activation h [M, N] (optional)
+    if (out2)
+      epilogue_bf16<W>(lds, acc, (uint16_t *)out2 + (size_t)m0 * N + j0, N, rows, N - j0, cx.wi,
+                       cx.wj, cx.lane, cx.wid);
+    epilogue_swiglu<W>(lds, acc, (uint16_t *)out + (size_t)m0 * (N / 2) + j0 / 2, N / 2, rows,
+                       (N - j0) / 2, cx.wi, cx.wj, cx.lane);
+  } else {
+    epilogue_bf16<W>(lds, acc, (uint16_t *)out + (size_t)m0 * ncols + j0, ncols, rows,
+                     ncols - j0, cx.wi, cx.wj, cx.lane, cx.wid);
+  }
+}
+
+// Output tile t of the weight-gradient GEMM: out[rho][i, j] += sum_m a[m, i] b[m, j] over
+// the rows m of segment rho, i < Kd, j < N; n_it x n_ct tiles per active segment (sStart:
+// index of each segment among the active ones).
+template <class W>
+__device__ inline void wgrad_tile(const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
+                                  float *__restrict__ out, int G, int Kd, int N, int n_it,
+                                  int n_ct, const int *sCu, const int *sStart, uint16_t *lds,
+                                  long long t, const TileCtx &cx) {
+  constexpr int TM = W::TM, TN = W::TN;
+  f32x16 acc[TM][TN];
+  const int per_seg = n_it * n_ct;
+  const int sidx = (int)(t / per_seg);
+  int it, ct;
+  swizzle((int)(t - (long long)sidx * per_seg), n_it, n_ct, &it, &ct);
+  const int rho = find_seg(sStart, G, sidx);
+  const int m0 = sCu[rho], len = sCu[rho + 1] - m0;
+  const int i0 = it * BM, j0 = ct * BN;
+  TileArgs ta;
+  ta.wave_off = cx.wave_off;
+  dma_init<W, false>(ta.a, a + (size_t)m0 * Kd + i0, ((long long)len * Kd - i0) * 2, Kd,
+                     Kd - i0);
+  dma_init<W, false>(ta.b, b + (size_t)m0 * N + j0, ((long long)len * N - j0) * 2, N, N - j0);
+  ta.c_len = len;
+  ta.nk = (len + BK - 1) / BK;
+  tile_mma<W, false, false, false>(lds, ta, acc);
+  float *o = out + ((size_t)rho * Kd + i0) * N + j0;
+  if (i0 + BM <= Kd && j0 + BN <= N) {
+    wgrad_rmw_full<W>(o, N, acc, lds, cx.wi, cx.wj, cx.lane);
+    return;
+  }
+  // a tile cut by the edge of the output: fp32 += straight from registers, one row block at
+  // a time (column and row tests per 16-byte element)
+  const int lane = cx.lane;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int i = cx.wi + tm * 32 + (lane & 31);
+    if (i0 + i >= Kd) continue;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j = cx.wj + tn * 32 + g * 8 + (lane >> 5) * 4;
+        if (j0 + j < N) {
+          const f32x16 &c = acc[tm][tn];
+          f32x4 *p = (f32x4 *)(o + (size_t)i * N + j);
+          f32x4 v = *p;
+          v[0] += c[4 * g + 0];
+          v[1] += c[4 * g + 1];
+          v[2] += c[4 * g + 2];
+          v[3] += c[4 * g + 3];
+          *p = v;
+        }
+      }
+    // at most one row block of read-modify-writes in flight (bounds live registers)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// LDS of the tile loops: the K loop's ring; the WGRAD epilogue stages through a slightly
+// larger area.
+constexpr int kLdsRing = kStages * STAGE_ELEMS;
+constexpr int kLdsWgrad = kRmwLdsElems > kLdsRing ? kRmwLdsElems : kLdsRing;
+
 template <int OP, bool RAGGED, int WN>
 __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
     const int32_t *__restrict__ cu, void *__restrict__ out, void *__restrict__ out2, int G,
     int M_total, int Kd, int N) {
   using W = Waves<WN>;
-  constexpr int TM = W::TM, TN = W::TN;
-  // the K loop's ring; the 8-wave WGRAD epilogue stages through a slightly larger area
-  constexpr int kLdsElems = OP == MOE_GEMM_WGRAD && kRmwLdsElems > kStages * STAGE_ELEMS
-                                ? kRmwLdsElems
-                                : kStages * STAGE_ELEMS;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
+  constexpr bool wgrad = OP == MOE_GEMM_WGRAD;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[wgrad ? kLdsWgrad : kLdsRing];
   __shared__ int sCu[kMaxG + 1], sStart[kMaxG + 1];
-  const bool wgrad = OP == MOE_GEMM_WGRAD;
   const int n_rt_total = build_tiles<W>(cu, G, M_total, sCu, sStart, wgrad);
   // FWD: i = rows, j = n in [0,N), c = kd.  DGRAD: i = rows, j = kd, c = n.
   // WGRAD: i = kd, j = n, c = rows of the segment (per active segment: n_it x n_jt tiles).
@@ -533,99 +655,15 @@ __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
   const int n_ct = (ncols + BN - 1) / BN;
   const int n_it = (Kd + BM - 1) / BM;
   const long long total = wgrad ? (long long)n_rt_total * n_it * n_ct : (long long)n_rt_total * n_ct;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wi = (wid / W::N) * (32 * TM), wj = (wid % W::N) * (32 * TN);
-  const uint32_t wave_off = __builtin_amdgcn_readfirstlane(wid) * 1024;
-
+  const TileCtx cx = tile_ctx<W>();
   for (long long t = logical_block(); t < total; t += gridDim.x) {
-    f32x16 acc[TM][TN];
-    if (!wgrad) {
-      int rt, ct;
-      swizzle((int)t, n_rt_total, n_ct, &rt, &ct);
-      const int rho = find_seg(sStart, G, rt);
-      const int m0 = sCu[rho] + (rt - sStart[rho]) * BM;
-      const int rows = min(BM, sCu[rho + 1] - m0);
-      const int j0 = ct * BN;
-      const uint16_t *w = b + (size_t)rho * Kd * N;
-      TileArgs ta;
-      ta.wave_off = wave_off;
-      if (OP == MOE_GEMM_FWD || OP == kOpSwiglu) {
-        dma_init<W, true>(ta.a, a + (size_t)m0 * Kd, (long long)rows * Kd * 2, Kd, rows);
-        dma_init<W, false>(ta.b, w + j0, ((long long)Kd * N - j0) * 2, N, N - j0);
-        ta.c_len = Kd;
-      } else {
-        dma_init<W, true>(ta.a, a + (size_t)m0 * N, (long long)rows * N * 2, N, rows);
-        dma_init<W, true>(ta.b, w + (size_t)j0 * N, (long long)(Kd - j0) * N * 2, N, Kd - j0);
-        ta.c_len = N;
-      }
-      ta.nk = (ta.c_len + BK - 1) / BK;
-      if (OP == MOE_GEMM_FWD || OP == kOpSwiglu)
-        tile_mma<W, true, false, RAGGED>(lds, ta, acc);
-      else
-        tile_mma<W, true, true, RAGGED>(lds, ta, acc);
-      if (OP == kOpSwiglu) {
-        // out = z [M, N/2], out2 = pre-activation h [M, N] (optional)
-        if (out2)
-          epilogue_bf16<W>(lds, acc, (uint16_t *)out2 + (size_t)m0 * N + j0, N, rows, N - j0,
-                           wi, wj, lane, wid);
-        epilogue_swiglu<W>(lds, acc, (uint16_t *)out + (size_t)m0 * (N / 2) + j0 / 2, N / 2,
-                           rows, (N - j0) / 2, wi, wj, lane);
-      } else {
-        epilogue_bf16<W>(lds, acc, (uint16_t *)out + (size_t)m0 * ncols + j0, ncols, rows,
-                         ncols - j0, wi, wj, lane, wid);
-      }
-    } else {
-      const int per_seg = n_it * n_ct;
-      const int sidx = (int)(t / per_seg);
-      int it, ct;
-      swizzle((int)(t - (long long)sidx * per_seg), n_it, n_ct, &it, &ct);
-      const int rho = find_seg(sStart, G, sidx);
-      const int m0 = sCu[rho], len = sCu[rho + 1] - m0;
-      const int i0 = it * BM, j0 = ct * BN;
-      TileArgs ta;
-      ta.wave_off = wave_off;
-      dma_init<W, false>(ta.a, a + (size_t)m0 * Kd + i0, ((long long)len * Kd - i0) * 2, Kd,
-                         Kd - i0);
-      dma_init<W, false>(ta.b, b + (size_t)m0 * N + j0, ((long long)len * N - j0) * 2, N, N - j0);
-      ta.c_len = len;
-      ta.nk = (len + BK - 1) / BK;
-      tile_mma<W, false, false, false>(lds, ta, acc);
-      float *o = (float *)out + ((size_t)rho * Kd + i0) * N + j0;
-      if constexpr (OP == MOE_GEMM_WGRAD && WN == 4) {
-        if (i0 + BM <= Kd && j0 + BN <= N) {
-          wgrad_rmw_full<W>(o, N, acc, lds, wi, wj, lane);
-          continue;
-        }
-      }
-      // a tile cut by the edge of the output: fp32 += straight from registers, one row block
-      // at a time (column and row tests per 16-byte element)
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int i = wi + tm * 32 + (lane & 31);
-        if (i0 + i >= Kd) continue;
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int j = wj + tn * 32 + g * 8 + (lane >> 5) * 4;
-            if (j0 + j < N) {
-              const f32x16 &c = acc[tm][tn];
-              f32x4 *p = (f32x4 *)(o + (size_t)i * N + j);
-              f32x4 v = *p;
-              v[0] += c[4 * g + 0];
-              v[1] += c[4 * g + 1];
-              v[2] += c[4 * g + 2];
-              v[3] += c[4 * g + 3];
-              *p = v;
-            }
-          }
-        // at most one row block of read-modify-writes in flight (bounds live registers)
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    if constexpr (wgrad)
+      wgrad_tile<W>(a, b, (float *)out, G, Kd, N, n_it, n_ct, sCu, sStart, lds, t, cx);
+    else
+      rows_tile<OP, RAGGED, W>(a, b, out, out2, G, Kd, N, n_rt_total, n_ct, sCu, sStart, lds,
+                               (int)t, cx);
   }
 }
-
 
 // ---------------------------------------------------------------------------------------
 // fp32 vector-ALU path (small shapes)
