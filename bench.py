@@ -378,6 +378,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=32768)
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay figure")
+    ap.add_argument("--main-only", action="store_true",
+                    help="time the main step only: no forward-only, graph-replay or sweep figures "
+                         "(keeps a profiler's per-kernel averages to the main step's launches)")
     ap.add_argument("--activation", choices=("identity", "swiglu"), default="identity",
                     help="activation between the projections (swiglu: gated up projection)")
     ap.add_argument("--probe", action="store_true",
@@ -459,10 +462,12 @@ def main():
         roof["traffic_unit"] = "bytes per launch (HBM, FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
     log(f"main: {ms_step:.3f} ms/step, {value:.0f} tokens/s, status {status}, slots used {n_slots}")
 
-    fwd_ms = run_steps(layer, args.steps, 2, forward_only=True) * 1000.0 / args.steps
-    log(f"forward only: {fwd_ms:.3f} ms/step")
+    fwd_ms = None
+    if not args.main_only:
+        fwd_ms = run_steps(layer, args.steps, 2, forward_only=True) * 1000.0 / args.steps
+        log(f"forward only: {fwd_ms:.3f} ms/step")
     graph = None
-    if not args.no_graph:
+    if not args.no_graph and not args.main_only:
         try:
             g_ms = graph_replay_ms(layer, args.steps)
             graph = {"ms_per_step": round(g_ms, 4), "tokens_per_s": round(s.S / (g_ms * 1e-3), 1)}
@@ -471,7 +476,7 @@ def main():
             graph = {"error": str(exc)[:200]}
 
     sweep = {}
-    if not args.no_sweep and wl.name == "skew8_large_fwdbwd":
+    if not args.no_sweep and not args.main_only and wl.name == "skew8_large_fwdbwd":
         def rank_stats():
             t = per_rank_ms(layer)
             return {"max_ms": round(max(t), 4), "min_ms": round(min(t), 4),
@@ -522,8 +527,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "copies_per_s": round(s.SK * args.steps / elapsed, 1),
-        "forward_only": {"ms_per_step": round(fwd_ms, 4),
-                         "tokens_per_s": round(s.S / (fwd_ms * 1e-3), 1)},
+        "forward_only": None if fwd_ms is None else {"ms_per_step": round(fwd_ms, 4),
+                                                     "tokens_per_s": round(s.S / (fwd_ms * 1e-3), 1)},
         "graph_replay": graph,
         "data": "synthetic",
         "config": {"workload": wl.name, "R": s.R, "S": s.S, "K": s.K, "E": s.E, "B": s.B,
