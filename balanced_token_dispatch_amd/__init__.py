@@ -26,7 +26,7 @@ EXPORTS = ("moe_status_string", "moe_plan_words", "moe_plan_workspace_bytes", "m
            "moe_dispatch_layout_workspace_bytes", "moe_dispatch_layout", "moe_prefetch",
            "moe_permute", "moe_group_gemm", "moe_combine", "moe_replica_grad_fold",
            "moe_unpermute_reduce", "moe_combine_weight_grad", "moe_group_gemm_swiglu",
-           "moe_swiglu_backward")
+           "moe_swiglu_backward", "moe_group_gemm_workspace_bytes")
 
 
 class MoeDims(ctypes.Structure):
@@ -47,14 +47,16 @@ _lib.moe_plan.argtypes = [_D, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.moe_dispatch_layout.argtypes = [_D, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.moe_prefetch.argtypes = [_D, _I32, _P, _P, _I64, _P]
 _lib.moe_permute.argtypes = [_D, ctypes.c_int, _I64, _P, _P, _P, _P, _P]
+_lib.moe_group_gemm_workspace_bytes.restype = _SZ
+_lib.moe_group_gemm_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
 _lib.moe_group_gemm.argtypes = [ctypes.c_int, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _P,
-                                _P, _P]
+                                _P, _P, _SZ, _P]
 _lib.moe_combine.argtypes = [_D, ctypes.c_int, _I64, _I32, _P, _P, _P, _P, _P]
 _lib.moe_replica_grad_fold.argtypes = [_D, _I32, _P, _P, _I64, _P]
 _lib.moe_unpermute_reduce.argtypes = [_D, ctypes.c_int, _I64, _I32, _P, _P, _P, _P]
 _lib.moe_combine_weight_grad.argtypes = [_D, ctypes.c_int, _I64, _I32, _P, _P, _P, _P, _P]
 _lib.moe_group_gemm_swiglu.argtypes = [ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
-                                       _P]
+                                       _P, _SZ, _P]
 _lib.moe_swiglu_backward.argtypes = [ctypes.c_int, _I64, _I64, _P, _P, _P, _P]
 for _n in EXPORTS[3:]:
     if _n.endswith("_bytes"):
@@ -134,17 +136,30 @@ def moe_permute(d, x_all, src_flat, xp, row_scale=None, stream=None):
            "moe_permute")
 
 
-def moe_group_gemm(op, a, b, cu_seqlens, out, Kd, N, stream=None):
+def group_gemm_workspace_bytes(op, dtype=BF16):
+    return _lib.moe_group_gemm_workspace_bytes(op, dtype)
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
+
+
+def moe_group_gemm(op, a, b, cu_seqlens, out, Kd, N, ws=None, stream=None):
+    """ws: optional scratch tensor of at least group_gemm_workspace_bytes(op) bytes."""
     G = cu_seqlens.numel() - 1
+    wp, wn = _ws(ws)
     _check(_lib.moe_group_gemm(op, _dtype(a), G, a.shape[0], Kd, N, _ptr(a), _ptr(b),
-                               _ptr(cu_seqlens), _ptr(out), _stream(stream)), "moe_group_gemm")
+                               _ptr(cu_seqlens), _ptr(out), wp, wn, _stream(stream)),
+           "moe_group_gemm")
 
 
-def moe_group_gemm_swiglu(a, b, cu_seqlens, z, h, Kd, N, stream=None):
+def moe_group_gemm_swiglu(a, b, cu_seqlens, z, h, Kd, N, ws=None, stream=None):
     """Gated up-projection: z = silu(gate) * up over (gate, up) column pairs of W; h optional."""
     G = cu_seqlens.numel() - 1
+    wp, wn = _ws(ws)
     _check(_lib.moe_group_gemm_swiglu(_dtype(a), G, a.shape[0], Kd, N, _ptr(a), _ptr(b),
-                                      _ptr(cu_seqlens), _ptr(z), _ptr(h), _stream(stream)),
+                                      _ptr(cu_seqlens), _ptr(z), _ptr(h), wp, wn,
+                                      _stream(stream)),
            "moe_group_gemm_swiglu")
 
 

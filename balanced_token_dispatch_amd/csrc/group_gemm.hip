@@ -27,7 +27,10 @@
 //     read-modify-write, see wgrad_rmw_full);
 //   * blockIdx is remapped so the 32 workgroups of one XCD work on
 //     neighbouring tiles (shared weight and activation panels in that XCD's
-//     L2); tiles are walked in groups of 8 row-tiles.
+//     L2); tiles are walked in groups of 8 row-tiles;
+//   * with a workspace, the row-operand GEMMs split the contraction of the
+//     tiles of a partial last round over all workgroups and add the parts in
+//     a second kernel (see sk_plan).
 // fp32 path: plain vector-ALU kernels (small shapes only).
 #include "common.hpp"
 
@@ -529,51 +532,158 @@ __device__ inline TileCtx tile_ctx() {
   return c;
 }
 
-// Output tile t of the row-operand GEMMs (FWD, DGRAD, gated FWD): rows of one segment x 256
-// output columns.  FWD: out[m, j] = sum_c a[m, c] W[rho][c, j], c < Kd.  DGRAD: out[m, j] =
-// sum_c a[m, c] W[rho][j, c], c < N, j < Kd.  n_rt_total row tiles (sStart: first row tile
-// of each segment), n_ct column tiles.
+// Split of the last, partial round of row-operand tiles (data-parallel rounds + a
+// stream-K round).  The T output tiles of a row-operand GEMM all take nk K steps; the
+// persistent grid deals them round-robin, so when T is not a multiple of the grid the last
+// round keeps only L = T mod grid workgroups busy for a whole tile.  With a workspace the
+// first F = T - L tiles are dealt as before and the L * nk K steps of the leftover tiles are
+// cut into Gs equal contiguous ranges, one per workgroup: workgroup c takes K steps
+// [start(c), start(c+1)) of the leftover list (tile u covers [u nk, (u+1) nk)), stores the
+// fp32 accumulators of every tile it covers only in part into its workspace slots (2c for
+// its first tile, 2c+1 for its last), and a second kernel adds each split tile's parts in
+// range order and runs the tile's usual epilogue.  The split is taken only when it saves
+// more than kSkGain K steps of the last round.
+constexpr int kSkGain = 48;     // K steps the split must save (covers its store and reduce)
+constexpr int kSkMinPart = 16;  // K steps per workgroup at least
+constexpr int kTileFloats = BM * BN;
+
+struct SkPlan {
+  int F, L, Gs, nk;  // whole tiles, leftover tiles, workgroups of the split, K steps per tile
+  long long J;       // K steps of the leftover tiles
+  bool on;
+  __device__ long long start(int c) const { return (long long)c * J / Gs; }
+};
+
+__device__ inline SkPlan sk_plan(long long T, int nk, int grid, bool allowed) {
+  SkPlan p;
+  p.F = (int)T;
+  p.L = 0;
+  p.Gs = 1;
+  p.nk = nk;
+  p.J = 0;
+  p.on = false;
+  const int L = (int)(T % grid);
+  if (!allowed || L == 0 || (long long)nk * (grid - L) <= (long long)kSkGain * grid) return p;
+  p.on = true;
+  p.F = (int)(T - L);
+  p.L = L;
+  p.J = (long long)L * nk;
+  p.Gs = (int)min((long long)grid, max(1LL, p.J / kSkMinPart));
+  return p;
+}
+
+// Partial accumulators of one tile in a workspace slot: 16-byte chunk i = (tm TN + tn) 4 + g
+// of thread x at slot + (i threads + x) 4 floats, so each wave instruction moves 1 KB.
+template <class W>
+__device__ inline void store_partial(float *__restrict__ slot, const f32x16 (&acc)[W::TM][W::TN]) {
+#pragma unroll
+  for (int tm = 0; tm < W::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < W::TN; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int i = (tm * W::TN + tn) * 4 + g;
+        const f32x4 v = {acc[tm][tn][4 * g], acc[tm][tn][4 * g + 1], acc[tm][tn][4 * g + 2],
+                         acc[tm][tn][4 * g + 3]};
+        *(f32x4 *)(slot + ((size_t)i * W::threads + threadIdx.x) * 4) = v;
+      }
+}
+
+template <class W>
+__device__ inline void add_partial(f32x16 (&acc)[W::TM][W::TN], const float *__restrict__ slot) {
+#pragma unroll
+  for (int tm = 0; tm < W::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < W::TN; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int i = (tm * W::TN + tn) * 4 + g;
+        const f32x4 v = *(const f32x4 *)(slot + ((size_t)i * W::threads + threadIdx.x) * 4);
+        acc[tm][tn][4 * g] += v[0];
+        acc[tm][tn][4 * g + 1] += v[1];
+        acc[tm][tn][4 * g + 2] += v[2];
+        acc[tm][tn][4 * g + 3] += v[3];
+      }
+}
+
+// Where output tile t of a row-operand GEMM lies: segment rho, first row m0, rows, first
+// output column j0 (row tiles of each segment from sStart, column tiles from n_ct).
+struct RowsTile {
+  int rho, m0, rows, j0;
+};
+
+__device__ inline RowsTile rows_tile_at(int t, int G, int n_rt_total, int n_ct, const int *sCu,
+                                        const int *sStart) {
+  RowsTile r;
+  int rt, ct;
+  swizzle(t, n_rt_total, n_ct, &rt, &ct);
+  r.rho = find_seg(sStart, G, rt);
+  r.m0 = sCu[r.rho] + (rt - sStart[r.rho]) * BM;
+  r.rows = min(BM, sCu[r.rho + 1] - r.m0);
+  r.j0 = ct * BN;
+  return r;
+}
+
+// The output-tile epilogue of the row-operand GEMMs.
+template <int OP, class W>
+__device__ inline void rows_epilogue(uint16_t *lds, const f32x16 (&acc)[W::TM][W::TN],
+                                     void *__restrict__ out, void *__restrict__ out2, int Kd,
+                                     int N, const RowsTile &r, const TileCtx &cx) {
+  if (OP == kOpSwiglu) {
+    // out = z [M, N/2], out2 = pre-activation h [M, N] (optional)
+    if (out2)
+      epilogue_bf16<W>(lds, acc, (uint16_t *)out2 + (size_t)r.m0 * N + r.j0, N, r.rows,
+                       N - r.j0, cx.wi, cx.wj, cx.lane, cx.wid);
+    epilogue_swiglu<W>(lds, acc, (uint16_t *)out + (size_t)r.m0 * (N / 2) + r.j0 / 2, N / 2,
+                       r.rows, (N - r.j0) / 2, cx.wi, cx.wj, cx.lane);
+  } else {
+    const int ncols = OP == MOE_GEMM_DGRAD ? Kd : N;
+    epilogue_bf16<W>(lds, acc, (uint16_t *)out + (size_t)r.m0 * ncols + r.j0, ncols, r.rows,
+                     ncols - r.j0, cx.wi, cx.wj, cx.lane, cx.wid);
+  }
+}
+
+// K steps [k0, k1) of output tile t of the row-operand GEMMs (FWD, DGRAD, gated FWD): rows of
+// one segment x 256 output columns.  FWD: out[m, j] = sum_c a[m, c] W[rho][c, j], c < Kd.
+// DGRAD: out[m, j] = sum_c a[m, c] W[rho][j, c], c < N, j < Kd.  The whole contraction ends
+// in the epilogue; a part of it is stored to `partial` instead.
 template <int OP, bool RAGGED, class W>
 __device__ inline void rows_tile(const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
                                  void *__restrict__ out, void *__restrict__ out2, int G, int Kd,
                                  int N, int n_rt_total, int n_ct, const int *sCu,
-                                 const int *sStart, uint16_t *lds, int t, const TileCtx &cx) {
+                                 const int *sStart, uint16_t *lds, int t, int k0, int k1,
+                                 float *__restrict__ partial, const TileCtx &cx) {
   f32x16 acc[W::TM][W::TN];
-  const int ncols = OP == MOE_GEMM_DGRAD ? Kd : N;
-  int rt, ct;
-  swizzle(t, n_rt_total, n_ct, &rt, &ct);
-  const int rho = find_seg(sStart, G, rt);
-  const int m0 = sCu[rho] + (rt - sStart[rho]) * BM;
-  const int rows = min(BM, sCu[rho + 1] - m0);
-  const int j0 = ct * BN;
-  const uint16_t *w = b + (size_t)rho * Kd * N;
+  const RowsTile r = rows_tile_at(t, G, n_rt_total, n_ct, sCu, sStart);
+  const uint16_t *w = b + (size_t)r.rho * Kd * N;
   TileArgs ta;
   ta.wave_off = cx.wave_off;
   if (OP == MOE_GEMM_FWD || OP == kOpSwiglu) {
-    dma_init<W, true>(ta.a, a + (size_t)m0 * Kd, (long long)rows * Kd * 2, Kd, rows);
-    dma_init<W, false>(ta.b, w + j0, ((long long)Kd * N - j0) * 2, N, N - j0);
+    dma_init<W, true>(ta.a, a + (size_t)r.m0 * Kd, (long long)r.rows * Kd * 2, Kd, r.rows);
+    dma_init<W, false>(ta.b, w + r.j0, ((long long)Kd * N - r.j0) * 2, N, N - r.j0);
     ta.c_len = Kd;
   } else {
-    dma_init<W, true>(ta.a, a + (size_t)m0 * N, (long long)rows * N * 2, N, rows);
-    dma_init<W, true>(ta.b, w + (size_t)j0 * N, (long long)(Kd - j0) * N * 2, N, Kd - j0);
+    dma_init<W, true>(ta.a, a + (size_t)r.m0 * N, (long long)r.rows * N * 2, N, r.rows);
+    dma_init<W, true>(ta.b, w + (size_t)r.j0 * N, (long long)(Kd - r.j0) * N * 2, N, Kd - r.j0);
     ta.c_len = N;
   }
-  ta.nk = (ta.c_len + BK - 1) / BK;
+  // K steps [k0, k1): both operands start k0 steps in (loads of steps past k1 - k0 read
+  // nothing), and the contraction length left for the ragged last step shrinks to match
+  const long long da = (long long)k0 * ta.a.step, db = (long long)k0 * ta.b.step;
+  ta.a.base += da;
+  ta.a.bytes -= da;
+  ta.b.base += db;
+  ta.b.bytes -= db;
+  ta.c_len -= k0 * BK;
+  ta.nk = k1 - k0;
   if (OP == MOE_GEMM_FWD || OP == kOpSwiglu)
     tile_mma<W, true, false, RAGGED>(lds, ta, acc);
   else
     tile_mma<W, true, true, RAGGED>(lds, ta, acc);
-  if (OP == kOpSwiglu) {
-    // out = z [M, N/2], out2 = pre-activation h [M, N] (optional)
-    if (out2)
-      epilogue_bf16<W>(lds, acc, (uint16_t *)out2 + (size_t)m0 * N + j0, N, rows, N - j0, cx.wi,
-                       cx.wj, cx.lane, cx.wid);
-    epilogue_swiglu<W>(lds, acc, (uint16_t *)out + (size_t)m0 * (N / 2) + j0 / 2, N / 2, rows,
-                       (N - j0) / 2, cx.wi, cx.wj, cx.lane);
-  } else {
-    epilogue_bf16<W>(lds, acc, (uint16_t *)out + (size_t)m0 * ncols + j0, ncols, rows,
-                     ncols - j0, cx.wi, cx.wj, cx.lane, cx.wid);
-  }
+  if (partial)
+    store_partial<W>(partial, acc);
+  else
+    rows_epilogue<OP, W>(lds, acc, out, out2, Kd, N, r, cx);
 }
 
 // Output tile t of the weight-gradient GEMM: out[rho][i, j] += sum_m a[m, i] b[m, j] over
@@ -642,8 +752,8 @@ constexpr int kLdsWgrad = kRmwLdsElems > kLdsRing ? kRmwLdsElems : kLdsRing;
 template <int OP, bool RAGGED, int WN>
 __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
-    const int32_t *__restrict__ cu, void *__restrict__ out, void *__restrict__ out2, int G,
-    int M_total, int Kd, int N) {
+    const int32_t *__restrict__ cu, void *__restrict__ out, void *__restrict__ out2,
+    float *__restrict__ ws, int G, int M_total, int Kd, int N) {
   using W = Waves<WN>;
   constexpr bool wgrad = OP == MOE_GEMM_WGRAD;
   __shared__ __attribute__((aligned(16))) uint16_t lds[wgrad ? kLdsWgrad : kLdsRing];
@@ -656,12 +766,105 @@ __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
   const int n_it = (Kd + BM - 1) / BM;
   const long long total = wgrad ? (long long)n_rt_total * n_it * n_ct : (long long)n_rt_total * n_ct;
   const TileCtx cx = tile_ctx<W>();
-  for (long long t = logical_block(); t < total; t += gridDim.x) {
-    if constexpr (wgrad)
+  if constexpr (wgrad) {
+    for (long long t = logical_block(); t < total; t += gridDim.x)
       wgrad_tile<W>(a, b, (float *)out, G, Kd, N, n_it, n_ct, sCu, sStart, lds, t, cx);
-    else
+  } else {
+    const int nk = ((OP == MOE_GEMM_DGRAD ? N : Kd) + BK - 1) / BK;
+    const SkPlan sk = sk_plan(total, nk, gridDim.x, ws != nullptr);
+    const int lb = logical_block();
+    // whole tiles lb, lb + grid, .. < F, then this workgroup's K-step range of the split
+    // round, one tile part per pass (one call site keeps one inlined copy of the tile code)
+    int t = lb;
+    long long it = 0, it_end = 0;
+    if (sk.on && lb < sk.Gs) {
+      it = sk.start(lb);
+      it_end = sk.start(lb + 1);
+    }
+    const int u_first = (int)(it / nk);
+    for (;;) {
+      int tile, k0 = 0, k1 = nk;
+      float *slot = nullptr;
+      if (t < sk.F) {
+        tile = t;
+        t += gridDim.x;
+      } else if (it < it_end) {
+        const int u = (int)(it / nk);
+        k0 = (int)(it - (long long)u * nk);
+        k1 = (int)min(it_end - (long long)u * nk, (long long)nk);
+        tile = sk.F + u;
+        if (k0 != 0 || k1 != nk) slot = ws + (size_t)(2 * lb + (u == u_first ? 0 : 1)) * kTileFloats;
+        it = (long long)(u + 1) * nk;
+      } else {
+        break;
+      }
       rows_tile<OP, RAGGED, W>(a, b, out, out2, G, Kd, N, n_rt_total, n_ct, sCu, sStart, lds,
-                               (int)t, cx);
+                               tile, k0, k1, slot, cx);
+    }
+  }
+}
+
+// Second kernel of a split last round: adds the parts of each split tile in range order
+// (fp32) and writes the tile's outputs as its epilogue would, chunk by chunk.  A chunk is one
+// 16-byte piece of a slot (4 consecutive output columns of one row, see store_partial), so
+// the reads of the parts are contiguous across threads and every workgroup of the grid takes
+// a share of every split tile.  Tiles one workgroup covered whole were written by the GEMM
+// itself.  Same grid and tile table as the GEMM (WN: its wave layout), so the same split.
+template <int OP, int WN>
+__global__ __launch_bounds__(256) void k_ggemm_sk_reduce(
+    const int32_t *__restrict__ cu, void *__restrict__ out, void *__restrict__ out2,
+    const float *__restrict__ ws, int G, int M_total, int Kd, int N) {
+  using W = Waves<WN>;      // the GEMM's layout of the slots
+  using B = Waves<2>;       // this kernel's 256 threads
+  __shared__ int sCu[kMaxG + 1], sStart[kMaxG + 1];
+  const int n_rt_total = build_tiles<B>(cu, G, M_total, sCu, sStart, false);
+  const int ncols = OP == MOE_GEMM_DGRAD ? Kd : N;
+  const int n_ct = (ncols + BN - 1) / BN;
+  const int nk = ((OP == MOE_GEMM_DGRAD ? N : Kd) + BK - 1) / BK;
+  const SkPlan sk = sk_plan((long long)n_rt_total * n_ct, nk, gridDim.x, true);
+  if (!sk.on) return;
+  constexpr int kChunks = kTileFloats / 4;
+  const long long total = (long long)sk.L * kChunks;
+  for (long long ch = (long long)blockIdx.x * B::threads + threadIdx.x; ch < total;
+       ch += (long long)gridDim.x * B::threads) {
+    const int u = (int)(ch / kChunks), e = (int)(ch - (long long)u * kChunks);
+    // the workgroups whose ranges meet [u nk, (u+1) nk): c_a .. c_b, where the last
+    // workgroup with start(c) <= x is floor(((x + 1) Gs - 1) / J)
+    const long long lo = (long long)u * nk, hi = lo + nk;
+    const int c_a = (int)min(((lo + 1) * sk.Gs - 1) / sk.J, (long long)sk.Gs - 1);
+    const int c_b = (int)min((hi * sk.Gs - 1) / sk.J, (long long)sk.Gs - 1);
+    if (c_a == c_b) continue;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int c = c_a; c <= c_b; ++c) {
+      const int first = (int)(sk.start(c) / nk);
+      const f32x4 p = *(const f32x4 *)(ws + ((size_t)(2 * c + (u == first ? 0 : 1)) * kTileFloats +
+                                             (size_t)e * 4));
+      v += p;
+    }
+    // chunk e = i * threads + x of the GEMM's thread x: accumulator block (tm, tn), group g
+    const int x = e % W::threads, i = e / W::threads;
+    const int tm = i / (W::TN * 4), tn = (i / 4) % W::TN, g = i % 4;
+    const int wid = x >> 6, lane = x & 63;
+    const int row = (wid / W::N) * (32 * W::TM) + tm * 32 + (lane & 31);
+    const int col = (wid % W::N) * (32 * W::TN) + tn * 32 + g * 8 + (lane >> 5) * 4;
+    const RowsTile r = rows_tile_at(sk.F + u, G, n_rt_total, n_ct, sCu, sStart);
+    if (row >= r.rows || r.j0 + col >= ncols) continue;
+    const size_t m = (size_t)(r.m0 + row);
+    if (OP == kOpSwiglu) {
+      if (out2) {
+        uint2 hv;
+        hv.x = pack_bf16x2(v[0], v[1]);
+        hv.y = pack_bf16x2(v[2], v[3]);
+        *(uint2 *)((uint16_t *)out2 + m * N + r.j0 + col) = hv;
+      }
+      *(uint32_t *)((uint16_t *)out + m * (N / 2) + (r.j0 + col) / 2) =
+          pack_bf16x2(silu_f32(v[0]) * v[1], silu_f32(v[2]) * v[3]);
+    } else {
+      uint2 o;
+      o.x = pack_bf16x2(v[0], v[1]);
+      o.y = pack_bf16x2(v[2], v[3]);
+      *(uint2 *)((uint16_t *)out + m * ncols + r.j0 + col) = o;
+    }
   }
 }
 
@@ -723,15 +926,44 @@ __global__ __launch_bounds__(256) void k_ggemm_f32_wgrad(const float *__restrict
 
 using namespace moe;
 
+// Workspace of the split last round: two fp32 tile slots per workgroup of the persistent grid.
+static size_t sk_workspace_bytes() { return (size_t)2 * device_cu_count() * kTileFloats * 4; }
+
+// A row-operand bf16 GEMM: the persistent kernel, then (when a workspace is given and the
+// tiles are long enough that a split could pay) the reduce of the split last round.  The
+// kernel decides on the device whether to split; the reduce returns at once when it did not.
+template <int OP, int WN>
+static void launch_rows(int contraction, const uint16_t *a, const uint16_t *b,
+                        const int32_t *cu, void *out, void *out2, void *ws, int G, int M_total,
+                        int Kd, int N, hipStream_t stream) {
+  const int grid = device_cu_count();
+  const int nk = (contraction + BK - 1) / BK;
+  float *sk_ws = ws && nk > kSkGain ? (float *)ws : nullptr;
+  if (contraction % BK)
+    hipLaunchKernelGGL((k_ggemm_bf16<OP, true, WN>), dim3(grid), dim3(Waves<WN>::threads), 0,
+                       stream, a, b, cu, out, out2, sk_ws, G, M_total, Kd, N);
+  else
+    hipLaunchKernelGGL((k_ggemm_bf16<OP, false, WN>), dim3(grid), dim3(Waves<WN>::threads), 0,
+                       stream, a, b, cu, out, out2, sk_ws, G, M_total, Kd, N);
+  if (sk_ws)
+    hipLaunchKernelGGL((k_ggemm_sk_reduce<OP, WN>), dim3(grid), dim3(256), 0, stream, cu, out,
+                       out2, sk_ws, G, M_total, Kd, N);
+}
+
+extern "C" size_t moe_group_gemm_workspace_bytes(moe_gemm_op op, moe_dtype dtype) {
+  return dtype == MOE_BF16 && op != MOE_GEMM_WGRAD ? sk_workspace_bytes() : 0;
+}
+
 extern "C" moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t G,
                                        int32_t M_total, int32_t Kd, int32_t N, const void *a,
                                        const void *b, const int32_t *cu_seqlens, void *out,
-                                       hipStream_t stream) {
+                                       void *ws, size_t ws_bytes, hipStream_t stream) {
   if (!a || !b || !cu_seqlens || !out) return MOE_EINVAL;
   if (G < 1 || G > kMaxG || M_total < 0 || Kd < 8 || N < 8 || Kd % 8 || N % 8) return MOE_EINVAL;
   if (op != MOE_GEMM_FWD && op != MOE_GEMM_DGRAD && op != MOE_GEMM_WGRAD) return MOE_EINVAL;
   if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_EINVAL;
   if ((long long)M_total * (Kd > N ? Kd : N) >= (1LL << 40)) return MOE_EINVAL;
+  if (ws && ws_bytes < moe_group_gemm_workspace_bytes(op, dtype)) return MOE_ENOSPACE;
   if (M_total == 0) return MOE_OK;
   if (dtype == MOE_F32) {
     if (op == MOE_GEMM_WGRAD) {
@@ -752,33 +984,24 @@ extern "C" moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t 
     }
     return launch_status();
   }
-  const int grid = device_cu_count();
   const uint16_t *a16 = (const uint16_t *)a, *b16 = (const uint16_t *)b;
   // FWD and DGRAD run 4 waves of 128x128, WGRAD 8 waves of 128x64 (its fp32
   // read-modify-write epilogue needs the registers).  A contiguous operand whose contraction
   // length is not a multiple of the K step needs a per-lane column test in its last K step;
   // every other shape runs the test-free loop.
-  constexpr int T4 = Waves<2>::threads, T8 = Waves<4>::threads;
   switch (op) {
     case MOE_GEMM_FWD:
-      if (Kd % BK)
-        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_FWD, true, 2>), dim3(grid), dim3(T4), 0,
-                           stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
-      else
-        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_FWD, false, 2>), dim3(grid), dim3(T4), 0,
-                           stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
+      launch_rows<MOE_GEMM_FWD, 2>(Kd, a16, b16, cu_seqlens, out, nullptr, ws, G, M_total, Kd, N,
+                                   stream);
       break;
     case MOE_GEMM_DGRAD:
-      if (N % BK)
-        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_DGRAD, true, 2>), dim3(grid), dim3(T4), 0,
-                           stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
-      else
-        hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_DGRAD, false, 2>), dim3(grid), dim3(T4), 0,
-                           stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
+      launch_rows<MOE_GEMM_DGRAD, 2>(N, a16, b16, cu_seqlens, out, nullptr, ws, G, M_total, Kd,
+                                     N, stream);
       break;
     default:
-      hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_WGRAD, false, 4>), dim3(grid), dim3(T8), 0,
-                         stream, a16, b16, cu_seqlens, out, nullptr, G, M_total, Kd, N);
+      hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_WGRAD, false, 4>), dim3(device_cu_count()),
+                         dim3(Waves<4>::threads), 0, stream, a16, b16, cu_seqlens, out, nullptr,
+                         nullptr, G, M_total, Kd, N);
   }
   return launch_status();
 }
@@ -786,21 +1009,16 @@ extern "C" moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t 
 extern "C" moe_status_t moe_group_gemm_swiglu(moe_dtype dtype, int32_t G, int32_t M_total,
                                               int32_t Kd, int32_t N, const void *a,
                                               const void *b, const int32_t *cu_seqlens,
-                                              void *z, void *h, hipStream_t stream) {
+                                              void *z, void *h, void *ws, size_t ws_bytes,
+                                              hipStream_t stream) {
   if (!a || !b || !cu_seqlens || !z) return MOE_EINVAL;
   if (dtype != MOE_BF16) return MOE_EINVAL;
   if (G < 1 || G > kMaxG || M_total < 0 || Kd < 8 || N < 16 || Kd % 8 || N % 16) return MOE_EINVAL;
   if ((long long)M_total * (Kd > N ? Kd : N) >= (1LL << 40)) return MOE_EINVAL;
+  if (ws && ws_bytes < moe_group_gemm_workspace_bytes(MOE_GEMM_FWD, dtype)) return MOE_ENOSPACE;
   if (M_total == 0) return MOE_OK;
-  const int grid = device_cu_count();
-  const uint16_t *a16 = (const uint16_t *)a, *b16 = (const uint16_t *)b;
   // 8 waves: the gated epilogue needs the registers the 128x128 wave tile would take
-  constexpr int T8 = Waves<4>::threads;
-  if (Kd % BK)
-    hipLaunchKernelGGL((k_ggemm_bf16<kOpSwiglu, true, 4>), dim3(grid), dim3(T8), 0, stream, a16,
-                       b16, cu_seqlens, z, h, G, M_total, Kd, N);
-  else
-    hipLaunchKernelGGL((k_ggemm_bf16<kOpSwiglu, false, 4>), dim3(grid), dim3(T8), 0, stream, a16,
-                       b16, cu_seqlens, z, h, G, M_total, Kd, N);
+  launch_rows<kOpSwiglu, 4>(Kd, (const uint16_t *)a, (const uint16_t *)b, cu_seqlens, z, h, ws,
+                            G, M_total, Kd, N, stream);
   return launch_status();
 }

@@ -25,9 +25,10 @@ from dataclasses import dataclass
 import torch
 
 from . import (GEMM_DGRAD, GEMM_FWD, GEMM_WGRAD, dims as _mk_dims, dispatch_layout_workspace_bytes,
-               moe_combine, moe_combine_weight_grad, moe_dispatch_layout, moe_group_gemm,
-               moe_group_gemm_swiglu, moe_permute, moe_plan, moe_prefetch, moe_replica_grad_fold,
-               moe_swiglu_backward, moe_unpermute_reduce, plan_words, plan_workspace_bytes)
+               group_gemm_workspace_bytes, moe_combine, moe_combine_weight_grad,
+               moe_dispatch_layout, moe_group_gemm, moe_group_gemm_swiglu, moe_permute, moe_plan,
+               moe_prefetch, moe_replica_grad_fold, moe_swiglu_backward, moe_unpermute_reduce,
+               plan_words, plan_workspace_bytes)
 
 
 @dataclass
@@ -70,6 +71,10 @@ class LayerStep:
         self.status = torch.zeros(1, **i32)
         ws = max(plan_workspace_bytes(self.d), dispatch_layout_workspace_bytes(self.d))
         self.ws = torch.zeros(ws, dtype=torch.uint8, device=device)
+        # the FWD and DGRAD GEMMs' scratch (split of their last round of tiles); the calls
+        # run one after another on one stream, so they share it
+        self.gemm_ws = torch.empty(group_gemm_workspace_bytes(GEMM_FWD), dtype=torch.uint8,
+                                   device=device) if dtype == torch.bfloat16 else None
         self.cu = torch.zeros(s.G + 1, **i32)
         self.dest = torch.zeros(s.R * s.SK, **i32)
         self.src = torch.zeros(s.SK, **i32)
@@ -127,12 +132,12 @@ class LayerStep:
         c(timer, "permute", moe_permute, self.d, self.x_all, self.src, self.xp)
         if self.activation == "swiglu":
             c(timer, "gemm_fwd_swiglu", moe_group_gemm_swiglu, self.xp, self.w_up, self.cu, self.z,
-              self.hpre, s.H, self.up_cols)
+              self.hpre, s.H, self.up_cols, self.gemm_ws)
         else:
             c(timer, "gemm_fwd", moe_group_gemm, GEMM_FWD, self.xp, self.w_up, self.cu, self.z,
-              s.H, s.Hp)
+              s.H, s.Hp, self.gemm_ws)
         c(timer, "gemm_fwd", moe_group_gemm, GEMM_FWD, self.z, self.w_down, self.cu, self.y, s.Hp,
-          s.H)
+          s.H, self.gemm_ws)
         c(timer, "combine", moe_combine, self.d, r, self.y_all, self.dest,
           self.topk_w.view(-1), self.out)
 
@@ -143,7 +148,7 @@ class LayerStep:
         c(timer, "combine_wgrad", moe_combine_weight_grad, self.d, r, self.y_all, self.dest,
           self.dout_all[r * s.S:(r + 1) * s.S], self.dtopk_w)
         c(timer, "gemm_dgrad", moe_group_gemm, GEMM_DGRAD, self.dy, self.w_down, self.cu, self.dz,
-          s.Hp, s.H)
+          s.Hp, s.H, self.gemm_ws)
         c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.z, self.dy, self.cu, self.dw_down,
           s.Hp, s.H)
         dup = self.dz
@@ -151,7 +156,7 @@ class LayerStep:
             c(timer, "swiglu_bwd", moe_swiglu_backward, self.hpre, self.dz, self.dh)
             dup = self.dh
         c(timer, "gemm_dgrad", moe_group_gemm, GEMM_DGRAD, dup, self.w_up, self.cu, self.dxp,
-          s.H, self.up_cols)
+          s.H, self.up_cols, self.gemm_ws)
         c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.xp, dup, self.cu, self.dw_up,
           s.H, self.up_cols)
         c(timer, "unpermute_reduce", moe_unpermute_reduce, self.d, r, self.dxp_all, self.dest,

@@ -190,11 +190,20 @@ moe_status_t moe_permute(const moe_dims *dims, moe_dtype dtype, int64_t width,
  *   DGRAD: a [M_total, N],  b = W [G, Kd, N]        -> out [M_total, Kd]
  *   WGRAD: a [M_total, Kd], b [M_total, N]          -> out fp32 [G, Kd, N], +=
  *   cu_seqlens [G+1] int32, non-decreasing, cu_seqlens[G] <= M_total.
- *   Kd % 8 == 0, N % 8 == 0.  No workspace.
+ *   Kd % 8 == 0, N % 8 == 0.
+ *   ws: optional device scratch (NULL: none) of at least
+ *   moe_group_gemm_workspace_bytes(op, dtype) bytes, else MOE_ENOSPACE.  With
+ *   it, bf16 FWD and DGRAD may split the contraction of the output tiles of
+ *   the persistent grid's last, partial round over all workgroups and add the
+ *   fp32 parts in a second kernel (same stream): the result is then rounded
+ *   from a sum in a different order than without the workspace (deterministic
+ *   for given inputs).  Calls that share one workspace must not overlap.
  * ------------------------------------------------------------------------- */
+size_t moe_group_gemm_workspace_bytes(moe_gemm_op op, moe_dtype dtype);
 moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t G, int32_t M_total,
                             int32_t Kd, int32_t N, const void *a, const void *b,
-                            const int32_t *cu_seqlens, void *out, hipStream_t stream);
+                            const int32_t *cu_seqlens, void *out, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_group_gemm_swiglu -- the FWD grouped GEMM with a gated (SwiGLU) epilogue:
@@ -207,12 +216,13 @@ moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t G, int32_t 
  * to the accumulators.  bf16 only.
  *   a [M_total, Kd], b = W [G, Kd, N] (N % 16 == 0), cu_seqlens as in
  *   moe_group_gemm, z [M_total, N/2] bf16, h [M_total, N] bf16 or NULL (the
- *   pre-activation, rounded once, kept for moe_swiglu_backward).
+ *   pre-activation, rounded once, kept for moe_swiglu_backward).  ws, ws_bytes
+ *   as for moe_group_gemm(FWD).
  * ------------------------------------------------------------------------- */
 moe_status_t moe_group_gemm_swiglu(moe_dtype dtype, int32_t G, int32_t M_total, int32_t Kd,
                                    int32_t N, const void *a, const void *b,
-                                   const int32_t *cu_seqlens, void *z, void *h,
-                                   hipStream_t stream);
+                                   const int32_t *cu_seqlens, void *z, void *h, void *ws,
+                                   size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_swiglu_backward -- gradient of the gated unit with respect to its

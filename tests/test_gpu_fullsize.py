@@ -131,8 +131,8 @@ def test_full_size_step(name, target):
 
     # --- forward: permute, up, down, combine
     moe_permute(L.d, L.x_all, L.src, L.xp)
-    moe_group_gemm(GEMM_FWD, L.xp, L.w_up, L.cu, L.z, H, Hp)
-    moe_group_gemm(GEMM_FWD, L.z, L.w_down, L.cu, L.y, Hp, H)
+    moe_group_gemm(GEMM_FWD, L.xp, L.w_up, L.cu, L.z, H, Hp, L.gemm_ws)
+    moe_group_gemm(GEMM_FWD, L.z, L.w_down, L.cu, L.y, Hp, H, L.gemm_ws)
     moe_combine(L.d, rank, L.y_all, L.dest, L.topk_w.view(-1), L.out)
     torch.cuda.synchronize()
     x_rows = host_rows(L.x_all, toks)
@@ -172,11 +172,11 @@ def test_full_size_step(name, target):
 
     # --- backward: weighted permute, down dgrad/wgrad, up dgrad/wgrad, fold
     moe_permute(L.d, L.dout_all, L.src, L.dy, L.topk_w.view(-1))
-    moe_group_gemm(GEMM_DGRAD, L.dy, L.w_down, L.cu, L.dz, Hp, H)
+    moe_group_gemm(GEMM_DGRAD, L.dy, L.w_down, L.cu, L.dz, Hp, H, L.gemm_ws)
     L.dw_down.zero_()
     L.dw_up.zero_()
     moe_group_gemm(GEMM_WGRAD, L.z, L.dy, L.cu, L.dw_down, Hp, H)
-    moe_group_gemm(GEMM_DGRAD, L.dz, L.w_up, L.cu, L.dxp, H, Hp)
+    moe_group_gemm(GEMM_DGRAD, L.dz, L.w_up, L.cu, L.dxp, H, Hp, L.gemm_ws)
     moe_group_gemm(GEMM_WGRAD, L.xp, L.dz, L.cu, L.dw_up, H, Hp)
     torch.cuda.synchronize()
     g_rows = host_rows(L.dout_all, toks)

@@ -351,7 +351,13 @@ def _gemm_inputs(op, G, M, Kd, N, dtype, gen):
     return a, b
 
 
-def _run_gemm(op, a, b, cu, Kd, N, dtype, out_init=None):
+def _gemm_ws(m, op):
+    """A GEMM workspace filled with 0xFF bytes (NaN floats), to see whether it was written."""
+    n = m.group_gemm_workspace_bytes(op)
+    return torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+
+
+def _run_gemm(op, a, b, cu, Kd, N, dtype, out_init=None, ws=None):
     m = mod()
     opc = {"fwd": m.GEMM_FWD, "dgrad": m.GEMM_DGRAD, "wgrad": m.GEMM_WGRAD}[op]
     ad, bd, cud = from_bits(a), from_bits(b), _dev(cu)
@@ -362,7 +368,7 @@ def _run_gemm(op, a, b, cu, Kd, N, dtype, out_init=None):
     else:
         cols = N if op == "fwd" else Kd
         out = poisoned((M, cols), torch.bfloat16 if dtype == "bf16" else torch.float32)
-    m.moe_group_gemm(opc, ad, bd, cud, out, Kd, N)
+    m.moe_group_gemm(opc, ad, bd, cud, out, Kd, N, ws)
     return bits(out) if op != "wgrad" else out.cpu().numpy()
 
 
@@ -414,6 +420,84 @@ def test_group_gemm_random_bf16(op, shape):
         assert err <= 1e-4, err
     else:
         check_close(got, ref, "bf16", what=f"gemm {op} {shape}")
+
+
+# Shapes whose last round of tiles the kernel splits over the workgroups when given a
+# workspace (64 or more K steps per tile, leftover tiles well under a round of 256 CUs).
+SPLIT_CASES = [
+    # op, G, M, Kd, N
+    ("fwd", 5, 3000, 2048, 256),      # ~14 tiles, no whole round: every tile split
+    ("fwd", 4, 1500, 2056, 512),      # ragged contraction: 65 K steps, the last one partial
+    ("dgrad", 3, 2100, 256, 2048),
+    ("dgrad", 6, 1800, 520, 2056),    # ragged contraction, a partial column tile
+    ("fwd", 3, 66000, 2048, 256),     # more tiles than a round: whole rounds, then the split
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES)
+def test_group_gemm_split_round_integer_exact(case):
+    """Ternary inputs: every partial sum is exact, so the split result is the oracle's, bit for
+    bit, and equal to the unsplit kernel's; the workspace was used."""
+    op, G, M, Kd, N = case
+    m = mod()
+    rng = np.random.default_rng(G * 13 + M)
+    cu = _segments(rng, G, M - 3)
+    a, b = _gemm_inputs(op, G, M, Kd, N, "bf16", lambda t, s: synth.host_ternary(G + M, t, s))
+    ws = _gemm_ws(m, m.GEMM_FWD if op == "fwd" else m.GEMM_DGRAD)
+    log(f"gemm split op={op} shape={case[1:]}")
+    got = _run_gemm(op, a, b, cu, Kd, N, "bf16", ws=ws)
+    assert (ws != 0xFF).any(), "the last round was not split"
+    plain = _run_gemm(op, a, b, cu, Kd, N, "bf16")
+    ref = oracle.group_gemm(op, a, b, cu, "bf16")
+    rows = cu[-1]
+    assert (got[:rows] == ref[:rows]).all()
+    assert (got == plain).all()
+    assert (got[rows:].view(np.uint16) == 0x7F7F).all(), "rows outside segments untouched"
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES[:4])
+def test_group_gemm_split_round_random(case):
+    """Random inputs: within the bf16 tolerance of the oracle, close to the unsplit result,
+    and the same on a second call."""
+    op, G, M, Kd, N = case
+    m = mod()
+    rng = np.random.default_rng(G * 17 + M)
+    cu = _segments(rng, G, M)
+    a, b = _gemm_inputs(op, G, M, Kd, N, "bf16",
+                        lambda t, s: synth.host_normal(G + M, t, s, 1.0 if t == 1 else 0.05))
+    ws = _gemm_ws(m, m.GEMM_FWD if op == "fwd" else m.GEMM_DGRAD)
+    got = _run_gemm(op, a, b, cu, Kd, N, "bf16", ws=ws)
+    again = _run_gemm(op, a, b, cu, Kd, N, "bf16", ws=ws)
+    assert (got == again).all()
+    ref = oracle.group_gemm(op, a, b, cu, "bf16")
+    check_close(got, ref, "bf16", what=f"split gemm {op} {case[1:]}")
+    # the split changes only the fp32 summation order of the last round's tiles: the two
+    # results differ in rare last-place roundings
+    plain = _run_gemm(op, a, b, cu, Kd, N, "bf16")
+    check_close(got[:cu[-1]], plain[:cu[-1]], "bf16", tol=1e-2, min_identical=0.98,
+                what="split vs unsplit")
+
+
+def test_group_gemm_swiglu_split_round():
+    """The gated FWD with a split last round: pre-activation exact on ternary inputs, z within
+    one bf16 unit of the oracle, both equal to the unsplit call's."""
+    rng = np.random.default_rng(5)
+    G, M, Kd, N = 4, 2500, 2048, 512
+    m = mod()
+    cu = _segments(rng, G, M)
+    a = synth.to_bf16_bits(synth.host_ternary(2, 1, (M, Kd)))
+    W = synth.to_bf16_bits(synth.host_ternary(2, 2, (G, Kd, N)))
+    ws = _gemm_ws(m, m.GEMM_FWD)
+    z, h = poisoned((M, N // 2), torch.bfloat16), poisoned((M, N), torch.bfloat16)
+    m.moe_group_gemm_swiglu(from_bits(a), from_bits(W), _dev(cu), z, h, Kd, N, ws)
+    assert (ws != 0xFF).any(), "the last round was not split"
+    z0, h0 = poisoned((M, N // 2), torch.bfloat16), poisoned((M, N), torch.bfloat16)
+    m.moe_group_gemm_swiglu(from_bits(a), from_bits(W), _dev(cu), z0, h0, Kd, N)
+    z_ref, h_ref = oracle.group_gemm_swiglu(a, W, cu, "bf16")
+    rows = np.arange(cu[0], cu[-1])
+    assert (bits(h)[rows] == h_ref[rows]).all()
+    assert (bits(h) == bits(h0)).all() and (bits(z) == bits(z0)).all()
+    within_one_bf16_ulp(bits(z)[rows], z_ref[rows], what="split swiglu z on ternary inputs")
 
 
 @pytest.mark.parametrize("op", ["fwd", "dgrad", "wgrad"])

@@ -79,14 +79,20 @@ def test_host_validation_rejects_before_launch(mod):
     assert lib.moe_replica_grad_fold(by(d), 0, P, P, 6, None) == mod.MOE_EINVAL
     assert lib.moe_prefetch(by(d), 0, P, P, 8, None) == mod.MOE_EINVAL
     gg = lib.moe_group_gemm
-    assert gg(mod.GEMM_FWD, mod.BF16, 18, 256, 12, 16, P, P, P, P, None) == mod.MOE_EINVAL  # Kd%8
-    assert gg(mod.GEMM_FWD, mod.BF16, 0, 256, 16, 16, P, P, P, P, None) == mod.MOE_EINVAL
-    assert gg(5, mod.BF16, 18, 256, 16, 16, P, P, P, P, None) == mod.MOE_EINVAL
-    assert gg(mod.GEMM_FWD, mod.BF16, 18, 256, 16, 16, None, P, P, P, None) == mod.MOE_EINVAL
+    assert gg(mod.GEMM_FWD, mod.BF16, 18, 256, 12, 16, P, P, P, P, None, 0, None) == mod.MOE_EINVAL
+    assert gg(mod.GEMM_FWD, mod.BF16, 0, 256, 16, 16, P, P, P, P, None, 0, None) == mod.MOE_EINVAL
+    assert gg(5, mod.BF16, 18, 256, 16, 16, P, P, P, P, None, 0, None) == mod.MOE_EINVAL
+    assert gg(mod.GEMM_FWD, mod.BF16, 18, 256, 16, 16, None, P, P, P, None, 0, None) == mod.MOE_EINVAL
+    need = mod.group_gemm_workspace_bytes(mod.GEMM_FWD)
+    assert need > 0 and mod.group_gemm_workspace_bytes(mod.GEMM_WGRAD) == 0
+    assert mod.group_gemm_workspace_bytes(mod.GEMM_FWD, mod.F32) == 0
+    assert gg(mod.GEMM_FWD, mod.BF16, 18, 256, 16, 16, P, P, P, P, P, need - 1, None) == mod.MOE_ENOSPACE
+    assert gg(mod.GEMM_DGRAD, mod.BF16, 18, 256, 16, 16, P, P, P, P, P, 0, None) == mod.MOE_ENOSPACE
     sw = lib.moe_group_gemm_swiglu
-    assert sw(mod.BF16, 18, 256, 16, 24, P, P, P, P, None, None) == mod.MOE_EINVAL  # N%16
-    assert sw(mod.F32, 18, 256, 16, 32, P, P, P, P, None, None) == mod.MOE_EINVAL   # bf16 only
-    assert sw(mod.BF16, 18, 256, 16, 32, P, P, P, None, None, None) == mod.MOE_EINVAL
+    assert sw(mod.BF16, 18, 256, 16, 24, P, P, P, P, None, None, 0, None) == mod.MOE_EINVAL  # N%16
+    assert sw(mod.F32, 18, 256, 16, 32, P, P, P, P, None, None, 0, None) == mod.MOE_EINVAL   # bf16
+    assert sw(mod.BF16, 18, 256, 16, 32, P, P, P, None, None, None, 0, None) == mod.MOE_EINVAL
+    assert sw(mod.BF16, 18, 256, 16, 32, P, P, P, P, None, P, need - 1, None) == mod.MOE_ENOSPACE
     assert lib.moe_swiglu_backward(mod.BF16, 4, 4, P, P, P, None) == mod.MOE_EINVAL  # 8 B rows
     assert lib.moe_swiglu_backward(mod.F32, 4, 8, None, P, P, None) == mod.MOE_EINVAL
     assert lib.moe_status_string(mod.MOE_ENOSPACE).startswith(b"workspace")
