@@ -809,11 +809,14 @@ __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
 // 16-byte piece of a slot (4 consecutive output columns of one row, see store_partial), so
 // the reads of the parts are contiguous across threads and every workgroup of the grid takes
 // a share of every split tile.  Tiles one workgroup covered whole were written by the GEMM
-// itself.  Same grid and tile table as the GEMM (WN: its wave layout), so the same split.
+// itself.  Same tile table and, through gemm_grid, the same split as the GEMM (WN: its wave
+// layout).  kSkReduceBlocks blocks per GEMM workgroup keep enough loads in flight.
+constexpr int kSkReduceBlocks = 8;
+
 template <int OP, int WN>
 __global__ __launch_bounds__(256) void k_ggemm_sk_reduce(
     const int32_t *__restrict__ cu, void *__restrict__ out, void *__restrict__ out2,
-    const float *__restrict__ ws, int G, int M_total, int Kd, int N) {
+    const float *__restrict__ ws, int gemm_grid, int G, int M_total, int Kd, int N) {
   using W = Waves<WN>;      // the GEMM's layout of the slots
   using B = Waves<2>;       // this kernel's 256 threads
   __shared__ int sCu[kMaxG + 1], sStart[kMaxG + 1];
@@ -821,7 +824,7 @@ __global__ __launch_bounds__(256) void k_ggemm_sk_reduce(
   const int ncols = OP == MOE_GEMM_DGRAD ? Kd : N;
   const int n_ct = (ncols + BN - 1) / BN;
   const int nk = ((OP == MOE_GEMM_DGRAD ? N : Kd) + BK - 1) / BK;
-  const SkPlan sk = sk_plan((long long)n_rt_total * n_ct, nk, gridDim.x, true);
+  const SkPlan sk = sk_plan((long long)n_rt_total * n_ct, nk, gemm_grid, true);
   if (!sk.on) return;
   constexpr int kChunks = kTileFloats / 4;
   const long long total = (long long)sk.L * kChunks;
@@ -835,6 +838,7 @@ __global__ __launch_bounds__(256) void k_ggemm_sk_reduce(
     const int c_b = (int)min((hi * sk.Gs - 1) / sk.J, (long long)sk.Gs - 1);
     if (c_a == c_b) continue;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int c = c_a; c <= c_b; ++c) {
       const int first = (int)(sk.start(c) / nk);
       const f32x4 p = *(const f32x4 *)(ws + ((size_t)(2 * c + (u == first ? 0 : 1)) * kTileFloats +
@@ -946,8 +950,8 @@ static void launch_rows(int contraction, const uint16_t *a, const uint16_t *b,
     hipLaunchKernelGGL((k_ggemm_bf16<OP, false, WN>), dim3(grid), dim3(Waves<WN>::threads), 0,
                        stream, a, b, cu, out, out2, sk_ws, G, M_total, Kd, N);
   if (sk_ws)
-    hipLaunchKernelGGL((k_ggemm_sk_reduce<OP, WN>), dim3(grid), dim3(256), 0, stream, cu, out,
-                       out2, sk_ws, G, M_total, Kd, N);
+    hipLaunchKernelGGL((k_ggemm_sk_reduce<OP, WN>), dim3(grid * kSkReduceBlocks), dim3(256), 0,
+                       stream, cu, out, out2, sk_ws, grid, G, M_total, Kd, N);
 }
 
 extern "C" size_t moe_group_gemm_workspace_bytes(moe_gemm_op op, moe_dtype dtype) {
