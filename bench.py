@@ -139,6 +139,41 @@ def render_traffic(fetch_csv, write_csv):
     print("\n".join(out))
 
 
+def render_mfma(csv_path):
+    """Summarise a rocprofv3 --pmc run of `bench.py --probe` with SQ_INSTS_VALU_MFMA_MOPS_BF16,
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: matrix-unit work and busy fraction of the
+    GEMM launches of the probed step."""
+    import csv
+    import collections
+
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    names, span = {}, {}
+    for r in csv.DictReader(open(csv_path)):
+        d = r["Dispatch_Id"]
+        vals[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+        span[d] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+    import synth
+    dm = synth.WORKLOADS["skew8_large_fwdbwd"].dims
+    gemm = 2.0 * dm.S * dm.K * dm.H * dm.Hp
+    simds = 256 * 4
+    out = ["| kernel | launches | MFMA GFLOP executed / launch | algorithmic GFLOP | MFMA busy, % of SIMD cycles | "
+           "clock from GRBM_GUI_ACTIVE, GHz |", "|---|---|---|---|---|---|"]
+    for k in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad"):
+        prefix = KERNEL_SOURCES[k][0]
+        ds = [d for d, n in names.items() if n.startswith(prefix) or n.startswith("void " + prefix)]
+        if not ds:
+            continue
+        ds = sorted(ds, key=int)[len(ds) // 2:]  # the probed step's launches (after the warm-up step)
+        fl = sum(vals[d]["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 for d in ds) / len(ds)
+        gui = [vals[d]["GRBM_GUI_ACTIVE"] / 8 for d in ds]  # summed over the 8 XCDs
+        busy = sum(vals[d]["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * simds) for d, g in zip(ds, gui)) / len(ds)
+        clk = sum(g / (span[d][1] - span[d][0]) for d, g in zip(ds, gui)) / len(ds)
+        out.append(f"| `{k}` | {len(ds)} | {fl / 1e9:.1f} | {gemm / 1e9:.1f} | {100 * busy:.1f} | "
+                   f"{clk:.2f} |")
+    print("\n".join(out))
+
+
 def algorithmic_work(shape, n_slots_used, gated=False):
     """Minimum bytes (or flops) per launch of each kernel of the step.
 
@@ -386,9 +421,13 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="one warm-up step, a 1 GiB calibration copy, one step (for --pmc runs)")
     ap.add_argument("--render-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--render-mfma", metavar="COUNTER_CSV")
     args = ap.parse_args()
     if args.render_traffic:
         render_traffic(*args.render_traffic)
+        return
+    if args.render_mfma:
+        render_mfma(args.render_mfma)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
