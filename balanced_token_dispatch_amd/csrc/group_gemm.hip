@@ -532,44 +532,43 @@ __device__ inline TileCtx tile_ctx() {
   return c;
 }
 
-// Split of the last, partial round of row-operand tiles (data-parallel rounds + a
-// stream-K round).  The T output tiles of a row-operand GEMM all take nk K steps; the
-// persistent grid deals them round-robin, so when T is not a multiple of the grid the last
-// round keeps only L = T mod grid workgroups busy for a whole tile.  With a workspace the
-// first F = T - L tiles are dealt as before and the L * nk K steps of the leftover tiles are
-// cut into Gs equal contiguous ranges, one per workgroup: workgroup c takes K steps
-// [start(c), start(c+1)) of the leftover list (tile u covers [u nk, (u+1) nk)), stores the
-// fp32 accumulators of every tile it covers only in part into its workspace slots (2c for
-// its first tile, 2c+1 for its last), and a second kernel adds each split tile's parts in
-// range order and runs the tile's usual epilogue.  The split is taken only when it saves
-// more than kSkGain K steps of the last round.
+// Split of the last, partial round of row-operand tiles (data-parallel rounds + a split
+// round).  The T output tiles of a row-operand GEMM all take nk K steps; the persistent grid
+// deals them round-robin, so when T is not a multiple of the grid the last round keeps only
+// L = T mod grid workgroups busy for a whole tile.  With a workspace the first F = T - L
+// tiles are dealt as before and each leftover tile u is cut into P equal K ranges (P =
+// grid / L, at least kSkMinPart K steps each): workgroup c = p L + u (in the XCD-grouped
+// order of logical_block) takes part p of tile u and stores its fp32 accumulators into
+// workspace slot c; a second kernel adds each tile's P parts in K order and runs the tile's
+// usual epilogue.  Part-major numbering puts the same K range of neighbouring tiles on one
+// XCD, so the split round shares operand panels in L2 as a whole round does.  The split is
+// taken only when it saves more than kSkGain K steps of the last round.
 constexpr int kSkGain = 48;     // K steps the split must save (covers its store and reduce)
-constexpr int kSkMinPart = 16;  // K steps per workgroup at least
+constexpr int kSkMinPart = 16;  // K steps per part at least
 constexpr int kTileFloats = BM * BN;
 
 struct SkPlan {
-  int F, L, Gs, nk;  // whole tiles, leftover tiles, workgroups of the split, K steps per tile
-  long long J;       // K steps of the leftover tiles
+  int F, L, P, nk;  // whole tiles, leftover tiles, parts per leftover tile, K steps per tile
   bool on;
-  __device__ long long start(int c) const { return (long long)c * J / Gs; }
+  __device__ int k_begin(int p) const { return (int)((long long)p * nk / P); }
 };
 
 __device__ inline SkPlan sk_plan(long long T, int nk, int grid, bool allowed) {
-  SkPlan p;
-  p.F = (int)T;
-  p.L = 0;
-  p.Gs = 1;
-  p.nk = nk;
-  p.J = 0;
-  p.on = false;
+  SkPlan s;
+  s.F = (int)T;
+  s.L = 0;
+  s.P = 1;
+  s.nk = nk;
+  s.on = false;
   const int L = (int)(T % grid);
-  if (!allowed || L == 0 || (long long)nk * (grid - L) <= (long long)kSkGain * grid) return p;
-  p.on = true;
-  p.F = (int)(T - L);
-  p.L = L;
-  p.J = (long long)L * nk;
-  p.Gs = (int)min((long long)grid, max(1LL, p.J / kSkMinPart));
-  return p;
+  if (!allowed || L == 0 || (long long)nk * (grid - L) <= (long long)kSkGain * grid) return s;
+  const int P = min(grid / L, nk / kSkMinPart);
+  if (P < 2) return s;
+  s.on = true;
+  s.F = (int)(T - L);
+  s.L = L;
+  s.P = P;
+  return s;
 }
 
 // Partial accumulators of one tile in a workspace slot: 16-byte chunk i = (tm TN + tn) 4 + g
@@ -773,28 +772,23 @@ __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
     const int nk = ((OP == MOE_GEMM_DGRAD ? N : Kd) + BK - 1) / BK;
     const SkPlan sk = sk_plan(total, nk, gridDim.x, ws != nullptr);
     const int lb = logical_block();
-    // whole tiles lb, lb + grid, .. < F, then this workgroup's K-step range of the split
-    // round, one tile part per pass (one call site keeps one inlined copy of the tile code)
+    // whole tiles lb, lb + grid, .. < F, then (workgroups lb < L P) part lb / L of leftover
+    // tile lb % L (one call site keeps one inlined copy of the tile code)
     int t = lb;
-    long long it = 0, it_end = 0;
-    if (sk.on && lb < sk.Gs) {
-      it = sk.start(lb);
-      it_end = sk.start(lb + 1);
-    }
-    const int u_first = (int)(it / nk);
+    bool part = sk.on && lb < sk.L * sk.P;
     for (;;) {
       int tile, k0 = 0, k1 = nk;
       float *slot = nullptr;
       if (t < sk.F) {
         tile = t;
         t += gridDim.x;
-      } else if (it < it_end) {
-        const int u = (int)(it / nk);
-        k0 = (int)(it - (long long)u * nk);
-        k1 = (int)min(it_end - (long long)u * nk, (long long)nk);
+      } else if (part) {
+        const int u = lb % sk.L, pp = lb / sk.L;
         tile = sk.F + u;
-        if (k0 != 0 || k1 != nk) slot = ws + (size_t)(2 * lb + (u == u_first ? 0 : 1)) * kTileFloats;
-        it = (long long)(u + 1) * nk;
+        k0 = sk.k_begin(pp);
+        k1 = sk.k_begin(pp + 1);
+        slot = ws + (size_t)lb * kTileFloats;
+        part = false;
       } else {
         break;
       }
@@ -804,13 +798,13 @@ __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
   }
 }
 
-// Second kernel of a split last round: adds the parts of each split tile in range order
+// Second kernel of a split last round: adds the P parts of each leftover tile in K order
 // (fp32) and writes the tile's outputs as its epilogue would, chunk by chunk.  A chunk is one
 // 16-byte piece of a slot (4 consecutive output columns of one row, see store_partial), so
 // the reads of the parts are contiguous across threads and every workgroup of the grid takes
-// a share of every split tile.  Tiles one workgroup covered whole were written by the GEMM
-// itself.  Same tile table and, through gemm_grid, the same split as the GEMM (WN: its wave
-// layout).  kSkReduceBlocks blocks per GEMM workgroup keep enough loads in flight.
+// a share of every split tile.  Same tile table and, through gemm_grid, the same split as the
+// GEMM (WN: its wave layout).  kSkReduceBlocks blocks per GEMM workgroup keep enough loads in
+// flight.
 constexpr int kSkReduceBlocks = 8;
 
 template <int OP, int WN>
@@ -831,20 +825,9 @@ __global__ __launch_bounds__(256) void k_ggemm_sk_reduce(
   for (long long ch = (long long)blockIdx.x * B::threads + threadIdx.x; ch < total;
        ch += (long long)gridDim.x * B::threads) {
     const int u = (int)(ch / kChunks), e = (int)(ch - (long long)u * kChunks);
-    // the workgroups whose ranges meet [u nk, (u+1) nk): c_a .. c_b, where the last
-    // workgroup with start(c) <= x is floor(((x + 1) Gs - 1) / J)
-    const long long lo = (long long)u * nk, hi = lo + nk;
-    const int c_a = (int)min(((lo + 1) * sk.Gs - 1) / sk.J, (long long)sk.Gs - 1);
-    const int c_b = (int)min((hi * sk.Gs - 1) / sk.J, (long long)sk.Gs - 1);
-    if (c_a == c_b) continue;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int c = c_a; c <= c_b; ++c) {
-      const int first = (int)(sk.start(c) / nk);
-      const f32x4 p = *(const f32x4 *)(ws + ((size_t)(2 * c + (u == first ? 0 : 1)) * kTileFloats +
-                                             (size_t)e * 4));
-      v += p;
-    }
+    for (int pp = 0; pp < sk.P; ++pp)
+      v += *(const f32x4 *)(ws + ((size_t)(pp * sk.L + u) * kTileFloats + (size_t)e * 4));
     // chunk e = i * threads + x of the GEMM's thread x: accumulator block (tm, tn), group g
     const int x = e % W::threads, i = e / W::threads;
     const int tm = i / (W::TN * 4), tn = (i / 4) % W::TN, g = i % 4;
@@ -930,8 +913,8 @@ __global__ __launch_bounds__(256) void k_ggemm_f32_wgrad(const float *__restrict
 
 using namespace moe;
 
-// Workspace of the split last round: two fp32 tile slots per workgroup of the persistent grid.
-static size_t sk_workspace_bytes() { return (size_t)2 * device_cu_count() * kTileFloats * 4; }
+// Workspace of the split last round: one fp32 tile slot per workgroup of the persistent grid.
+static size_t sk_workspace_bytes() { return (size_t)device_cu_count() * kTileFloats * 4; }
 
 // A row-operand bf16 GEMM: the persistent kernel, then (when a workspace is given and the
 // tiles are long enough that a split could pay) the reduce of the split last round.  The
