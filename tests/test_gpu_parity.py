@@ -182,8 +182,9 @@ def _plan_for(R, S, K, E, B, seed, skew=0.5):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("scaled", [False, True])
-def test_permute(dtype, scaled):
-    R, S, K, E, B, H = 4, 300, 3, 16, 1, 136
+@pytest.mark.parametrize("S", [300, 301])   # S*K even and odd (the weighted form pairs rows)
+def test_permute(dtype, scaled, S):
+    R, K, E, B, H = 4, 3, 16, 1, 136
     idx, pl = _plan_for(R, S, K, E, B, 3, skew=0.2)
     m = mod()
     d = m.dims(R, S, K, E, B)
