@@ -10,9 +10,10 @@
 //   * persistent grid of one workgroup per CU; every workgroup rebuilds the
 //     tile table from cu_seqlens in LDS (no host sync, the grid is sized from
 //     the machine, not from the routing);
-//   * 256x256 output tile, K step 32, v_mfma_f32_32x32x16_bf16 blocks with
-//     fp32 accumulators; FWD and DGRAD run 4 waves (one per SIMD) of 128x128,
-//     WGRAD and the gated FWD 8 waves of 128x64;
+//   * 256x256 output tile, K step 32 (DGRAD: 64-wide stages, see tile_mma64),
+//     v_mfma_f32_32x32x16_bf16 blocks with fp32 accumulators; FWD and DGRAD
+//     run 4 waves (one per SIMD) of 128x128, WGRAD and the gated FWD 8 waves
+//     of 128x64;
 //   * operands go global -> LDS with direct-to-LDS buffer loads (no register
 //     staging) into a 4-stage ring, XOR-swizzled by 16-byte chunks so the
 //     fragment reads are conflict-free; an operand whose contraction index is
@@ -308,6 +309,178 @@ __device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta,
   __syncthreads();
 }
 
+// ---- DGRAD: 64-wide K stages ----------------------------------------------------------
+// Both DGRAD operands are contiguous along the contraction, and at K steps of 32 each
+// direct-to-LDS instruction of such an operand covers 16 rows x 64 B (16 half cache lines):
+// the texture addresser, not the matrix units, then limits the loop (busy ~88% of the cycles
+// against ~55% in FWD, whose weight operand comes in 512-byte rows).  DGRAD therefore loads
+// 64-wide K stages, 8 rows x 128 B per instruction, in a ring of two 64-KB stages.  16-byte
+// chunk k (0..7) of row r sits at position k ^ ((r >> 1) & 7), which keeps the fragment reads
+// (16 rows per 256 B of banks) conflict-free.  (The FWD loop measured slower in this form:
+// its weight operand already moves whole lines, and two stages give the loads less lead than
+// the four-stage ring.)
+constexpr int BK64 = 64;
+constexpr int OP64_ELEMS = 256 * BK64;      // one operand of one stage
+constexpr int STAGE64_ELEMS = 2 * OP64_ELEMS;
+constexpr int kMaxBlk64 = 8;
+
+struct DmaOp64 {
+  const char *base;   // byte address of element (row 0, contraction 0) of the tile
+  long long bytes;    // bytes readable from base
+  int voff[kMaxBlk64];  // per-lane byte offset of this wave's blocks, or kOOB
+  int kc[kMaxBlk64];    // contraction index of each block's chunk within a stage
+};
+
+template <class W>
+__device__ inline void dma_init64(DmaOp64 &d, const uint16_t *base, long long bytes, int ld,
+                                  int row_lim) {
+  constexpr int NB = 32 / W::n;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  d.base = (const char *)base;
+  d.bytes = bytes;
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int blk = u * W::n + wid;        // 1-KB block of the 32-KB operand tile
+    const int o = blk * 1024 + lane * 16;  // this lane's LDS byte offset
+    const int r = o >> 7, p = (o >> 4) & 7;
+    const int k = p ^ ((r >> 1) & 7);
+    d.voff[u] = r < row_lim ? (r * ld + k * 8) * 2 : kOOB;
+    d.kc[u] = k * 8;
+  }
+}
+
+// Buffer resource of stage kt (a zero-byte resource past the last stage).
+__device__ inline __amdgpu_buffer_rsrc_t dma_rsrc64(const DmaOp64 &d, int kt, int nk) {
+  const long long c0b = (long long)kt * BK64 * 2;
+  const long long rem = d.bytes - c0b;
+  return make_rsrc(d.base + c0b, (kt < nk && rem > 0) ? rem : 0);
+}
+
+template <class W, bool RAGGED>
+__device__ inline void dma_one64(const DmaOp64 &d, __amdgpu_buffer_rsrc_t rs, uint32_t lds_op,
+                                 uint32_t wave_off, int kt, int c_lim, int u) {
+  int off = d.voff[u];
+  if (RAGGED) off = kt * BK64 + d.kc[u] < c_lim ? off : kOOB;
+  // as dma_one: direct-to-LDS load at M0 + 16 * lane, one wait state after the M0 write
+  const uint32_t m0 = lds_op + wave_off + u * W::n * 1024;
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off),
+      "s"(rs), "{m0}"(m0)
+      : "memory");
+}
+
+// MFMA operand t of lane `lane` at contraction 16 ks + 8 (lane / 32) .. +8 of the stage.
+__device__ inline bf16x8 read_operand64(const uint16_t *src, int wbase, int t, int lane, int ks) {
+  const int r = wbase + 32 * t + (lane & 31);
+  const int k = 2 * ks + (lane >> 5);
+  const int p = k ^ ((r >> 1) & 7);
+  return __builtin_bit_cast(bf16x8, *(const u32x4 *)(src + r * BK64 + p * 8));
+}
+
+struct TileArgs64 {
+  DmaOp64 a, b;
+  int c_len, nk;      // contraction length from the first stage, stages
+  uint32_t wave_off;  // this wave's 1-KB block offset within an operand tile (wave-uniform)
+};
+
+// One 256x256 output tile from two contiguous operands, stage s in LDS stage s % 2.  Stage s:
+// sub-steps 0..3 of 16, TM*TN MFMAs each; sub-steps 0-2 read the next sub-step's fragments
+// and sub-step 0 issues the column-side loads of stage s+1 (its row-side loads went out in
+// sub-step 3 of stage s-1); after sub-step 2 each wave waits for its loads (stage s+1) and a
+// barrier follows, after which stage s+1 has landed everywhere and stage s has been read
+// everywhere (the barrier waits for this wave's LDS reads); sub-step 3 reads stage s+1's first
+// fragments and issues the row-side loads of stage s+2 into stage s's buffer.  The prologue
+// issues stage 0 and the row side of stage 1 and waits for stage 0.  Loads of stages past the
+// last write zeros into buffers no later read uses.
+template <class W, bool RAGGED>
+__device__ inline void tile_mma64(uint16_t *lds, const TileArgs64 &ta,
+                                  f32x16 (&acc)[W::TM][W::TN]) {
+  constexpr int TM = W::TM, TN = W::TN, NB = 32 / W::n;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wi = (wid / W::N) * (32 * TM), wj = (wid % W::N) * (32 * TN);
+  const int nk = ta.nk;
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = (f32x16){};
+  auto stage_addr = [&](int s) {
+    return (uint32_t)(uintptr_t)(lds_vptr)(lds + (s & 1) * STAGE64_ELEMS);
+  };
+  {
+    const __amdgpu_buffer_rsrc_t ra0 = dma_rsrc64(ta.a, 0, nk), rb0 = dma_rsrc64(ta.b, 0, nk);
+    const __amdgpu_buffer_rsrc_t ra1 = dma_rsrc64(ta.a, 1, nk);
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      dma_one64<W, RAGGED>(ta.a, ra0, stage_addr(0), ta.wave_off, 0, ta.c_len, u);
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      dma_one64<W, RAGGED>(ta.b, rb0, stage_addr(0) + OP64_ELEMS * 2, ta.wave_off, 0, ta.c_len,
+                           u);
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      dma_one64<W, RAGGED>(ta.a, ra1, stage_addr(1), ta.wave_off, 1, ta.c_len, u);
+  }
+  waitcnt_vm<NB>();
+  __syncthreads();
+  Frags<W> F0, F1;
+#pragma unroll
+  for (int t = 0; t < TM; ++t) F0.a[t] = read_operand64(lds, wi, t, lane, 0);
+#pragma unroll
+  for (int t = 0; t < TN; ++t) F0.b[t] = read_operand64(lds + OP64_ELEMS, wj, t, lane, 0);
+  for (int s = 0; s < nk; ++s) {
+    const uint16_t *cur = lds + (s & 1) * STAGE64_ELEMS;
+    const uint16_t *nxt = lds + ((s + 1) & 1) * STAGE64_ELEMS;
+    __amdgpu_buffer_rsrc_t rb, ra;
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {  // sub-steps 0..2
+      Frags<W> &Fc = (ks & 1) ? F1 : F0;
+      Frags<W> &Fn = (ks & 1) ? F0 : F1;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TM * TN; ++i) {
+        const int tm = i / TN, tn = i % TN;
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Fc.b[tn], Fc.a[tm], acc[tm][tn], 0,
+                                                              0, 0);
+        if (i < TM)
+          Fn.a[i] = read_operand64(cur, wi, i, lane, ks + 1);
+        else if (i < TM + TN)
+          Fn.b[i - TM] = read_operand64(cur + OP64_ELEMS, wj, i - TM, lane, ks + 1);
+        if (ks == 0) {
+          if (i == 1) rb = dma_rsrc64(ta.b, s + 1, nk);
+#pragma unroll
+          for (int u = 0; u < NB; ++u)
+            if (i == (u + 1) * TM * TN / (NB + 1))
+              dma_one64<W, RAGGED>(ta.b, rb, stage_addr(s + 1) + OP64_ELEMS * 2, ta.wave_off,
+                                   s + 1, ta.c_len, u);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    waitcnt_vm<0>();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TM * TN; ++i) {  // sub-step 3
+      const int tm = i / TN, tn = i % TN;
+      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F1.b[tn], F1.a[tm], acc[tm][tn], 0,
+                                                            0, 0);
+      if (i < TM)
+        F0.a[i] = read_operand64(nxt, wi, i, lane, 0);
+      else if (i < TM + TN)
+        F0.b[i - TM] = read_operand64(nxt + OP64_ELEMS, wj, i - TM, lane, 0);
+      if (i == 1) ra = dma_rsrc64(ta.a, s + 2, nk);
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (i == (u + 1) * TM * TN / (NB + 1))
+          dma_one64<W, RAGGED>(ta.a, ra, stage_addr(s + 2), ta.wave_off, s + 2, ta.c_len, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  waitcnt_vm<0>();  // the trailing out-of-range loads land before the stages are reused
+  __syncthreads();
+}
+
 // Decode a tile index into (row tile, col tile) walking groups of kGroupM row tiles.
 __device__ inline void swizzle(int t, int n_rt, int n_ct, int *rt, int *ct) {
   const int per_group = kGroupM * n_ct;
@@ -537,23 +710,28 @@ __device__ inline TileCtx tile_ctx() {
 // deals them round-robin, so when T is not a multiple of the grid the last round keeps only
 // L = T mod grid workgroups busy for a whole tile.  With a workspace the first F = T - L
 // tiles are dealt as before and each leftover tile u is cut into P equal K ranges (P =
-// grid / L, at least kSkMinPart K steps each): workgroup c = p L + u (in the XCD-grouped
+// grid / L, at least kSkMinPart of contraction each): workgroup c = p L + u (in the XCD-grouped
 // order of logical_block) takes part p of tile u and stores its fp32 accumulators into
 // workspace slot c; a second kernel adds each tile's P parts in K order and runs the tile's
 // usual epilogue.  Part-major numbering puts the same K range of neighbouring tiles on one
 // XCD, so the split round shares operand panels in L2 as a whole round does.  The split is
-// taken only when it saves more than kSkGain K steps of the last round.
-constexpr int kSkGain = 48;     // K steps the split must save (covers its store and reduce)
-constexpr int kSkMinPart = 16;  // K steps per part at least
+// taken only when it saves more than kSkGain of contraction in the last round.
+constexpr int kSkGain = 1536;     // contraction the split must save (covers its store and reduce)
+constexpr int kSkMinPart = 512;   // contraction per part at least
 constexpr int kTileFloats = BM * BN;
 
+// Width of a K stage of the row-operand GEMMs: 64 for DGRAD (see tile_mma64), else 32.
+template <int OP>
+constexpr int kStageK = OP == MOE_GEMM_DGRAD ? BK64 : BK;
+
 struct SkPlan {
-  int F, L, P, nk;  // whole tiles, leftover tiles, parts per leftover tile, K steps per tile
+  int F, L, P, nk;  // whole tiles, leftover tiles, parts per leftover tile, K stages per tile
   bool on;
   __device__ int k_begin(int p) const { return (int)((long long)p * nk / P); }
 };
 
-__device__ inline SkPlan sk_plan(long long T, int nk, int grid, bool allowed) {
+// nk K stages of width bk per tile
+__device__ inline SkPlan sk_plan(long long T, int nk, int bk, int grid, bool allowed) {
   SkPlan s;
   s.F = (int)T;
   s.L = 0;
@@ -561,8 +739,9 @@ __device__ inline SkPlan sk_plan(long long T, int nk, int grid, bool allowed) {
   s.nk = nk;
   s.on = false;
   const int L = (int)(T % grid);
-  if (!allowed || L == 0 || (long long)nk * (grid - L) <= (long long)kSkGain * grid) return s;
-  const int P = min(grid / L, nk / kSkMinPart);
+  if (!allowed || L == 0 || (long long)nk * bk * (grid - L) <= (long long)kSkGain * grid)
+    return s;
+  const int P = min(grid / L, nk * bk / kSkMinPart);
   if (P < 2) return s;
   s.on = true;
   s.F = (int)(T - L);
@@ -655,30 +834,35 @@ __device__ inline void rows_tile(const uint16_t *__restrict__ a, const uint16_t 
   f32x16 acc[W::TM][W::TN];
   const RowsTile r = rows_tile_at(t, G, n_rt_total, n_ct, sCu, sStart);
   const uint16_t *w = b + (size_t)r.rho * Kd * N;
-  TileArgs ta;
-  ta.wave_off = cx.wave_off;
-  if (OP == MOE_GEMM_FWD || OP == kOpSwiglu) {
+  // K stages [k0, k1): both operands start k0 stages in (loads of stages past k1 - k0 read
+  // nothing), and the contraction length left for the ragged last stage shrinks to match
+  if constexpr (OP == MOE_GEMM_DGRAD) {
+    TileArgs64 ta;
+    ta.wave_off = cx.wave_off;
+    dma_init64<W>(ta.a, a + (size_t)r.m0 * N, (long long)r.rows * N * 2, N, r.rows);
+    dma_init64<W>(ta.b, w + (size_t)r.j0 * N, (long long)(Kd - r.j0) * N * 2, N, Kd - r.j0);
+    const long long d0 = (long long)k0 * BK64 * 2;
+    ta.a.base += d0;
+    ta.a.bytes -= d0;
+    ta.b.base += d0;
+    ta.b.bytes -= d0;
+    ta.c_len = N - k0 * BK64;
+    ta.nk = k1 - k0;
+    tile_mma64<W, RAGGED>(lds, ta, acc);
+  } else {
+    TileArgs ta;
+    ta.wave_off = cx.wave_off;
     dma_init<W, true>(ta.a, a + (size_t)r.m0 * Kd, (long long)r.rows * Kd * 2, Kd, r.rows);
     dma_init<W, false>(ta.b, w + r.j0, ((long long)Kd * N - r.j0) * 2, N, N - r.j0);
-    ta.c_len = Kd;
-  } else {
-    dma_init<W, true>(ta.a, a + (size_t)r.m0 * N, (long long)r.rows * N * 2, N, r.rows);
-    dma_init<W, true>(ta.b, w + (size_t)r.j0 * N, (long long)(Kd - r.j0) * N * 2, N, Kd - r.j0);
-    ta.c_len = N;
-  }
-  // K steps [k0, k1): both operands start k0 steps in (loads of steps past k1 - k0 read
-  // nothing), and the contraction length left for the ragged last step shrinks to match
-  const long long da = (long long)k0 * ta.a.step, db = (long long)k0 * ta.b.step;
-  ta.a.base += da;
-  ta.a.bytes -= da;
-  ta.b.base += db;
-  ta.b.bytes -= db;
-  ta.c_len -= k0 * BK;
-  ta.nk = k1 - k0;
-  if (OP == MOE_GEMM_FWD || OP == kOpSwiglu)
+    const long long da = (long long)k0 * ta.a.step, db = (long long)k0 * ta.b.step;
+    ta.a.base += da;
+    ta.a.bytes -= da;
+    ta.b.base += db;
+    ta.b.bytes -= db;
+    ta.c_len = Kd - k0 * BK;
+    ta.nk = k1 - k0;
     tile_mma<W, true, false, RAGGED>(lds, ta, acc);
-  else
-    tile_mma<W, true, true, RAGGED>(lds, ta, acc);
+  }
   if (partial)
     store_partial<W>(partial, acc);
   else
@@ -769,8 +953,9 @@ __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
     for (long long t = logical_block(); t < total; t += gridDim.x)
       wgrad_tile<W>(a, b, (float *)out, G, Kd, N, n_it, n_ct, sCu, sStart, lds, t, cx);
   } else {
-    const int nk = ((OP == MOE_GEMM_DGRAD ? N : Kd) + BK - 1) / BK;
-    const SkPlan sk = sk_plan(total, nk, gridDim.x, ws != nullptr);
+    constexpr int bk = kStageK<OP>;
+    const int nk = ((OP == MOE_GEMM_DGRAD ? N : Kd) + bk - 1) / bk;
+    const SkPlan sk = sk_plan(total, nk, bk, gridDim.x, ws != nullptr);
     const int lb = logical_block();
     // whole tiles lb, lb + grid, .. < F, then (workgroups lb < L P) part lb / L of leftover
     // tile lb % L (one call site keeps one inlined copy of the tile code)
@@ -817,8 +1002,9 @@ __global__ __launch_bounds__(256) void k_ggemm_sk_reduce(
   const int n_rt_total = build_tiles<B>(cu, G, M_total, sCu, sStart, false);
   const int ncols = OP == MOE_GEMM_DGRAD ? Kd : N;
   const int n_ct = (ncols + BN - 1) / BN;
-  const int nk = ((OP == MOE_GEMM_DGRAD ? N : Kd) + BK - 1) / BK;
-  const SkPlan sk = sk_plan((long long)n_rt_total * n_ct, nk, gemm_grid, true);
+  constexpr int bk = kStageK<OP>;
+  const int nk = ((OP == MOE_GEMM_DGRAD ? N : Kd) + bk - 1) / bk;
+  const SkPlan sk = sk_plan((long long)n_rt_total * n_ct, nk, bk, gemm_grid, true);
   if (!sk.on) return;
   constexpr int kChunks = kTileFloats / 4;
   const long long total = (long long)sk.L * kChunks;
@@ -924,9 +1110,11 @@ static void launch_rows(int contraction, const uint16_t *a, const uint16_t *b,
                         const int32_t *cu, void *out, void *out2, void *ws, int G, int M_total,
                         int Kd, int N, hipStream_t stream) {
   const int grid = device_cu_count();
-  const int nk = (contraction + BK - 1) / BK;
-  float *sk_ws = ws && nk > kSkGain ? (float *)ws : nullptr;
-  if (contraction % BK)
+  // a split can pay only when a tile's contraction exceeds what it must save
+  float *sk_ws = ws && contraction > kSkGain ? (float *)ws : nullptr;
+  // a contiguous operand whose contraction is not a multiple of the K stage needs a per-lane
+  // column test in its last stage
+  if (contraction % kStageK<OP>)
     hipLaunchKernelGGL((k_ggemm_bf16<OP, true, WN>), dim3(grid), dim3(Waves<WN>::threads), 0,
                        stream, a, b, cu, out, out2, sk_ws, G, M_total, Kd, N);
   else
@@ -973,9 +1161,7 @@ extern "C" moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t 
   }
   const uint16_t *a16 = (const uint16_t *)a, *b16 = (const uint16_t *)b;
   // FWD and DGRAD run 4 waves of 128x128, WGRAD 8 waves of 128x64 (its fp32
-  // read-modify-write epilogue needs the registers).  A contiguous operand whose contraction
-  // length is not a multiple of the K step needs a per-lane column test in its last K step;
-  // every other shape runs the test-free loop.
+  // read-modify-write epilogue needs the registers); DGRAD loads 64-wide K stages.
   switch (op) {
     case MOE_GEMM_FWD:
       launch_rows<MOE_GEMM_FWD, 2>(Kd, a16, b16, cu_seqlens, out, nullptr, ws, G, M_total, Kd, N,
