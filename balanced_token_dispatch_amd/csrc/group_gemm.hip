@@ -31,7 +31,9 @@
 //     L2); tiles are walked in groups of 8 row-tiles;
 //   * with a workspace, the row-operand GEMMs split the contraction of the
 //     tiles of a partial last round over all workgroups and add the parts in
-//     a second kernel (see sk_plan).
+//     a second kernel (see sk_plan);
+//   * WGRAD tiles cost their segment's row count: segments are dealt longest
+//     first and rounds of tiles alternate direction (see order_by_length).
 // fp32 path: plain vector-ALU kernels (small shapes only).
 #include "common.hpp"
 
@@ -551,6 +553,29 @@ __device__ inline int find_seg(const int *sStart, int G, int t) {
   return lo;
 }
 
+// sOrd[i] = index (among the non-empty segments, as sStart counts them for WGRAD) of the
+// i-th longest non-empty segment; ties keep segment order.  tmp: n_ne ints of scratch LDS.
+template <class W>
+__device__ inline void order_by_length(const int *sCu, const int *sStart, int G, int n_ne,
+                                       int *sOrd, int *tmp) {
+  const int tid = threadIdx.x;
+  for (int rho = tid; rho < G; rho += W::threads) {
+    const int len = sCu[rho + 1] - sCu[rho];
+    if (len > 0) tmp[sStart[rho]] = len;
+  }
+  __syncthreads();
+  for (int i = tid; i < n_ne; i += W::threads) {
+    const int len = tmp[i];
+    int rank = 0;
+    for (int j = 0; j < n_ne; ++j) {
+      const int l = tmp[j];
+      rank += l > len || (l == len && j < i);
+    }
+    sOrd[rank] = i;
+  }
+  __syncthreads();
+}
+
 // bf16 output-tile epilogue.  The accumulator layout leaves each lane 4 consecutive columns
 // of one row, so a store straight from registers writes 32 rows x 16 B per instruction.
 // The tile goes through LDS instead (free once the K loop has drained): each wave writes its
@@ -875,15 +900,15 @@ __device__ inline void rows_tile(const uint16_t *__restrict__ a, const uint16_t 
 template <class W>
 __device__ inline void wgrad_tile(const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
                                   float *__restrict__ out, int G, int Kd, int N, int n_it,
-                                  int n_ct, const int *sCu, const int *sStart, uint16_t *lds,
-                                  long long t, const TileCtx &cx) {
+                                  int n_ct, const int *sCu, const int *sStart, const int *sOrd,
+                                  uint16_t *lds, long long t, const TileCtx &cx) {
   constexpr int TM = W::TM, TN = W::TN;
   f32x16 acc[TM][TN];
   const int per_seg = n_it * n_ct;
   const int sidx = (int)(t / per_seg);
   int it, ct;
   swizzle((int)(t - (long long)sidx * per_seg), n_it, n_ct, &it, &ct);
-  const int rho = find_seg(sStart, G, sidx);
+  const int rho = find_seg(sStart, G, sOrd[sidx]);
   const int m0 = sCu[rho], len = sCu[rho + 1] - m0;
   const int i0 = it * BM, j0 = ct * BN;
   TileArgs ta;
@@ -950,8 +975,19 @@ __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
   const long long total = wgrad ? (long long)n_rt_total * n_it * n_ct : (long long)n_rt_total * n_ct;
   const TileCtx cx = tile_ctx<W>();
   if constexpr (wgrad) {
-    for (long long t = logical_block(); t < total; t += gridDim.x)
-      wgrad_tile<W>(a, b, (float *)out, G, Kd, N, n_it, n_ct, sCu, sStart, lds, t, cx);
+    // A WGRAD tile's cost grows with its segment's row count.  Deal the segments longest
+    // first and the rounds of tiles back and forth (snake), so the workgroups that drew long
+    // tiles in one round draw short ones in the next; each XCD still takes 32 neighbouring
+    // tiles per round.
+    __shared__ int sOrd[kMaxG];
+    order_by_length<W>(sCu, sStart, G, n_rt_total, sOrd, (int *)lds);
+    const int lb = logical_block(), grid = gridDim.x;
+    long long base = 0;
+    for (int r = 0; base < total; ++r, base += grid) {
+      const long long t = base + ((r & 1) ? grid - 1 - lb : lb);
+      if (t < total)
+        wgrad_tile<W>(a, b, (float *)out, G, Kd, N, n_it, n_ct, sCu, sStart, sOrd, lds, t, cx);
+    }
   } else {
     constexpr int bk = kStageK<OP>;
     const int nk = ((OP == MOE_GEMM_DGRAD ? N : Kd) + bk - 1) / bk;

@@ -501,6 +501,27 @@ def test_group_gemm_swiglu_split_round():
     within_one_bf16_ulp(bits(z)[rows], z_ref[rows], what="split swiglu z on ternary inputs")
 
 
+def test_group_gemm_wgrad_unequal_segments():
+    """WGRAD tiles are dealt longest segment first, rounds alternating direction: segments of
+    many different lengths (repeated lengths, empty segments, one long one), about 2.6 rounds
+    of tiles on 256 CUs, ternary inputs, bit for bit against the oracle."""
+    G, Kd, N = 60, 768, 1024
+    rng = np.random.default_rng(60)
+    lens = rng.integers(1, 90, size=G)
+    lens[[3, 17, 40]] = 0                    # empty segments
+    lens[[5, 6, 30]] = 57                    # equal lengths
+    lens[10] = 700                           # one long segment
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    M = int(cu[-1]) + 5                      # a few rows outside every segment
+    a, b = _gemm_inputs("wgrad", G, M, Kd, N, "bf16",
+                        lambda t, s: synth.host_ternary(61, t, s))
+    init = synth.host_ternary(62, 9, (G, Kd, N))
+    log(f"gemm wgrad unequal segments G={G} M={M}")
+    got = _run_gemm("wgrad", a, b, cu, Kd, N, "bf16", init)
+    ref = oracle.group_gemm("wgrad", a, b, cu, "bf16", out=init)
+    assert (got == ref).all()
+
+
 @pytest.mark.parametrize("op", ["fwd", "dgrad", "wgrad"])
 def test_group_gemm_f32(op):
     G, M, Kd, N = 18, 256, 256, 512
