@@ -17,7 +17,16 @@ namespace moe {
 
 constexpr int kRowThreads = 256;      // combine / fold / prefetch blocks
 constexpr int kPermMaxThreads = 1024; // permute: one block spans a whole row
-constexpr int kCombU = 4;             // vectors per thread per combine block
+// Combine / un-permute reduce blocks: kCombU vectors per thread, the block sized to the row
+// (whole wavefronts, at most kCombMaxThreads), so a 14 KB bf16 row of 896 vectors is 448
+// threads with no idle lane; 4 vectors on 256 threads (the last pass half idle) measured
+// 3-4% slower, one vector per thread on 896 threads 8% slower.
+constexpr int kCombU = 2;
+constexpr int kCombMaxThreads = 1024;
+inline int comb_threads(int vec) {
+  const int t = (vec + kCombU - 1) / kCombU;
+  return t >= kCombMaxThreads ? kCombMaxThreads : (t + 63) / 64 * 64;
+}
 constexpr int kStreamU = 4;           // vectors per thread per fold / prefetch block
 constexpr int kMaxGridX = 1 << 20;
 constexpr int kMaxGridY = 65535;
@@ -104,16 +113,16 @@ __device__ inline u32x4 round_row16(const float (&acc)[8]) {
 }
 
 // out[s] = sum_k w[c] * y_all[dest_pos[c]], c = (rank*S + s)*K + k.  grid (tokens, chunks);
-// a block covers kRowThreads*kCombU vectors of one token, all K source rows in flight.
+// a block covers blockDim.x*kCombU vectors of one token, all K source rows in flight.
 // Without WEIGHTED every weight is 1 (the un-permute reduce of the dispatch's backward): the
 // fused multiply-add by 1 rounds exactly like a plain add.
 template <bool BF16, bool WEIGHTED = true>
-__global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict__ y_all,
+__global__ __launch_bounds__(kCombMaxThreads) void k_combine(const u32x4 *__restrict__ y_all,
                                                         const int32_t *__restrict__ dest_pos,
                                                         const float *__restrict__ topk_w,
                                                         u32x4 *__restrict__ out, int S, int K,
                                                         int rank, int vec_per_row) {
-  constexpr int kChunk = kRowThreads * kCombU;
+  const int T = blockDim.x, kChunk = T * kCombU;
   for (int s = blockIdx.x; s < S; s += gridDim.x) {
     const size_t c0 = ((size_t)rank * S + s) * K;
     int dst[kMaxKUnrolled];
@@ -127,7 +136,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict
     for (int base = blockIdx.y * kChunk; base < vec_per_row; base += gridDim.y * kChunk) {
 #pragma unroll
       for (int u = 0; u < kCombU; ++u) {
-        const int v = base + u * kRowThreads + threadIdx.x;
+        const int v = base + u * T + threadIdx.x;
         if (v >= vec_per_row) break;
         u32x4 t[kMaxKUnrolled];
 #pragma unroll
@@ -145,18 +154,18 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(const u32x4 *__restrict
 
 // Generic-K combine for K > kMaxKUnrolled: same arithmetic and order, one k at a time.
 template <bool BF16, bool WEIGHTED = true>
-__global__ __launch_bounds__(kRowThreads) void k_combine_anyk(const u32x4 *__restrict__ y_all,
+__global__ __launch_bounds__(kCombMaxThreads) void k_combine_anyk(const u32x4 *__restrict__ y_all,
                                                              const int32_t *__restrict__ dest_pos,
                                                              const float *__restrict__ topk_w,
                                                              u32x4 *__restrict__ out, int S,
                                                              int K, int rank, int vec_per_row) {
-  constexpr int kChunk = kRowThreads * kCombU;
+  const int T = blockDim.x, kChunk = T * kCombU;
   for (int s = blockIdx.x; s < S; s += gridDim.x) {
     const size_t c0 = ((size_t)rank * S + s) * K;
     u32x4 *o = out + (size_t)s * vec_per_row;
     for (int base = blockIdx.y * kChunk; base < vec_per_row; base += gridDim.y * kChunk) {
       for (int u = 0; u < kCombU; ++u) {
-        const int v = base + u * kRowThreads + threadIdx.x;
+        const int v = base + u * T + threadIdx.x;
         if (v >= vec_per_row) break;
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int k = 0; k < K; ++k) {
@@ -396,25 +405,26 @@ extern "C" moe_status_t moe_combine(const moe_dims *d, moe_dtype dtype, int64_t 
   const int eb = elem_bytes(dtype);
   if (!eb || width <= 0 || (width * eb) % 16 != 0 || width * eb / 16 > INT32_MAX) return MOE_EINVAL;
   const int vec = (int)(width * eb / 16);
+  const int threads = comb_threads(vec);
   const dim3 grid(clamp_grid(d->S, kMaxGridX),
-                  clamp_grid(ceil_div(vec, kRowThreads * kCombU), kMaxGridY));
+                  clamp_grid(ceil_div(vec, threads * kCombU), kMaxGridY));
   const bool bf = dtype == MOE_BF16;
   if (d->K <= kMaxKUnrolled) {
     if (bf)
-      hipLaunchKernelGGL(k_combine<true>, grid, dim3(kRowThreads), 0, stream,
+      hipLaunchKernelGGL(k_combine<true>, grid, dim3(threads), 0, stream,
                          (const u32x4 *)y_all, dest_pos, topk_w, (u32x4 *)out, d->S, d->K, rank,
                          vec);
     else
-      hipLaunchKernelGGL(k_combine<false>, grid, dim3(kRowThreads), 0, stream,
+      hipLaunchKernelGGL(k_combine<false>, grid, dim3(threads), 0, stream,
                          (const u32x4 *)y_all, dest_pos, topk_w, (u32x4 *)out, d->S, d->K, rank,
                          vec);
   } else {
     if (bf)
-      hipLaunchKernelGGL(k_combine_anyk<true>, grid, dim3(kRowThreads), 0, stream,
+      hipLaunchKernelGGL(k_combine_anyk<true>, grid, dim3(threads), 0, stream,
                          (const u32x4 *)y_all, dest_pos, topk_w, (u32x4 *)out, d->S, d->K, rank,
                          vec);
     else
-      hipLaunchKernelGGL(k_combine_anyk<false>, grid, dim3(kRowThreads), 0, stream,
+      hipLaunchKernelGGL(k_combine_anyk<false>, grid, dim3(threads), 0, stream,
                          (const u32x4 *)y_all, dest_pos, topk_w, (u32x4 *)out, d->S, d->K, rank,
                          vec);
   }
@@ -430,23 +440,24 @@ extern "C" moe_status_t moe_unpermute_reduce(const moe_dims *d, moe_dtype dtype,
   const int eb = elem_bytes(dtype);
   if (!eb || width <= 0 || (width * eb) % 16 != 0 || width * eb / 16 > INT32_MAX) return MOE_EINVAL;
   const int vec = (int)(width * eb / 16);
+  const int threads = comb_threads(vec);
   const dim3 grid(clamp_grid(d->S, kMaxGridX),
-                  clamp_grid(ceil_div(vec, kRowThreads * kCombU), kMaxGridY));
+                  clamp_grid(ceil_div(vec, threads * kCombU), kMaxGridY));
   const bool bf = dtype == MOE_BF16;
   const u32x4 *src = (const u32x4 *)dxp_all;
   if (d->K <= kMaxKUnrolled) {
     if (bf)
-      hipLaunchKernelGGL((k_combine<true, false>), grid, dim3(kRowThreads), 0, stream, src,
+      hipLaunchKernelGGL((k_combine<true, false>), grid, dim3(threads), 0, stream, src,
                          dest_pos, nullptr, (u32x4 *)dx, d->S, d->K, rank, vec);
     else
-      hipLaunchKernelGGL((k_combine<false, false>), grid, dim3(kRowThreads), 0, stream, src,
+      hipLaunchKernelGGL((k_combine<false, false>), grid, dim3(threads), 0, stream, src,
                          dest_pos, nullptr, (u32x4 *)dx, d->S, d->K, rank, vec);
   } else {
     if (bf)
-      hipLaunchKernelGGL((k_combine_anyk<true, false>), grid, dim3(kRowThreads), 0, stream, src,
+      hipLaunchKernelGGL((k_combine_anyk<true, false>), grid, dim3(threads), 0, stream, src,
                          dest_pos, nullptr, (u32x4 *)dx, d->S, d->K, rank, vec);
     else
-      hipLaunchKernelGGL((k_combine_anyk<false, false>), grid, dim3(kRowThreads), 0, stream, src,
+      hipLaunchKernelGGL((k_combine_anyk<false, false>), grid, dim3(threads), 0, stream, src,
                          dest_pos, nullptr, (u32x4 *)dx, d->S, d->K, rank, vec);
   }
   return launch_status();
