@@ -255,6 +255,32 @@ def test_unpermute_reduce(dtype, K):
         check_close(bits(dx), ref, dtype, what=f"unpermute reduce K={K} rank={rank}")
 
 
+@pytest.mark.parametrize("dtype,W", [("bf16", 16400), ("f32", 8216)])
+def test_combine_and_unpermute_wide_rows(dtype, W):
+    """Rows wider than one block takes (2050 and 2054 vectors of 16 bytes: a second block per
+    row covers the last few vectors), K = 3, both weighted and unweighted forms."""
+    R, S, K, E, B = 2, 24, 3, 8, 1
+    idx, pl = _plan_for(R, S, K, E, B, 31)
+    m = mod()
+    d = m.dims(R, S, K, E, B)
+    _, dest, _ = oracle.layout(idx, pl, 0)
+    dest = dest.copy()
+    dest[4::13] = -1
+    w = np.random.default_rng(2).random(R * S * K).astype(np.float32)
+    y = synth.host_normal(13, 2, (R * S * K, W))
+    y = synth.to_bf16_bits(y) if dtype == "bf16" else y
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for rank in (0, R - 1):
+        out = poisoned((S, W), tdt)
+        m.moe_combine(d, rank, from_bits(y), _dev(dest), _dev(w), out)
+        check_close(bits(out), oracle.combine(y, dest, w, rank, S, K, dtype), dtype,
+                    what=f"wide combine rank={rank}")
+        dx = poisoned((S, W), tdt)
+        m.moe_unpermute_reduce(d, rank, from_bits(y), _dev(dest), dx)
+        check_close(bits(dx), oracle.unpermute_reduce(y, dest, rank, S, K, dtype), dtype,
+                    what=f"wide unpermute reduce rank={rank}")
+
+
 def test_unpermute_reduce_integer_exact():
     R, S, K, E, B, W = 4, 128, 8, 32, 4, 520
     idx, pl = _plan_for(R, S, K, E, B, 22)
