@@ -23,8 +23,12 @@
 
 namespace moe {
 
-constexpr int kLayChunk = 4096;
-constexpr int kLayThreads = 256;
+// Chunk of one rank's copies per block, and block size.  In k_lay_scatter each wave walks
+// kLayChunk / kLayWaves copies one wavefront at a time (a dependent chain of ballots and LDS
+// counter updates), so that length sets its latency: 2048 copies on 8 waves (256 per wave)
+// measured 28 us for the whole layout at R32 S4096 K8, against 52 us for 4096 on 4 waves.
+constexpr int kLayChunk = 2048;
+constexpr int kLayThreads = 512;
 constexpr int kLayWaves = kLayThreads / kWave;
 constexpr int kLayMaxE = 1024;
 constexpr int kLayMaxL = 1024 + 512;
