@@ -73,6 +73,10 @@ CASES = [
     (64, 130, 8, 384, 8, 0.3),
     (5, 999, 3, 20, 0, 0.5),         # B = 0
     (512, 16, 2, 1024, 4, 0.5),      # maximum R and E
+    (4, 1, 1, 4, 1, 0.5),            # one token per rank, K = 1, one expert per rank
+    (6, 33, 1, 6, 3, 5.0),           # K = 1, one expert per rank, near-uniform routing
+    (3, 40, 6, 6, 2, 0.5),           # K = E: every token on every expert, exactly balanced
+    (2, 2049, 2, 4, 1, 0.4),         # S*K = 4098: two full layout chunks and a 2-copy tail
 ]
 
 
