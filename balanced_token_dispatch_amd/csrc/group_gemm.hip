@@ -651,12 +651,15 @@ __device__ inline void epilogue_swiglu(uint16_t *lds, const f32x16 (&acc)[W::TM]
   __syncthreads();
 }
 
-// WGRAD epilogue of a tile inside the output (every element in range): fp32 out += acc, staged
-// through LDS (free once the K loop has drained) so that global memory sees whole rows.  Two
-// passes; in pass p every wave writes its row blocks tm = 2p, 2p+1 into LDS (tile rows
+// WGRAD epilogue: fp32 out += acc for the `rows` x `cols` part of the tile inside the output,
+// staged through LDS (free once the K loop has drained) so that global memory sees whole rows.
+// Two passes; in pass p every wave writes its row blocks tm = 2p, 2p+1 into LDS (tile rows
 // 64p .. 64p+63 and 128+64p .. 128+64p+63: 128 rows x 1 KB) and issues its loads of the old
-// values, then after a barrier every thread adds and stores 16 chunks of 16 bytes, a wave
-// instruction covering one whole 1-KB row.  Compared with read-modify-writes straight from
+// values, then after a barrier every thread adds and stores its 16-byte chunks, a wave
+// instruction covering one whole 1-KB row.  Rows past the edge lie beyond the buffer
+// resource and chunks past the last column take an offset beyond it, so their loads return
+// zero and their stores are dropped (a tile cut by the edge needs no separate code path:
+// the per-element register form it replaced also cost the kernel ~30 registers and 1-2%).  Compared with read-modify-writes straight from
 // the accumulator layout (32 bytes of each of 32 rows per instruction) this sends 8x fewer
 // requests to L2 for the same bytes; the old values are read and written non-temporally
 // (each is touched once per call).  LDS rows are padded to kRmwLd floats, which spreads the
@@ -666,16 +669,20 @@ constexpr int kRmwLdsElems = 2 * 128 * kRmwLd;  // bf16 elements of the staging 
 constexpr int kNonTemporal = 2;                 // cache-policy bit of buffer loads and stores
 
 template <class W>
-__device__ inline void wgrad_rmw_full(float *o, int N, const f32x16 (&acc)[W::TM][W::TN],
-                                      uint16_t *lds_raw, int wi, int wj, int lane) {
+__device__ inline void wgrad_rmw_full(float *o, int N, int rows, int cols,
+                                      const f32x16 (&acc)[W::TM][W::TN], uint16_t *lds_raw,
+                                      int wi, int wj, int lane) {
   constexpr int TN = W::TN;
-  static_assert(W::threads == 512 && W::TM == 4, "8 waves of 128-row blocks");
+  static_assert(W::TM == 4, "128-row wave blocks");
+  constexpr int RS = W::threads / 64;   // staged rows per pass of all threads
+  constexpr int Q = 128 / RS;           // staged rows per thread
   float *L = (float *)lds_raw;  // 128 rows x kRmwLd floats
-  const int c = threadIdx.x & 63, r0 = threadIdx.x >> 6;  // chunk, first staged row (+8 q)
+  const int c = threadIdx.x & 63, r0 = threadIdx.x >> 6;  // chunk, first staged row (+RS q)
   // one resource over the tile's 256 rows; per-lane offset of (row r0, chunk c), the row of
   // each load and store in the (wave-uniform) scalar offset
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(o, (long long)BM * N * 4);
-  const int voff = (r0 * N + c * 4) * 4;
+  // rows >= `rows` lie past the resource; chunks at columns >= `cols` take an offset past it
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(o, ((long long)rows * N - (N - cols)) * 4);
+  const int voff = c * 4 < cols ? (r0 * N + c * 4) * 4 : kOOB;
   float *wr = L + ((wi >> 1) + (lane & 31)) * kRmwLd + wj + (lane >> 5) * 4;
   const float *rd = L + r0 * kRmwLd + c * 4;
 #pragma unroll
@@ -691,23 +698,32 @@ __device__ inline void wgrad_rmw_full(float *o, int N, const f32x16 (&acc)[W::TM
           *(f32x4 *)(wr + b * 32 * kRmwLd + tn * 32 + g * 8) = v;
         }
     // staged row r0 + 8q is tile row 64p + r0 + 8q (q < 8) or 128 + 64p + r0 + 8(q - 8)
-    u32x4 old[16];
+    constexpr int QB = Q < 16 ? Q : 16;  // old values held per batch
+    u32x4 old[QB];
+    auto soff = [&](int q) { return ((q < Q / 2 ? 64 * p : 64 + 64 * p) + RS * q) * N * 4; };
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      old[q] = __builtin_amdgcn_raw_buffer_load_b128(
-          rs, voff, ((q < 8 ? 64 * p : 64 + 64 * p) + 8 * q) * N * 4, kNonTemporal);
+    for (int q = 0; q < QB; ++q)
+      old[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff(q), kNonTemporal);
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const f32x4 a = *(const f32x4 *)(rd + 8 * q * kRmwLd);
-      f32x4 v = __builtin_bit_cast(f32x4, old[q]);
-      v[0] += a[0];
-      v[1] += a[1];
-      v[2] += a[2];
-      v[3] += a[3];
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff,
-                                             ((q < 8 ? 64 * p : 64 + 64 * p) + 8 * q) * N * 4,
-                                             kNonTemporal);
+    for (int b = 0; b < Q / QB; ++b) {
+      if (b > 0) {
+#pragma unroll
+        for (int q = 0; q < QB; ++q)
+          old[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff(b * QB + q),
+                                                         kNonTemporal);
+      }
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        const f32x4 a = *(const f32x4 *)(rd + RS * (b * QB + q) * kRmwLd);
+        f32x4 v = __builtin_bit_cast(f32x4, old[q]);
+        v[0] += a[0];
+        v[1] += a[1];
+        v[2] += a[2];
+        v[3] += a[3];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff,
+                                               soff(b * QB + q), kNonTemporal);
+      }
     }
     __syncthreads();
   }
@@ -920,36 +936,7 @@ __device__ inline void wgrad_tile(const uint16_t *__restrict__ a, const uint16_t
   ta.nk = (len + BK - 1) / BK;
   tile_mma<W, false, false, false>(lds, ta, acc);
   float *o = out + ((size_t)rho * Kd + i0) * N + j0;
-  if (i0 + BM <= Kd && j0 + BN <= N) {
-    wgrad_rmw_full<W>(o, N, acc, lds, cx.wi, cx.wj, cx.lane);
-    return;
-  }
-  // a tile cut by the edge of the output: fp32 += straight from registers, one row block at
-  // a time (column and row tests per 16-byte element)
-  const int lane = cx.lane;
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const int i = cx.wi + tm * 32 + (lane & 31);
-    if (i0 + i >= Kd) continue;
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j = cx.wj + tn * 32 + g * 8 + (lane >> 5) * 4;
-        if (j0 + j < N) {
-          const f32x16 &c = acc[tm][tn];
-          f32x4 *p = (f32x4 *)(o + (size_t)i * N + j);
-          f32x4 v = *p;
-          v[0] += c[4 * g + 0];
-          v[1] += c[4 * g + 1];
-          v[2] += c[4 * g + 2];
-          v[3] += c[4 * g + 3];
-          *p = v;
-        }
-      }
-    // at most one row block of read-modify-writes in flight (bounds live registers)
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  wgrad_rmw_full<W>(o, N, Kd - i0, N - j0, acc, lds, cx.wi, cx.wj, cx.lane);
 }
 
 // LDS of the tile loops: the K loop's ring; the WGRAD epilogue stages through a slightly
@@ -1174,6 +1161,9 @@ extern "C" moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t 
   if (op != MOE_GEMM_FWD && op != MOE_GEMM_DGRAD && op != MOE_GEMM_WGRAD) return MOE_EINVAL;
   if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_EINVAL;
   if ((long long)M_total * (Kd > N ? Kd : N) >= (1LL << 40)) return MOE_EINVAL;
+  // WGRAD's epilogue addresses a tile's fp32 rows with 32-bit buffer offsets (row * N * 4
+  // plus an out-of-range marker for masked chunks), which must not wrap
+  if (op == MOE_GEMM_WGRAD && N > (1 << 20)) return MOE_EINVAL;
   if (ws && ws_bytes < moe_group_gemm_workspace_bytes(op, dtype)) return MOE_ENOSPACE;
   if (M_total == 0) return MOE_OK;
   if (dtype == MOE_F32) {

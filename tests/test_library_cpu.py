@@ -83,6 +83,9 @@ def test_host_validation_rejects_before_launch(mod):
     assert gg(mod.GEMM_FWD, mod.BF16, 0, 256, 16, 16, P, P, P, P, None, 0, None) == mod.MOE_EINVAL
     assert gg(5, mod.BF16, 18, 256, 16, 16, P, P, P, P, None, 0, None) == mod.MOE_EINVAL
     assert gg(mod.GEMM_FWD, mod.BF16, 18, 256, 16, 16, None, P, P, P, None, 0, None) == mod.MOE_EINVAL
+    # WGRAD rows are addressed with 32-bit offsets: N above 2^20 is refused
+    assert gg(mod.GEMM_WGRAD, mod.BF16, 2, 256, 16, (1 << 20) + 8, P, P, P, P, None, 0,
+              None) == mod.MOE_EINVAL
     need = mod.group_gemm_workspace_bytes(mod.GEMM_FWD)
     assert need > 0 and mod.group_gemm_workspace_bytes(mod.GEMM_WGRAD) == 0
     assert mod.group_gemm_workspace_bytes(mod.GEMM_FWD, mod.F32) == 0
