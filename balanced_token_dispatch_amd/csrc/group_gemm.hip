@@ -25,7 +25,7 @@
 //   * the MFMA is issued as (column-side x row-side) so each lane ends with
 //     4 consecutive output columns; output tiles leave through LDS so that
 //     global memory sees whole rows (bf16 stores; WGRAD's fp32
-//     read-modify-write, see wgrad_rmw_full);
+//     read-modify-write, see wgrad_rmw);
 //   * blockIdx is remapped so the 32 workgroups of one XCD work on
 //     neighbouring tiles (shared weight and activation panels in that XCD's
 //     L2); tiles are walked in groups of 8 row-tiles;
@@ -656,31 +656,34 @@ __device__ inline void epilogue_swiglu(uint16_t *lds, const f32x16 (&acc)[W::TM]
 // Two passes; in pass p every wave writes its row blocks tm = 2p, 2p+1 into LDS (tile rows
 // 64p .. 64p+63 and 128+64p .. 128+64p+63: 128 rows x 1 KB) and issues its loads of the old
 // values, then after a barrier every thread adds and stores its 16-byte chunks, a wave
-// instruction covering one whole 1-KB row.  Rows past the edge lie beyond the buffer
-// resource and chunks past the last column take an offset beyond it, so their loads return
-// zero and their stores are dropped (a tile cut by the edge needs no separate code path:
-// the per-element register form it replaced also cost the kernel ~30 registers and 1-2%).  Compared with read-modify-writes straight from
-// the accumulator layout (32 bytes of each of 32 rows per instruction) this sends 8x fewer
-// requests to L2 for the same bytes; the old values are read and written non-temporally
-// (each is touched once per call).  LDS rows are padded to kRmwLd floats, which spreads the
-// 32 rows a wave writes per instruction over all banks.
+// instruction covering one whole 1-KB row.  A chunk outside the output (a row at or past
+// `rows`, or columns at or past `cols`) takes a per-lane offset past the buffer resource, so
+// its load returns zero and its store is dropped: a tile cut by the edge needs no separate
+// code path (the per-element register form it replaced also cost the kernel ~30 registers
+// and 1-2%).  Compared with read-modify-writes straight from the accumulator layout (32 bytes
+// of each of 32 rows per instruction) this sends 8x fewer requests to L2 for the same bytes;
+// the old values are read and written non-temporally (each is touched once per call).  LDS
+// rows are padded to kRmwLd floats, which spreads the 32 rows a wave writes per instruction
+// over all banks.
 constexpr int kRmwLd = 260;
 constexpr int kRmwLdsElems = 2 * 128 * kRmwLd;  // bf16 elements of the staging area
 constexpr int kNonTemporal = 2;                 // cache-policy bit of buffer loads and stores
 
 template <class W>
-__device__ inline void wgrad_rmw_full(float *o, int N, int rows, int cols,
-                                      const f32x16 (&acc)[W::TM][W::TN], uint16_t *lds_raw,
-                                      int wi, int wj, int lane) {
+__device__ inline void wgrad_rmw(float *o, int N, int rows, int cols,
+                                 const f32x16 (&acc)[W::TM][W::TN], uint16_t *lds_raw, int wi,
+                                 int wj, int lane) {
   constexpr int TN = W::TN;
   static_assert(W::TM == 4, "128-row wave blocks");
-  constexpr int RS = W::threads / 64;   // staged rows per pass of all threads
-  constexpr int Q = 128 / RS;           // staged rows per thread
+  constexpr int RS = W::threads / 64;   // staged rows per pass of all threads (one per wave)
+  constexpr int Q = 128 / RS;           // staged rows per thread and pass
   float *L = (float *)lds_raw;  // 128 rows x kRmwLd floats
   const int c = threadIdx.x & 63, r0 = threadIdx.x >> 6;  // chunk, first staged row (+RS q)
-  // one resource over the tile's 256 rows; per-lane offset of (row r0, chunk c), the row of
-  // each load and store in the (wave-uniform) scalar offset
-  // rows >= `rows` lie past the resource; chunks at columns >= `cols` take an offset past it
+  // One resource over the tile's rows; the row of each load and store goes in the
+  // (wave-uniform) scalar offset, the chunk's column in the per-lane offset.  Chunks outside
+  // the output get the per-lane offset kOOB, which is past the resource whether or not the
+  // hardware's range check counts the scalar offset (kOOB + any row offset of a tile stays
+  // below 2^32: rows < 256 and N <= 2^20).
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(o, ((long long)rows * N - (N - cols)) * 4);
   const int voff = c * 4 < cols ? (r0 * N + c * 4) * 4 : kOOB;
   float *wr = L + ((wi >> 1) + (lane & 31)) * kRmwLd + wj + (lane >> 5) * 4;
@@ -697,20 +700,23 @@ __device__ inline void wgrad_rmw_full(float *o, int N, int rows, int cols,
           const f32x4 v = {a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
           *(f32x4 *)(wr + b * 32 * kRmwLd + tn * 32 + g * 8) = v;
         }
-    // staged row r0 + 8q is tile row 64p + r0 + 8q (q < 8) or 128 + 64p + r0 + 8(q - 8)
+    // staged row r0 + RS q (q < Q) holds tile row r0 + trow(q): the first Q/2 staged rows are
+    // tile rows 64p .., the last Q/2 are tile rows 128 + 64p ..
     constexpr int QB = Q < 16 ? Q : 16;  // old values held per batch
     u32x4 old[QB];
-    auto soff = [&](int q) { return ((q < Q / 2 ? 64 * p : 64 + 64 * p) + RS * q) * N * 4; };
+    auto trow = [&](int q) { return (q < Q / 2 ? 64 * p : 64 + 64 * p) + RS * q; };
+    auto soff = [&](int q) { return trow(q) * N * 4; };
+    auto vof = [&](int q) { return r0 + trow(q) < rows ? voff : kOOB; };
 #pragma unroll
     for (int q = 0; q < QB; ++q)
-      old[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff(q), kNonTemporal);
+      old[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, vof(q), soff(q), kNonTemporal);
     __syncthreads();
 #pragma unroll
     for (int b = 0; b < Q / QB; ++b) {
       if (b > 0) {
 #pragma unroll
         for (int q = 0; q < QB; ++q)
-          old[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff(b * QB + q),
+          old[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, vof(b * QB + q), soff(b * QB + q),
                                                          kNonTemporal);
       }
 #pragma unroll
@@ -721,8 +727,8 @@ __device__ inline void wgrad_rmw_full(float *o, int N, int rows, int cols,
         v[1] += a[1];
         v[2] += a[2];
         v[3] += a[3];
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff,
-                                               soff(b * QB + q), kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
+                                               vof(b * QB + q), soff(b * QB + q), kNonTemporal);
       }
     }
     __syncthreads();
@@ -936,7 +942,7 @@ __device__ inline void wgrad_tile(const uint16_t *__restrict__ a, const uint16_t
   ta.nk = (len + BK - 1) / BK;
   tile_mma<W, false, false, false>(lds, ta, acc);
   float *o = out + ((size_t)rho * Kd + i0) * N + j0;
-  wgrad_rmw_full<W>(o, N, Kd - i0, N - j0, acc, lds, cx.wi, cx.wj, cx.lane);
+  wgrad_rmw<W>(o, N, Kd - i0, N - j0, acc, lds, cx.wi, cx.wj, cx.lane);
 }
 
 // LDS of the tile loops: the K loop's ring; the WGRAD epilogue stages through a slightly

@@ -51,8 +51,8 @@ __global__ __launch_bounds__(kLayThreads) void k_lay_hist(const int32_t *__restr
   for (int e = threadIdx.x; e < E; e += blockDim.x) part[(size_t)e * npc + col] = hist[e];
 }
 
-// Exclusive scan of one int per thread over a 256-thread block.
-__device__ int block256_scan_excl(int v, int *tmp /* >= 4 */, int *total) {
+// Exclusive scan of one int per thread over a kLayThreads-thread block (kLayWaves waves).
+__device__ int lay_block_scan_excl(int v, int *tmp /* >= kLayWaves */, int *total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kLayThreads) void k_lay_scan(
       const int i = base + tid;
       const int v = i < npc ? row[i] : 0;
       int total;
-      const int ex = block256_scan_excl(v, tmp, &total);
+      const int ex = lay_block_scan_excl(v, tmp, &total);
       if (i < npc) row[i] = carry + ex;
       carry += total;
     }
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kLayThreads) void k_lay_scan(
     else if (rho < G)
       n = plan[L.off_scount + rank * B + (rho - E)];
     int total;
-    const int ex = block256_scan_excl(n, tmp, &total);
+    const int ex = lay_block_scan_excl(n, tmp, &total);
     const int carry = carry_s;
     if (rho < G) cu_out[rho] = carry + ex;
     __syncthreads();
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kLayThreads) void k_lay_scatter(
   }
   __syncthreads();
 
-  // each wave owns a contiguous quarter of the chunk
+  // each of the kLayWaves waves owns a contiguous 1/kLayWaves of the chunk
   const int per_wave = kLayChunk / kLayWaves;
   const int w0 = wid * per_wave;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));

@@ -50,7 +50,19 @@ def compact_cu(seg, G):
 
 
 WORKLOADS = [("balanced_bf16", None), ("skew1_large", 1.0), ("skew8_large_fwdbwd", 8.0),
-             ("sweep_r64", 16.0), ("sweep_r64", 0.0)]
+             ("sweep_r64", 16.0), ("sweep_r64", 4.0), ("sweep_r64", 1.0), ("sweep_r64", 0.0)]
+
+
+def seg_weight_cols(W, rho, cols):
+    """[1, rows, len(cols)]: columns `cols` of weight row rho (a FWD over them gives exactly
+    those output columns: every output element is its own float64 dot product)."""
+    return W[rho][:, np.asarray(cols)][None]
+
+
+def seg_weight_rows(W, rho, rows):
+    """[1, len(rows), cols]: rows `rows` of weight row rho (a DGRAD over them gives exactly
+    those output columns)."""
+    return W[rho][np.asarray(rows)][None]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -123,7 +135,7 @@ def test_full_size_step(name, target):
     rows = []
     for rho in pick:
         lo, hi = int(cu[rho]), int(cu[rho + 1])
-        rows += [lo, hi - 1] + rng.integers(lo, hi, size=4).tolist()
+        rows += [lo, hi - 1] + rng.integers(lo, hi, size=10).tolist()
     rows = np.array(sorted(set(rows)), np.int64)
     seg = np.searchsorted(cu, rows, side="right") - 1
     cu_c = compact_cu(seg, G)
@@ -148,7 +160,7 @@ def test_full_size_step(name, target):
         mine = ds[(ds >= rank * SK) & (ds < (rank + 1) * SK)] - rank * SK
         if np.isin(np.searchsorted(cu, mine, side="right") - 1, pick).all():
             tok_s.append(int(s_))
-        if len(tok_s) == 6:
+        if len(tok_s) == 12:
             break
     if len(tok_s) < 2:
         tok_s = sorted(set(tok_s) | {0, S - 1})
@@ -189,34 +201,36 @@ def test_full_size_step(name, target):
     check_close(host_rows(L.dz, rows), dz_ref, "bf16", what="down dgrad rows")
     _, dxp_ref = oracle.group_gemm_rows("dgrad", dz_ref, Wu, cu_c, np.arange(rows.size))
     check_close(host_rows(L.dxp, rows), dxp_ref, "bf16", what="up dgrad rows")
-    # wgrad entries of the smallest sampled segment: the oracle recomputes the whole segment
+    # wgrad entries of the smallest sampled segment, at any segment length: an entry
+    # dW_down[i, j] = sum_m z[m, i] dy[m, j] needs column i of z (x @ W_up[:, i]) and column j
+    # of dy over the segment's rows; dW_up[i, j] = sum_m x[m, i] dz[m, j] needs column j of dz
+    # (dy @ W_down[j, :]^T).  The oracle recomputes only those columns.
     rho = min(pick, key=lambda r_: cu[r_ + 1] - cu[r_])
     lo, hi = int(cu[rho]), int(cu[rho + 1])
-    if hi - lo <= 4096:
-        seg_rows = np.arange(lo, hi)
-        stoks = src[seg_rows] // K
-        xs = host_rows(L.x_all, stoks)
-        cu1 = np.array([0] * (rho + 1) + [hi - lo] * (G - rho), np.int64)
-        _, zs = oracle.group_gemm_rows("fwd", xs, Wu, cu1, np.arange(hi - lo))
-        gs = host_rows(L.dout_all, stoks)
-        wsc = w_flat[src[seg_rows]]
-        dys = oracle.permute(gs, (np.arange(hi - lo) * K).astype(np.int32), K,
-                             row_scale=np.repeat(wsc, K).astype(np.float32))
-        _, dzs = oracle.group_gemm_rows("dgrad", dys, Wd, cu1, np.arange(hi - lo))
-        ii = rng.integers(0, Hp, 6)
-        jj = rng.integers(0, H, 6)
-        cu2 = np.array([0, hi - lo])
-        ent = oracle.wgrad_entries(zs, dys, cu2, 0, ii, jj, "bf16")
-        got = L.dw_down[rho][torch.as_tensor(ii, device="cuda"),
-                             torch.as_tensor(jj, device="cuda")].cpu().numpy()
-        assert np.abs(got - ent).max() <= 1e-3 * max(1.0, np.abs(ent).max()), (got, ent)
-        ii2 = rng.integers(0, H, 6)
-        jj2 = rng.integers(0, Hp, 6)
-        ent2 = oracle.wgrad_entries(xs, dzs, cu2, 0, ii2, jj2, "bf16")
-        got2 = L.dw_up[rho][torch.as_tensor(ii2, device="cuda"),
-                            torch.as_tensor(jj2, device="cuda")].cpu().numpy()
-        assert np.abs(got2 - ent2).max() <= 1e-3 * max(1.0, np.abs(ent2).max()), (got2, ent2)
-        log(f"  wgrad entries of segment {rho} ({hi - lo} rows) within tolerance")
+    n_seg = hi - lo
+    seg_rows = np.arange(lo, hi)
+    stoks = src[seg_rows] // K
+    xs = host_rows(L.x_all, stoks)
+    gs = host_rows(L.dout_all, stoks)
+    wsc = w_flat[src[seg_rows]]
+    dys = oracle.permute(gs, (np.arange(n_seg) * K).astype(np.int32), K,
+                         row_scale=np.repeat(wsc, K).astype(np.float32))
+    cu2 = np.array([0, n_seg])
+    ii = rng.integers(0, Hp, 8)
+    jj = rng.integers(0, H, 8)
+    z_cols = oracle.group_gemm("fwd", xs, seg_weight_cols(Wu, rho, ii), cu2, "bf16")
+    ent = oracle.wgrad_entries(z_cols, dys, cu2, 0, np.arange(ii.size), jj, "bf16")
+    got = L.dw_down[rho][torch.as_tensor(ii, device="cuda"),
+                         torch.as_tensor(jj, device="cuda")].cpu().numpy()
+    assert np.abs(got - ent).max() <= 1e-3 * max(1.0, np.abs(ent).max()), (got, ent)
+    ii2 = rng.integers(0, H, 8)
+    jj2 = rng.integers(0, Hp, 8)
+    dz_cols = oracle.group_gemm("dgrad", dys, seg_weight_rows(Wd, rho, jj2), cu2, "bf16")
+    ent2 = oracle.wgrad_entries(xs, dz_cols, cu2, 0, ii2, np.arange(jj2.size), "bf16")
+    got2 = L.dw_up[rho][torch.as_tensor(ii2, device="cuda"),
+                        torch.as_tensor(jj2, device="cuda")].cpu().numpy()
+    assert np.abs(got2 - ent2).max() <= 1e-3 * max(1.0, np.abs(ent2).max()), (got2, ent2)
+    log(f"  wgrad entries of segment {rho} ({n_seg} rows) within tolerance")
     # router-weight gradient and un-permute reduce of the sampled tokens, on the rows the
     # GPU produced (rank 0's expert outputs and input gradients, the peers' staged rows)
     moe_combine_weight_grad(L.d, rank, L.y_all, L.dest, L.dout_all[rank * S:(rank + 1) * S],
@@ -326,27 +340,33 @@ def test_full_size_gated_step():
     check_close(host_rows(L.dxp, rows), dxp_ref, "bf16", min_identical=0.95,
                 what="up dgrad rows (gated)")
     log(f"  gated forward/backward rows within tolerance ({rows.size} rows, segments {pick})")
-    # up-WGRAD entries of the smallest sampled home-expert segment (no fold touches it)
+    # up-WGRAD entries of the smallest sampled home-expert segment (no fold touches it), at any
+    # segment length: entry (i, c) of dW_up needs column c of dh, which needs the (gate, up)
+    # pair p = c // 2 of the pre-activation (columns 2p, 2p+1 of x @ W_up) and column p of dz
+    # (dy @ W_down[p, :]^T).  The oracle recomputes only those columns.
     rho = min([r_ for r_ in pick if r_ < E], key=lambda r_: cu[r_ + 1] - cu[r_])
     lo, hi = int(cu[rho]), int(cu[rho + 1])
-    if hi - lo <= 4096:
-        seg_rows = np.arange(lo, hi)
-        stoks = src[seg_rows] // K
-        xs = host_rows(L.x_all, stoks)
-        cu1 = np.array([0] * (rho + 1) + [hi - lo] * (G - rho), np.int64)
-        _, hs = oracle.group_gemm_swiglu(xs, Wu, cu1, "bf16")
-        gs = host_rows(L.dout_all, stoks)
-        dys = oracle.permute(gs, (np.arange(hi - lo) * K).astype(np.int32), K,
-                             row_scale=np.repeat(w.reshape(-1)[src[seg_rows]], K).astype(np.float32))
-        _, dzs = oracle.group_gemm_rows("dgrad", dys, Wd, cu1, np.arange(hi - lo))
-        dhs = oracle.swiglu_backward(dzs, hs, "bf16")
-        ii = rng.integers(0, H, 8)
-        jj = rng.integers(0, 2 * Hp, 8)
-        ent = oracle.wgrad_entries(xs, dhs, np.array([0, hi - lo]), 0, ii, jj, "bf16")
-        got = L.dw_up[rho][torch.as_tensor(ii, device="cuda"),
-                           torch.as_tensor(jj, device="cuda")].cpu().numpy()
-        assert np.abs(got - ent).max() <= 1e-3 * max(1.0, np.abs(ent).max()), (got, ent)
-        log(f"  gated up-WGRAD entries of segment {rho} ({hi - lo} rows) within tolerance")
+    n_seg = hi - lo
+    seg_rows = np.arange(lo, hi)
+    stoks = src[seg_rows] // K
+    xs = host_rows(L.x_all, stoks)
+    gs = host_rows(L.dout_all, stoks)
+    dys = oracle.permute(gs, (np.arange(n_seg) * K).astype(np.int32), K,
+                         row_scale=np.repeat(w.reshape(-1)[src[seg_rows]], K).astype(np.float32))
+    cu2 = np.array([0, n_seg])
+    ii = rng.integers(0, H, 8)
+    jj = rng.integers(0, 2 * Hp, 8)
+    pairs = jj // 2
+    hcols = np.stack([2 * pairs, 2 * pairs + 1], axis=1).reshape(-1)   # gate, up of each pair
+    hs = oracle.group_gemm("fwd", xs, Wu[rho][:, hcols][None], cu2, "bf16")
+    dzs = oracle.group_gemm("dgrad", dys, Wd[rho][pairs][None], cu2, "bf16")
+    dhs = oracle.swiglu_backward(dzs, hs, "bf16")                        # [n, 2 * len(jj)]
+    sel = 2 * np.arange(jj.size) + (jj % 2)                              # column jj of dh
+    ent = oracle.wgrad_entries(xs, dhs, cu2, 0, ii, sel, "bf16")
+    got = L.dw_up[rho][torch.as_tensor(ii, device="cuda"),
+                       torch.as_tensor(jj, device="cuda")].cpu().numpy()
+    assert np.abs(got - ent).max() <= 1e-3 * max(1.0, np.abs(ent).max()), (got, ent)
+    log(f"  gated up-WGRAD entries of segment {rho} ({n_seg} rows) within tolerance")
     del L
     gc.collect()
     torch.cuda.empty_cache()

@@ -552,6 +552,35 @@ def test_group_gemm_wgrad_unequal_segments():
     assert (got == ref).all()
 
 
+@pytest.mark.parametrize("Kd,N", [(1408, 2048), (264, 520), (1408, 136)])
+def test_group_gemm_wgrad_row_edge_guard(Kd, N):
+    """WGRAD tiles cut by the output's row edge (Kd % 256 != 0) write nothing outside their own
+    weight row.  Between two active segments lies an empty one, whose weight row no tile owns,
+    and after the last (active) weight row lies a guard region; both hold -0.0, which any
+    read-add-write of a masked row (its accumulators are +0) would turn into +0.0, and must keep
+    their bits.  The active rows match the oracle bit for bit (ternary inputs)."""
+    m = mod()
+    G = 4
+    cu = np.concatenate([[0], np.cumsum([300, 0, 200, 150])]).astype(np.int32)
+    M = int(cu[-1])
+    a, b = _gemm_inputs("wgrad", G, M, Kd, N, "bf16",
+                        lambda t, s: synth.host_ternary(Kd + N, t, s))
+    init = synth.host_ternary(Kd, 9, (G, Kd, N))
+    init[1] = -0.0
+    n_out, n_guard = G * Kd * N, 256 * N
+    full = torch.empty(n_out + n_guard, dtype=torch.float32, device="cuda")
+    full.view(torch.int32).fill_(-2 ** 31)          # every word -0.0
+    full[:n_out] = _dev(init.reshape(-1))
+    log(f"gemm wgrad row edge Kd={Kd} N={N}")
+    m.moe_group_gemm(m.GEMM_WGRAD, from_bits(a), from_bits(b), _dev(cu),
+                     full[:n_out].view(G, Kd, N), Kd, N)
+    got = full.cpu().numpy().view(np.uint32)
+    ref = oracle.group_gemm("wgrad", a, b, cu, "bf16", out=init)
+    assert (got[:n_out] == ref.reshape(-1).view(np.uint32)).all()
+    assert (got[Kd * N:2 * Kd * N] == 0x80000000).all(), "empty segment's weight row untouched"
+    assert (got[n_out:] == 0x80000000).all(), "guard after the last weight row untouched"
+
+
 @pytest.mark.parametrize("op", ["fwd", "dgrad", "wgrad"])
 def test_group_gemm_f32(op):
     G, M, Kd, N = 18, 256, 256, 512
