@@ -26,7 +26,9 @@ EXPORTS = ("moe_status_string", "moe_plan_words", "moe_plan_workspace_bytes", "m
            "moe_dispatch_layout_workspace_bytes", "moe_dispatch_layout", "moe_prefetch",
            "moe_permute", "moe_group_gemm", "moe_combine", "moe_replica_grad_fold",
            "moe_unpermute_reduce", "moe_combine_weight_grad", "moe_group_gemm_swiglu",
-           "moe_swiglu_backward", "moe_group_gemm_workspace_bytes")
+           "moe_swiglu_backward", "moe_group_gemm_workspace_bytes", "moe_plan_noalloc")
+
+PLAN_NOALLOC_SCRATCH_BYTES = 4 << 20   # MOE_PLAN_NOALLOC_SCRATCH_BYTES in moe.h
 
 
 class MoeDims(ctypes.Structure):
@@ -44,6 +46,7 @@ for _n in ("moe_plan_words", "moe_plan_workspace_bytes", "moe_dispatch_layout_wo
     getattr(_lib, _n).restype = _SZ
     getattr(_lib, _n).argtypes = [_D]
 _lib.moe_plan.argtypes = [_D, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.moe_plan_noalloc.argtypes = [_D, _P, _P, _P, _P, _P]
 _lib.moe_dispatch_layout.argtypes = [_D, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.moe_prefetch.argtypes = [_D, _I32, _P, _P, _I64, _P]
 _lib.moe_permute.argtypes = [_D, ctypes.c_int, _I64, _P, _P, _P, _P, _P]
@@ -115,6 +118,12 @@ def moe_plan(d, topk_idx, counts, plan, dev_status, ws, stream=None):
     _check(_lib.moe_plan(ctypes.byref(d), _ptr(topk_idx), _ptr(counts), _ptr(plan),
                          _ptr(dev_status), _ptr(ws), ws.numel() * ws.element_size(),
                          _stream(stream)), "moe_plan")
+
+
+def moe_plan_noalloc(d, topk_idx, counts, plan, dev_status, stream=None):
+    """moe_plan without a workspace: the library's static per-GPU scratch (see moe.h)."""
+    _check(_lib.moe_plan_noalloc(ctypes.byref(d), _ptr(topk_idx), _ptr(counts), _ptr(plan),
+                                 _ptr(dev_status), _stream(stream)), "moe_plan_noalloc")
 
 
 def moe_dispatch_layout(d, rank, topk_idx, plan, cu_seqlens, dest_pos, src_flat, ws, stream=None):

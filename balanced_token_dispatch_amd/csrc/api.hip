@@ -30,7 +30,7 @@ extern "C" const char *moe_status_string(moe_status_t s) {
   switch (s) {
     case MOE_OK: return "ok";
     case MOE_EINVAL: return "invalid argument (null pointer, shape, dtype or op)";
-    case MOE_ENOSPACE: return "workspace smaller than the size query";
+    case MOE_ENOSPACE: return "workspace smaller than the size query (or, for a no-allocation call, than the call needs of its static scratch)";
     case MOE_EHIP: return "HIP kernel launch failed";
   }
   return "unknown status";

@@ -19,6 +19,8 @@
 //                  need more than B slots, one thread then re-places the
 //                  walk's replicas with the relay fallback (relay_pass) and
 //                  the block regroups the list by expert.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace moe {
@@ -514,11 +516,12 @@ extern "C" size_t moe_plan_workspace_bytes(const moe_dims *d) {
   return (size_t)d->R * nchunk * (d->E + 1) * sizeof(int32_t) + (size_t)d->R * sizeof(int32_t);
 }
 
-extern "C" moe_status_t moe_plan(const moe_dims *d, const int32_t *topk_idx, int32_t *counts,
-                                 int32_t *plan, uint32_t *dev_status, void *ws, size_t ws_bytes,
-                                 hipStream_t stream) {
-  if (!dims_ok(d) || !topk_idx || !counts || !plan || !ws) return MOE_EINVAL;
-  if (ws_bytes < moe_plan_workspace_bytes(d)) return MOE_ENOSPACE;
+// The three launches of a plan, with scratch `ws` of at least moe_plan_workspace_bytes(d)
+// bytes: per-chunk histograms, then the per-rank bad-id counts.  Every scratch word is written
+// before it is read, so the scratch needs no clearing.
+static moe_status_t plan_launch(const moe_dims *d, const int32_t *topk_idx, int32_t *counts,
+                                int32_t *plan, uint32_t *dev_status, void *ws,
+                                hipStream_t stream) {
   const int SK = d->S * d->K;
   const int nchunk = ceil_div(SK, kPlanChunk);
   int32_t *partial = (int32_t *)ws;
@@ -530,4 +533,50 @@ extern "C" moe_status_t moe_plan(const moe_dims *d, const int32_t *topk_idx, int
   hipLaunchKernelGGL(k_plan_solve, dim3(1), dim3(kSolveThreads), 0, stream, counts, bad, plan,
                      dev_status, d->R, d->S, d->K, d->E, d->B);
   return launch_status();
+}
+
+extern "C" moe_status_t moe_plan(const moe_dims *d, const int32_t *topk_idx, int32_t *counts,
+                                 int32_t *plan, uint32_t *dev_status, void *ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  if (!dims_ok(d) || !topk_idx || !counts || !plan || !ws) return MOE_EINVAL;
+  if (ws_bytes < moe_plan_workspace_bytes(d)) return MOE_ENOSPACE;
+  return plan_launch(d, topk_idx, counts, plan, dev_status, ws, stream);
+}
+
+// ---- moe_plan_noalloc: the same plan with its scratch in a static device array ----------
+// For callers that cannot allocate (HIP graph capture, serving loops).  The array is a
+// file-scope __device__ object, so every GPU the library runs on holds its own copy, at its
+// own address, until the process ends.  In host code the array's name is only a host-side
+// stand-in for the symbol: its device address is looked up once per device with
+// hipGetSymbolAddress (on the entry point's first call with that device current) and that
+// address, never the name, is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[MOE_PLAN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void *g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+}  // namespace
+
+// Device address of the current device's copy of `scratch`, or nullptr.
+static void *plan_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void *ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  return g_scratch_ptr[dev];
+}
+
+extern "C" moe_status_t moe_plan_noalloc(const moe_dims *d, const int32_t *topk_idx,
+                                         int32_t *counts, int32_t *plan, uint32_t *dev_status,
+                                         hipStream_t stream) {
+  if (!dims_ok(d) || !topk_idx || !counts || !plan) return MOE_EINVAL;
+  if (moe_plan_workspace_bytes(d) > MOE_PLAN_NOALLOC_SCRATCH_BYTES) return MOE_ENOSPACE;
+  void *ws = plan_scratch();
+  if (!ws) return MOE_EHIP;
+  return plan_launch(d, topk_idx, counts, plan, dev_status, ws, stream);
 }

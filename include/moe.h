@@ -20,9 +20,10 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is DEVICE memory owned by the caller, except
- *     `dims` (host).  The library allocates nothing and keeps no mutable
- *     state; calls only enqueue work on `stream` (0 = the null stream) and
- *     never synchronise with the host.
+ *     `dims` (host).  The library allocates nothing; its only state is a
+ *     per-device cache of device properties and the static per-GPU scratch of
+ *     moe_plan_noalloc.  Calls only enqueue work on `stream` (0 = the null
+ *     stream) and never synchronise with the host.
  *   - Host-side argument checks run before anything is enqueued and return
  *     MOE_EINVAL / MOE_ENOSPACE with nothing launched.  MOE_EHIP reports a
  *     failed kernel launch.  Call moe_status_string() for a message.
@@ -59,7 +60,9 @@ typedef struct {
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = 1,   /* bad pointer, shape, dtype or op                     */
-  MOE_ENOSPACE = 2, /* workspace smaller than the *_workspace_bytes query  */
+  MOE_ENOSPACE = 2, /* workspace smaller than the *_workspace_bytes query, or
+                       a no-allocation call needing more than its static
+                       scratch                                              */
   MOE_EHIP = 3      /* a HIP launch failed                                  */
 } moe_status_t;
 
@@ -129,6 +132,28 @@ size_t moe_plan_workspace_bytes(const moe_dims *dims);
 moe_status_t moe_plan(const moe_dims *dims, const int32_t *topk_idx, int32_t *counts,
                       int32_t *plan, uint32_t *dev_status, void *ws, size_t ws_bytes,
                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_plan_noalloc -- moe_plan with no workspace argument and no allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments (minus ws, ws_bytes), same outputs, bit for bit, as
+ * moe_plan.  The scratch moe_plan takes from `ws` lives instead in one static
+ * device array of MOE_PLAN_NOALLOC_SCRATCH_BYTES per GPU, which the library
+ * holds from its load until the process ends.  Its device address is looked
+ * up once per device, on the first call with that device current (MOE_EHIP if
+ * the lookup fails).  Returns MOE_ENOSPACE, with nothing launched, when
+ * moe_plan_workspace_bytes(dims) exceeds that size (e.g. R=64, S=8192, K=8,
+ * E=384 needs 1.6 MB; R=32, S=4096, K=8, E=256 needs 0.26 MB).  Every scratch
+ * word is written before it is read, so no call needs it cleared.
+ * Calls on one GPU share its one array: calls that can overlap on one GPU
+ * (on different streams, or from several host threads) race and give
+ * unspecified plans; calls on one stream are ordered and do not.
+ * ------------------------------------------------------------------------- */
+#define MOE_PLAN_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status_t moe_plan_noalloc(const moe_dims *dims, const int32_t *topk_idx, int32_t *counts,
+                              int32_t *plan, uint32_t *dev_status, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_dispatch_layout -- turn the plan into rank `rank`'s cu_seqlens and the

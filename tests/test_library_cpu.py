@@ -101,6 +101,26 @@ def test_host_validation_rejects_before_launch(mod):
     assert lib.moe_status_string(mod.MOE_ENOSPACE).startswith(b"workspace")
 
 
+def test_plan_noalloc_host_checks(mod):
+    """moe_plan_noalloc: bad arguments and plans whose scratch exceeds the static array are
+    refused before anything touches the GPU; the binding's size constant is the header's."""
+    text = open(HEADER).read()
+    m = re.search(r"#define MOE_PLAN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == mod.PLAN_NOALLOC_SCRATCH_BYTES
+    lib = mod.library()
+    P = ctypes.c_void_p(16)  # never dereferenced
+    by = ctypes.byref
+    d = mod.dims(4, 128, 2, 16, 2)
+    assert lib.moe_plan_noalloc(by(d), None, P, P, None, None) == mod.MOE_EINVAL
+    assert lib.moe_plan_noalloc(by(d), P, None, P, None, None) == mod.MOE_EINVAL
+    assert lib.moe_plan_noalloc(by(mod.dims(3, 128, 2, 16, 2)), P, P, P, None, None) == mod.MOE_EINVAL
+    for ok in (mod.dims(32, 4096, 8, 256, 8), mod.dims(64, 8192, 8, 384, 8)):
+        assert mod.plan_workspace_bytes(ok) <= mod.PLAN_NOALLOC_SCRATCH_BYTES
+    big = mod.dims(512, 8192, 8, 1024, 8)
+    assert mod.plan_workspace_bytes(big) > mod.PLAN_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_plan_noalloc(by(big), P, P, P, None, None) == mod.MOE_ENOSPACE
+
+
 def test_oracle_is_not_reachable_from_the_product():
     """The binding and the kernels never import or name the oracle."""
     pkg = os.path.join(ROOT, "balanced_token_dispatch_amd")
