@@ -299,14 +299,26 @@ class _LazyRows:
         return self.cache[rho]
 
 
-def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
+def _median_of(n, fn):
+    """Run fn() n times; (median wall seconds, the last result)."""
+    import statistics
+    times, out = [], None
+    for _ in range(n):
+        t0 = time.perf_counter()
+        out = fn()
+        times.append(time.perf_counter() - t0)
+    return statistics.median(times), out
+
+
+def cpu_baseline(layer, idx, w, rows_sample, tokens_sample, reps=3):
     """The oracle as it stands, on a bounded sample of the same step, scaled to tokens/s.
 
-    Timed on this host: the full plan and layout of all R ranks' routing, then permute,
-    both projections forward (with the gated unit, when the layer has it), the weighted
-    permute, both DGRADs and WGRADs on the first ``rows_sample`` rows of rank r's buffer, the combine, router-weight gradient and
-    un-permute reduce of ``tokens_sample`` tokens, and the fold on 1/8 of each replica row.
-    Each part is scaled to the full step.
+    Timed on this host, each part the median of ``reps`` runs: the full plan and layout of all
+    R ranks' routing, then permute, both projections forward (with the gated unit, when the
+    layer has it), the weighted permute, both DGRADs and WGRADs on the first ``rows_sample``
+    rows of rank r's buffer, the combine, router-weight gradient and un-permute reduce of
+    ``tokens_sample`` tokens, and the fold on 1/8 of each replica row.  Each part is scaled to
+    the full step.
     """
     import numpy as np
     import torch
@@ -314,12 +326,8 @@ def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
     s, r = layer.s, layer.rank
     bwd = layer.backward_enabled
     t = {}
-    t0 = time.perf_counter()
-    pl = oracle.plan(idx, s.E, s.B)
-    t["plan"] = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    cu, dest, src = oracle.layout(idx, pl, r)
-    t["layout"] = time.perf_counter() - t0
+    t["plan"], pl = _median_of(reps, lambda: oracle.plan(idx, s.E, s.B))
+    t["layout"], (cu, dest, src) = _median_of(reps, lambda: oracle.layout(idx, pl, r))
     n = int(min(rows_sample, cu[-1]))
     se, _, _ = pl.slot_table()
     pmap = {s.E + j: int(se[r, j]) for j in range(s.B) if se[r, j] >= 0}
@@ -338,27 +346,29 @@ def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
     for rho in range(s.G):                       # weight rows fetched outside the timed parts
         if cu_s[rho + 1] > cu_s[rho]:
             wu[rho], wd[rho]
-    t0 = time.perf_counter()
     gated = layer.activation == "swiglu"
-    xp = oracle.permute(x_rows, src_l.astype(np.int32), s.K)
-    if gated:
-        z, h = oracle.group_gemm_swiglu(xp, wu, cu_s)
-    else:
-        z = oracle.group_gemm("fwd", xp, wu, cu_s)
-    oracle.group_gemm("fwd", z, wd, cu_s)
-    if bwd:
-        dy = oracle.permute(g_rows, src_l.astype(np.int32), s.K, row_scale=w_flat)
-        dz = oracle.group_gemm("dgrad", dy, wd, cu_s)
-        dup = oracle.swiglu_backward(dz, h) if gated else dz
-        oracle.group_gemm("dgrad", dup, wu, cu_s)
-        act = [rho for rho in range(s.G) if cu_s[rho + 1] > cu_s[rho]]
-        for a, b, K_, N_ in ((z, dy, s.Hp, s.H), (xp, dup, s.H, layer.up_cols)):
-            for rho in act:                      # wgrad of the sampled segments only
-                lo, hi = cu_s[rho], cu_s[rho + 1]
-                sub = np.array([0, hi - lo])
-                oracle.group_gemm("wgrad", a[lo:hi], b[lo:hi], sub,
-                                  out=np.zeros((1, K_, N_), np.float32))
-    t["rows"] = time.perf_counter() - t0
+
+    def rows_part():
+        xp = oracle.permute(x_rows, src_l.astype(np.int32), s.K)
+        if gated:
+            z, h = oracle.group_gemm_swiglu(xp, wu, cu_s)
+        else:
+            z = oracle.group_gemm("fwd", xp, wu, cu_s)
+        oracle.group_gemm("fwd", z, wd, cu_s)
+        if bwd:
+            dy = oracle.permute(g_rows, src_l.astype(np.int32), s.K, row_scale=w_flat)
+            dz = oracle.group_gemm("dgrad", dy, wd, cu_s)
+            dup = oracle.swiglu_backward(dz, h) if gated else dz
+            oracle.group_gemm("dgrad", dup, wu, cu_s)
+            act = [rho for rho in range(s.G) if cu_s[rho + 1] > cu_s[rho]]
+            for a, b, K_, N_ in ((z, dy, s.Hp, s.H), (xp, dup, s.H, layer.up_cols)):
+                for rho in act:                      # wgrad of the sampled segments only
+                    lo, hi = cu_s[rho], cu_s[rho + 1]
+                    sub = np.array([0, hi - lo])
+                    oracle.group_gemm("wgrad", a[lo:hi], b[lo:hi], sub,
+                                      out=np.zeros((1, K_, N_), np.float32))
+
+    t["rows"], _ = _median_of(reps, rows_part)
     # combine: tokens_sample tokens of rank r, expert outputs gathered from a staged buffer
     ts = np.arange(min(tokens_sample, s.S))
     need = dest.reshape(s.R, s.S, s.K)[r, ts].reshape(-1)
@@ -372,24 +382,43 @@ def cpu_baseline(layer, idx, w, rows_sample, tokens_sample):
         g_full = np.zeros((s.S, s.H), np.uint16)
         g_full[ts] = g_tok
         dxp_rows = layer.dxp_all[torch.from_numpy(need.astype(np.int64)).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
-    t0 = time.perf_counter()
-    oracle.combine(y_rows, dest_l, w, r, s.S, s.K, tokens=ts)
-    if bwd:
-        oracle.combine_weight_grad(y_rows, dest_l, g_full, r, s.S, s.K, tokens=ts)
-        oracle.unpermute_reduce(dxp_rows, dest_l, r, s.S, s.K, tokens=ts)
-    t["combine"] = time.perf_counter() - t0
+
+    def combine_part():
+        oracle.combine(y_rows, dest_l, w, r, s.S, s.K, tokens=ts)
+        if bwd:
+            oracle.combine_weight_grad(y_rows, dest_l, g_full, r, s.S, s.K, tokens=ts)
+            oracle.unpermute_reduce(dxp_rows, dest_l, r, s.S, s.K, tokens=ts)
+
+    t["combine"], _ = _median_of(reps, combine_part)
     frac = 8
     t["fold"] = 0.0
     if bwd:
         dw_u = np.zeros((s.G, s.H * layer.up_cols // frac), np.float32)
         dw_d = np.zeros((s.G, s.H * s.Hp // frac), np.float32)
-        t0 = time.perf_counter()
-        oracle.replica_grad_fold(dw_u, pl, r)
-        oracle.replica_grad_fold(dw_d, pl, r)
-        t["fold"] = (time.perf_counter() - t0) * frac
+
+        def fold_part():
+            oracle.replica_grad_fold(dw_u, pl, r)
+            oracle.replica_grad_fold(dw_d, pl, r)
+
+        tf, _ = _median_of(reps, fold_part)
+        t["fold"] = tf * frac
     est = (t["plan"] + t["layout"] + t["rows"] * s.SK / max(n, 1)
            + t["combine"] * s.S / max(len(ts), 1) + t["fold"])
     return est, t, n, len(ts)
+
+
+def host_cpu():
+    """CPU model name, the CPUs this process may run on, and the BLAS thread count."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas_threads": blas_threads()}
 
 
 def blas_threads():
@@ -401,6 +430,113 @@ def blas_threads():
         return 1
 
 
+# Maxvio points of each workload's sweep: (workload whose calibration gives the routing, target).
+# The R32 shape's sweep takes maxvio 0 and 1 from the forward workload of the same shape.
+SWEEPS = {
+    "skew8_large_fwdbwd": [("skew1_large", 0.0), ("skew1_large", 1.0)],
+    "sweep_r64": [("sweep_r64", 0.0), ("sweep_r64", 1.0), ("sweep_r64", 4.0)],
+}
+SCALE_WORKLOAD = "sweep_r64"
+
+
+def rank_stats(layer):
+    import numpy as np
+    t = per_rank_ms(layer)
+    return {"max_ms": round(max(t), 4), "min_ms": round(min(t), 4),
+            "argmax_rank": int(np.argmax(t)), "max_over_min": round(max(t) / min(t), 4)}
+
+
+def kernel_fracs(timer, shape, n_slots, steps, gated=False):
+    """Per-kernel average launch time and fraction of its roofline from HIP-event timings."""
+    import numpy as np
+    work = algorithmic_work(shape, n_slots, gated=gated)
+    kernels, totals = {}, {}
+    for name, times in timer.ms().items():
+        bound, amount = work[name]
+        avg = float(np.mean(times))
+        totals[name] = float(np.sum(times)) / steps
+        if bound == "mfma":
+            ach = amount / (avg * 1e-3) / 1e12
+            kernels[name] = {"avg_ms": round(avg, 4), "launches_per_step": len(times) // steps,
+                             "tflops": round(ach, 1), "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+        else:
+            ach = amount / (avg * 1e-3) / 1e9 if avg > 0 else 0.0
+            kernels[name] = {"avg_ms": round(avg, 4), "launches_per_step": len(times) // steps,
+                             "gbs": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4)}
+    return kernels, totals
+
+
+def slots_used(layer):
+    s = layer.s
+    plan = layer.plan.cpu().numpy()
+    off_sexp = 8 + 4 * s.E + 5 * (s.E + s.R)
+    slots = plan[off_sexp + layer.rank * s.B: off_sexp + (layer.rank + 1) * s.B]
+    return int((slots >= 0).sum())
+
+
+def maxvio_sweep(layer, wl, info, ms_step, value, args):
+    """The step at the workload's other maxvio points on the same buffers, every rank's share
+    timed at each point; flatness of rank 0's time and of the slowest rank's across skews."""
+    s = layer.s
+    sweep = {f"{info['maxvio']:.2f}": {"ms_per_step": round(ms_step, 4),
+                                        "tokens_per_s": round(value, 1),
+                                        "home_load_ratio": round(info["home_load_ratio"], 3),
+                                        "every_rank": rank_stats(layer)}}
+    for wname, t in SWEEPS[wl.name]:
+        import synth
+        layer, _, _, info_t = setup_layer(synth.WORKLOADS[wname], t, args.rank, layer=layer)
+        n = max(5, args.steps // 2)
+        ms_t = run_steps(layer, n, 2) * 1000.0 / n
+        key = f"{info_t['maxvio']:.2f}"
+        sweep[key] = {"ms_per_step": round(ms_t, 4), "tokens_per_s": round(s.S / (ms_t * 1e-3), 1),
+                      "home_load_ratio": round(info_t["home_load_ratio"], 3),
+                      "status": int(layer.status.item()), "every_rank": rank_stats(layer)}
+        log(f"sweep maxvio {key}: {ms_t:.3f} ms/step, every rank {sweep[key]['every_rank']}")
+    pts = list(sweep.values())
+    t_all = [v["ms_per_step"] for v in pts]
+    sweep["flatness_max_over_min"] = round(max(t_all) / min(t_all), 4)
+    t_max = [v["every_rank"]["max_ms"] for v in pts]
+    sweep["flatness_of_slowest_rank"] = round(max(t_max) / min(t_max), 4)
+    return sweep
+
+
+def scale_sweep(args):
+    """R64 S8192 E384 K8 B8 H7168 H'2048, forward + backward, at maxvio 0, 1, 4 and 16: rank 0's
+    step time, tokens/s and every kernel's roofline fraction at each point, every rank's share
+    timed at each point, and the flatness across skews."""
+    import synth
+    import torch
+    wl = synth.WORKLOADS[SCALE_WORKLOAD]
+    layer = None
+    points = {}
+    for t in wl.maxvio_targets:
+        layer, _, _, info = setup_layer(wl, t, args.rank, layer=layer)
+        n = max(5, args.steps // 2)
+        run_steps(layer, 0, 2)
+        timer = EventTimer()
+        el = run_steps(layer, n, 0, timer)
+        ms_t = el * 1000.0 / n
+        kern, _ = kernel_fracs(timer, layer.s, slots_used(layer), n)
+        key = f"{info['maxvio']:.2f}"
+        points[key] = {"target": t, "ms_per_step": round(ms_t, 4),
+                       "tokens_per_s": round(layer.s.S / (ms_t * 1e-3), 1),
+                       "home_load_ratio": round(info["home_load_ratio"], 3),
+                       "status": int(layer.status.item()),
+                       "replica_slots_used_on_rank": slots_used(layer),
+                       "every_rank": rank_stats(layer),
+                       "kernels": {k: {kk: v[kk] for kk in ("avg_ms", "frac")} for k, v in kern.items()}}
+        log(f"scale sweep maxvio {key}: {ms_t:.3f} ms/step, every rank {points[key]['every_rank']}")
+    s = layer.s
+    del layer
+    torch.cuda.empty_cache()
+    t_all = [v["ms_per_step"] for v in points.values()]
+    t_max = [v["every_rank"]["max_ms"] for v in points.values()]
+    return {"workload": wl.name, "R": s.R, "S": s.S, "K": s.K, "E": s.E, "B": s.B, "H": s.H,
+            "H_prime": s.Hp, "step": "forward+backward", "points": points,
+            "flatness_max_over_min": round(max(t_all) / min(t_all), 4),
+            "flatness_of_slowest_rank": round(max(t_max) / min(t_max), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,7 +546,9 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=32768)
+    ap.add_argument("--no-scale-sweep", action="store_true",
+                    help="skip the R64 S8192 E384 sweep over maxvio 0/1/4/16")
+    ap.add_argument("--cpu-rows", type=int, default=16384)
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay figure")
     ap.add_argument("--main-only", action="store_true",
@@ -459,32 +597,17 @@ def main():
     timer = EventTimer()
     elapsed = run_steps(layer, args.steps, args.warmup, timer)
     status = int(layer.status.item())
-    plan = layer.plan.cpu().numpy()
     if status != 0:
         log(f"WARNING: plan status {status} (bad ids / slot overflow)")
-    E, R, B = s.E, s.R, s.B
-    off_sexp = 8 + 4 * E + 5 * (E + R)
-    slots = plan[off_sexp + args.rank * B: off_sexp + (args.rank + 1) * B]
-    n_slots = int((slots >= 0).sum())
+    n_slots = slots_used(layer)
     ms_step = elapsed * 1000.0 / args.steps
     value = s.S * args.steps / elapsed
 
     work = algorithmic_work(s, n_slots, gated=args.activation == "swiglu")
-    kernels = {}
-    totals = {}
-    for name, times in timer.ms().items():
-        bound, amount = work[name]
-        avg = float(np.mean(times))
-        per_step = float(np.sum(times)) / args.steps
-        totals[name] = per_step
-        if bound == "mfma":
-            ach = amount / (avg * 1e-3) / 1e12
-            kernels[name] = {"avg_ms": round(avg, 4), "launches_per_step": len(times) // args.steps,
-                             "tflops": round(ach, 1), "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
-        else:
-            ach = amount / (avg * 1e-3) / 1e9 if avg > 0 else 0.0
-            kernels[name] = {"avg_ms": round(avg, 4), "launches_per_step": len(times) // args.steps,
-                             "gbs": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4)}
+    kernels, totals = kernel_fracs(timer, s, n_slots, args.steps,
+                                   gated=args.activation == "swiglu")
+    # the sum of the kernels' event times against the wall-clock step: the rest is launch gaps
+    kern_ms = sum(totals.values())
     dom = max(totals, key=totals.get)
     bound, amount = work[dom]
     avg = kernels[dom]["avg_ms"]
@@ -515,57 +638,49 @@ def main():
             graph = {"error": str(exc)[:200]}
 
     sweep = {}
-    if not args.no_sweep and not args.main_only and wl.name == "skew8_large_fwdbwd":
-        def rank_stats():
-            t = per_rank_ms(layer)
-            return {"max_ms": round(max(t), 4), "min_ms": round(min(t), 4),
-                    "argmax_rank": int(np.argmax(t))}
-        sweep[f"{info['maxvio']:.2f}"] = {"ms_per_step": round(ms_step, 4),
-                                          "tokens_per_s": round(value, 1),
-                                          "home_load_ratio": round(info["home_load_ratio"], 3),
-                                          "every_rank": rank_stats()}
-        for t in (0.0, 1.0):
-            wl_t = synth.WORKLOADS["skew1_large"]
-            layer, idx_t, _, info_t = setup_layer(wl_t, t, args.rank, layer=layer)
-            el = run_steps(layer, max(5, args.steps // 2), 2)
-            ms_t = el * 1000.0 / max(5, args.steps // 2)
-            sweep[f"{info_t['maxvio']:.2f}"] = {
-                "ms_per_step": round(ms_t, 4), "tokens_per_s": round(s.S / (ms_t * 1e-3), 1),
-                "home_load_ratio": round(info_t["home_load_ratio"], 3),
-                "status": int(layer.status.item()), "every_rank": rank_stats()}
-            key = f"{info_t['maxvio']:.2f}"
-            log(f"sweep maxvio {key}: {ms_t:.3f} ms/step, every rank {sweep[key]['every_rank']}")
+    if not args.no_sweep and not args.main_only and wl.name in SWEEPS:
+        sweep = maxvio_sweep(layer, wl, info, ms_step, value, args)
         # restore the headline routing for the CPU baseline below
         layer, idx, w, info = setup_layer(wl, target, args.rank, layer=layer)
-        pts = [v for v in sweep.values() if isinstance(v, dict)]
-        t_all = [v["ms_per_step"] for v in pts]
-        sweep["flatness_max_over_min"] = round(max(t_all) / min(t_all), 4)
-        t_max = [v["every_rank"]["max_ms"] for v in pts]
-        sweep["flatness_of_slowest_rank"] = round(max(t_max) / min(t_max), 4)
 
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
         est, parts, n_rows, n_tok = cpu_baseline(layer, idx, w, args.cpu_rows, args.cpu_tokens)
-        cpu = {"value": round(s.S / est, 2), "unit": "tokens/s", "cores": blas_threads(),
+        hc = host_cpu()
+        cpu = {"value": round(s.S / est, 2), "unit": "tokens/s", "cores": hc["blas_threads"],
                "kind": "oracle",
                "sample": ((f"plan+layout of all {s.R} ranks' routing in full; permute, fwd up/down, "
                            f"weighted permute, dgrad x2, wgrad x2 on {n_rows} of {s.SK} rows; "
                            f"combine, router-weight gradient and un-permute reduce of {n_tok} of "
                            f"{s.S} tokens; fold on 1/8 of each row; "
-                           f"each part scaled to the full step") if layer.backward_enabled else
+                           f"each part timed 3 times (median) and scaled to the full step")
+                          if layer.backward_enabled else
                           (f"plan+layout of all {s.R} ranks' routing in full; permute, fwd up/down "
                            f"on {n_rows} of {s.SK} rows; combine of {n_tok} of {s.S} tokens; "
-                           f"each part scaled to the full forward")),
+                           f"each part timed 3 times (median) and scaled to the full forward")),
+               "cpu_model": hc["cpu_model"], "affinity_cpus": hc["affinity_cpus"],
+               "blas_threads": hc["blas_threads"],
                "seconds_measured": round(time.time() - t0, 1),
                "parts_s": {k: round(v, 3) for k, v in parts.items()}}
-        log(f"cpu baseline: {cpu['value']} tokens/s ({cpu['seconds_measured']} s)")
+        log(f"cpu baseline: {cpu['value']} tokens/s ({cpu['seconds_measured']} s, "
+            f"{hc['blas_threads']} BLAS threads, {hc['affinity_cpus']} CPUs, {hc['cpu_model']})")
+
+    scale = None
+    if not args.no_scale_sweep and not args.main_only and wl.name != SCALE_WORKLOAD:
+        # the R64 S8192 E384 sweep needs ~205 GB of the 288 GB: free this layer first
+        del layer
+        import gc
+        gc.collect()
+        torch.cuda.empty_cache()
+        scale = scale_sweep(args)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "copies_per_s": round(s.SK * args.steps / elapsed, 1),
+        "kernel_ms_per_step": round(kern_ms, 4),
         "forward_only": None if fwd_ms is None else {"ms_per_step": round(fwd_ms, 4),
                                                      "tokens_per_s": round(s.S / (fwd_ms * 1e-3), 1)},
         "graph_replay": graph,
@@ -573,13 +688,14 @@ def main():
         "config": {"workload": wl.name, "R": s.R, "S": s.S, "K": s.K, "E": s.E, "B": s.B,
                    "H": s.H, "H_prime": s.Hp, "activation": args.activation,
                    "rank": args.rank,
-                   "step": "forward+backward" if layer.backward_enabled else "forward",
+                   "step": "forward+backward" if wl.backward else "forward",
                    "maxvio": round(info["maxvio"], 3), "zipf_s": info["zipf_s"],
                    "plan_status": status, "replica_slots_used_on_rank": n_slots},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "maxvio_sweep": sweep or None,
+        "scale_sweep": scale,
     }
     print(json.dumps(out), flush=True)
 
