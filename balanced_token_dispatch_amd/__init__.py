@@ -26,7 +26,8 @@ EXPORTS = ("moe_status_string", "moe_plan_words", "moe_plan_workspace_bytes", "m
            "moe_dispatch_layout_workspace_bytes", "moe_dispatch_layout", "moe_prefetch",
            "moe_permute", "moe_group_gemm", "moe_combine", "moe_replica_grad_fold",
            "moe_unpermute_reduce", "moe_combine_weight_grad", "moe_group_gemm_swiglu",
-           "moe_swiglu_backward", "moe_group_gemm_workspace_bytes", "moe_plan_noalloc")
+           "moe_swiglu_backward", "moe_group_gemm_workspace_bytes", "moe_plan_noalloc",
+           "moe_group_gemm_gather")
 
 PLAN_NOALLOC_SCRATCH_BYTES = 4 << 20   # MOE_PLAN_NOALLOC_SCRATCH_BYTES in moe.h
 
@@ -54,6 +55,8 @@ _lib.moe_group_gemm_workspace_bytes.restype = _SZ
 _lib.moe_group_gemm_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
 _lib.moe_group_gemm.argtypes = [ctypes.c_int, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _P,
                                 _P, _P, _SZ, _P]
+_lib.moe_group_gemm_gather.argtypes = [ctypes.c_int, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _I64,
+                                       _P, _I32, _P, _P, _P, _P, _SZ, _P]
 _lib.moe_combine.argtypes = [_D, ctypes.c_int, _I64, _I32, _P, _P, _P, _P, _P]
 _lib.moe_replica_grad_fold.argtypes = [_D, _I32, _P, _P, _I64, _P]
 _lib.moe_unpermute_reduce.argtypes = [_D, ctypes.c_int, _I64, _I32, _P, _P, _P, _P]
@@ -160,6 +163,18 @@ def moe_group_gemm(op, a, b, cu_seqlens, out, Kd, N, ws=None, stream=None):
     _check(_lib.moe_group_gemm(op, _dtype(a), G, a.shape[0], Kd, N, _ptr(a), _ptr(b),
                                _ptr(cu_seqlens), _ptr(out), wp, wn, _stream(stream)),
            "moe_group_gemm")
+
+
+def moe_group_gemm_gather(op, x_src, gather, gather_div, b, cu_seqlens, out, Kd, N, ws=None,
+                          stream=None):
+    """moe_group_gemm (FWD or WGRAD) with row m of the row operand read from token row
+    x_src[gather[m] // gather_div]: the permute fused into the GEMM."""
+    G = cu_seqlens.numel() - 1
+    wp, wn = _ws(ws)
+    _check(_lib.moe_group_gemm_gather(op, _dtype(x_src), G, gather.numel(), Kd, N, _ptr(x_src),
+                                      x_src.shape[0], _ptr(gather), gather_div, _ptr(b),
+                                      _ptr(cu_seqlens), _ptr(out), wp, wn, _stream(stream)),
+           "moe_group_gemm_gather")
 
 
 def moe_group_gemm_swiglu(a, b, cu_seqlens, z, h, Kd, N, ws=None, stream=None):

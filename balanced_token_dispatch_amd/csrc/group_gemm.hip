@@ -184,6 +184,196 @@ __device__ inline bf16x8 read_operand(const uint16_t *src, int wbase, int t, int
   }
 }
 
+// ---- Gathered row operand ------------------------------------------------------------
+// With a gather, row m of the row operand is token row idx[m] / div of x: the row is read
+// straight from the token rows as the operand is loaded, so the tokens need not be permuted
+// into expert-grouped order first.  Token rows are scattered over x, which may be larger than
+// a buffer resource's 32-bit offsets reach, so these loads take per-lane 64-bit addresses
+// (global_load_lds_dwordx4: 16 bytes per lane into LDS at M0 + 16 * lane, the same layout as
+// the buffer form).  A chunk outside the operand (contraction past its end, rows past a
+// segment, columns past the output) reads from g_zeros instead, the gathered form of the
+// buffer resource's zero fill.
+struct GatherParams {
+  const char *x;       // token rows
+  uint32_t ld_bytes;   // bytes per token row (the operand's contraction or row length * 2)
+  const int32_t *idx;  // gather entry of every operand row
+  int n_tok;           // token rows in x
+  uint32_t magic;      // floor(e / div) = mulhi(2 e, magic) >> shift for 0 <= e < 2^31
+  int shift;
+  int div;
+};
+
+// 512 zero bytes: a __device__ object, zero-initialised when the code object loads and never
+// written.
+__device__ __align__(256) uint16_t g_zeros[256];
+
+__device__ inline int gather_div(int e, const GatherParams &gp) {
+  return (int)(__umulhi((uint32_t)e << 1, gp.magic) >> gp.shift);
+}
+
+// Token row of gather entry e, or -1 when e does not name one of the n_tok rows.
+__device__ inline int gather_token(int e, const GatherParams &gp) {
+  const int t = gather_div(e, gp);
+  return (e >= 0 && t < gp.n_tok) ? t : -1;
+}
+
+// A load of one 16-byte chunk per lane into LDS at M0 + 16 * lane from a 64-bit address.
+// As dma_one: asm so the compiler does not track it (ordering is by the explicit vmcnt waits),
+// no register result, one wait state after the M0 write.
+__device__ inline void gload_lds(const char *p, uint32_t m0) {
+  asm volatile(
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off" ::"v"(p),
+      "{m0}"(m0)
+      : "memory");
+}
+
+// A 32-bit load from a wave-uniform address, through the scalar data cache (SMEM, counted
+// by lgkmcnt): it leaves the vector-memory counter, which orders the operand loads, alone.
+__device__ inline int load_uniform(const int32_t *p) {
+  typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
+  return *(const_i32_ptr)p;
+}
+
+// Gathered operand whose contraction index is contiguous (the activation rows of FWD): each
+// lane loads one 16-byte chunk of one row per block and K step; its row is fixed for the
+// tile, so the token of each block's row is looked up once per tile.
+struct GatherC {
+  const char *x;
+  uint32_t ld_bytes;
+  int tok[kMaxBlk];  // token row of this lane's row in each block (0 for rows past the tile)
+  int coff;          // byte offset of this lane's chunk in the row at K step 0 of the tile
+  int zc;            // byte offset of this lane's chunk in g_zeros
+  int kc;            // contraction index of this lane's chunk within a K step
+};
+
+// Row r of block blk of a contiguous [256][BK] operand tile is 16 blk + lane / 4 and its chunk
+// is (lane & 3) ^ ((r >> 2) & 3) = (lane & 3) ^ ((lane >> 4) & 3) (see dma_init).
+template <class W>
+__device__ inline void gather_c_init(GatherC &g, const GatherParams &gp, int m0, int rows,
+                                     int k0) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int k = (lane & 3) ^ ((lane >> 4) & 3);
+  g.x = gp.x;
+  g.ld_bytes = gp.ld_bytes;
+  g.kc = k * 8;
+  g.zc = k * 16;
+  g.coff = k * 16 + k0 * (BK * 2);
+#pragma unroll
+  for (int u = 0; u < W::blk; ++u) {
+    const int r = (u * W::n + wid) * 16 + (lane >> 2);
+    int tok = 0;
+    if (r < rows) tok = max(gather_token(gp.idx[m0 + r], gp), 0);
+    g.tok[u] = tok;
+  }
+}
+
+// Load u of K step kt (contraction kt * BK .. of the tile's part); chunks at or past c_lim
+// (a ragged last step, or a step past the last) read zeros.
+template <class W>
+__device__ inline void gather_c_one(const GatherC &g, uint32_t lds_op, uint32_t wave_off, int kt,
+                                    int c_lim, int u) {
+  const char *p = g.x + (unsigned long long)(uint32_t)g.tok[u] * g.ld_bytes + g.coff +
+                  (long long)kt * (BK * 2);
+  if (kt * BK + g.kc >= c_lim) p = (const char *)g_zeros + g.zc;
+  gload_lds(p, lds_op + wave_off + u * W::n * 1024);
+}
+
+// Gathered operand whose contraction index is strided (the activation rows of WGRAD, where
+// the contraction runs over the segment's rows): each block of a K step covers two
+// contraction rows (lanes 0-31 and 32-63), so the rows, and their tokens, change every step.
+// Their gather entries are read with scalar loads (gather_s_fetch) right after a mid-step
+// barrier and turned into per-lane addresses (gather_s_addr) in the last two MFMA slots of
+// the same half step.  Scalar loads share the LDS reads' counter and return out of order, so
+// any wait while one is outstanding must wait for everything: issued where the counter has
+// just been drained and consumed after the half step's last fragment read, they cost neither
+// an early wait for the fragments nor arithmetic ahead of a step's first MFMA.
+struct GatherS {
+  GatherParams gp;
+  int m0, len;       // first operand row and row count of the segment (wave-uniform)
+  uint32_t e_lim;    // gather entries in [0, e_lim) name a token row
+  const char *xcol;  // x + this lane's column byte offset
+  long long ozero;   // xcol + ozero = this lane's chunk of g_zeros (wave-uniform)
+  int half;          // which of a block's two contraction rows this lane loads
+  int e[kMaxBlk][2];          // gather entries of the rows of the next step to be issued
+  const char *addr[kMaxBlk];  // this lane's load addresses for the step being issued
+};
+
+// Block blk = u n + wid of a strided [BK][256] operand tile covers contraction rows 2 blk and
+// 2 blk + 1; lane chunk p = lane & 31 of its row sits at column chunk p ^ (4 (cr & 3)) with
+// cr & 3 = 2 (wid & 1) + lane / 32 (see dma_init).  A chunk at or past the operand's last
+// column is moved onto its last chunk: its values only reach output rows past the edge, which
+// are never stored.
+template <class W>
+__device__ inline void gather_s_init(GatherS &g, const GatherParams &gp, int m0, int len, int i0,
+                                     int Kd) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int k = (lane & 31) ^ (4 * (2 * (wid & 1) + (lane >> 5)));
+  const int col = min(i0 + k * 8, Kd - 8);
+  g.gp = gp;
+  g.m0 = __builtin_amdgcn_readfirstlane(m0);
+  g.len = __builtin_amdgcn_readfirstlane(len);
+  const unsigned long long lim = (unsigned long long)gp.n_tok * gp.div;
+  g.e_lim = lim < 0x80000000ull ? (uint32_t)lim : 0x80000000u;
+  g.xcol = gp.x + (long long)col * 2;
+  g.ozero = (long long)((uintptr_t)g_zeros - (uintptr_t)gp.x) - (long long)i0 * 2;
+  g.half = lane >> 5;
+}
+
+// First segment row of block u's pair of contraction rows in K step kt (wave-uniform).
+template <class W>
+__device__ inline int gather_s_row(int kt, int u) {
+  return kt * BK + 2 * (u * W::n + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+}
+
+// Scalar loads of the gather entries of K step kt's rows (rows past the segment read its
+// last row's entry, which gather_s_addr then ignores).
+template <class W>
+__device__ inline void gather_s_fetch(GatherS &g, int kt) {
+#pragma unroll
+  for (int u = 0; u < W::blk; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      g.e[u][h] = load_uniform(g.gp.idx + g.m0 + min(gather_s_row<W>(kt, u) + h, g.len - 1));
+}
+
+// Byte offset from x of a contraction row's token (wave-uniform), or the offset that lands on
+// g_zeros for a row past the segment or one whose gather entry names no token row (zeros,
+// as the permute writes for such rows).  The empty asms keep the arithmetic in scalar
+// registers and free of branches: left alone, the compiler turns the choice into a branch
+// around the multiply, or selects the token per lane and multiplies in vector registers.
+__device__ inline long long gather_s_off(const GatherS &g, int e, bool in_seg) {
+  long long prod = (long long)((unsigned long long)(uint32_t)gather_div(e, g.gp) * g.gp.ld_bytes);
+  asm volatile("" : "+s"(prod));
+  long long o = ((uint32_t)e < g.e_lim && in_seg) ? prod : g.ozero;
+  asm volatile("" : "+s"(o));
+  return o;
+}
+
+// Address of this lane's load u of K step kt from the entries gather_s_fetch(kt) read.  The
+// entries pass through an empty asm first, so none of the arithmetic can be scheduled ahead
+// of the call's place.
+template <class W>
+__device__ inline void gather_s_addr(GatherS &g, int kt, int u) {
+  int e0 = g.e[u][0], e1 = g.e[u][1];
+  asm volatile("" : "+s"(e0), "+s"(e1));
+  const int c0 = gather_s_row<W>(kt, u);
+  const long long o0 = gather_s_off(g, e0, c0 < g.len);
+  const long long o1 = gather_s_off(g, e1, c0 + 1 < g.len);
+  g.addr[u] = g.xcol + (g.half ? o1 : o0);
+}
+
+template <class W>
+__device__ inline void gather_s_addr(GatherS &g, int kt) {
+#pragma unroll
+  for (int u = 0; u < W::blk; ++u) gather_s_addr<W>(g, kt, u);
+}
+
+template <class W>
+__device__ inline void gather_s_one(const GatherS &g, uint32_t lds_op, uint32_t wave_off, int u) {
+  gload_lds(g.addr[u], lds_op + wave_off + u * W::n * 1024);
+}
+
 template <int N>
 __device__ inline void waitcnt_vm() {
   // s_waitcnt vmcnt(N), expcnt and lgkmcnt at their maximum (no wait on them);
@@ -212,17 +402,31 @@ struct TileArgs {
   DmaOp a, b;
   int c_len, nk;
   uint32_t wave_off;  // this wave's 1-KB block offset within an operand tile (wave-uniform)
+  GatherC gc;         // the row-side operand gathered from token rows (AG == 1)
+  GatherS gs;         // (AG == 2)
 };
 
-// This wave's loads of K step kt (both operands) into LDS stage `stage`.
-template <class W, bool A_CONTIG, bool B_CONTIG, bool RAGGED>
-__device__ inline void dma_step(const uint16_t *lds, int stage, const TileArgs &ta, int kt) {
+// Row-side operand source of the K loop: AG = 0 buffer loads from one operand tensor;
+// AG = 1 gathered, contraction contiguous (FWD); AG = 2 gathered, contraction strided (WGRAD).
+// This wave's loads of K step kt (both operands) into LDS stage `stage`; with AG == 2,
+// gs.addr must hold the addresses of step kt (gather_s_addr).
+template <class W, bool A_CONTIG, bool B_CONTIG, bool RAGGED, int AG>
+__device__ inline void dma_step(const uint16_t *lds, int stage, const TileArgs &ta,
+                                const GatherS &gs, int kt) {
   const uint32_t st = (uint32_t)(uintptr_t)(lds_vptr)(lds + stage * STAGE_ELEMS);
-  const __amdgpu_buffer_rsrc_t ra = dma_rsrc(ta.a, kt, ta.nk);
   const __amdgpu_buffer_rsrc_t rb = dma_rsrc(ta.b, kt, ta.nk);
+  if constexpr (AG == 0) {
+    const __amdgpu_buffer_rsrc_t ra = dma_rsrc(ta.a, kt, ta.nk);
 #pragma unroll
-  for (int u = 0; u < W::blk; ++u)
-    dma_one<W, A_CONTIG, RAGGED>(ta.a, ra, st, ta.wave_off, kt, ta.c_len, u);
+    for (int u = 0; u < W::blk; ++u)
+      dma_one<W, A_CONTIG, RAGGED>(ta.a, ra, st, ta.wave_off, kt, ta.c_len, u);
+  } else if constexpr (AG == 1) {
+#pragma unroll
+    for (int u = 0; u < W::blk; ++u) gather_c_one<W>(ta.gc, st, ta.wave_off, kt, ta.c_len, u);
+  } else {
+#pragma unroll
+    for (int u = 0; u < W::blk; ++u) gather_s_one<W>(gs, st, ta.wave_off, u);
+  }
 #pragma unroll
   for (int u = 0; u < W::blk; ++u)
     dma_one<W, B_CONTIG, RAGGED>(ta.b, rb, st + OP_ELEMS * 2, ta.wave_off, kt, ta.c_len, u);
@@ -246,7 +450,7 @@ __device__ inline void dma_step(const uint16_t *lds, int stage, const TileArgs &
 // the middle of step k follows every wave's wait for step k+1, which half B then reads.
 // The prologue issues steps 0-2 and waits for step 0.  Loads of steps past the last have
 // every offset out of range and write zeros into stages no later read uses.
-template <class W, bool A_CONTIG, bool B_CONTIG, bool RAGGED>
+template <class W, bool A_CONTIG, bool B_CONTIG, bool RAGGED, int AG = 0>
 __device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta,
                                 f32x16 (&acc)[W::TM][W::TN]) {
   constexpr int TM = W::TM, TN = W::TN, NB = W::blk;
@@ -259,8 +463,20 @@ __device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta,
     for (int b = 0; b < TN; ++b) acc[a][b] = (f32x16){};
 
   Frags<W> F0, F1;
+  GatherS gs;
+  if constexpr (AG == 2) gs = ta.gs;
 #pragma unroll
-  for (int kt = 0; kt < 3; ++kt) dma_step<W, A_CONTIG, B_CONTIG, RAGGED>(lds, kt, ta, kt);
+  for (int kt = 0; kt < 3; ++kt) {
+    if constexpr (AG == 2) {
+      gather_s_fetch<W>(gs, kt);
+      gather_s_addr<W>(gs, kt);
+    }
+    dma_step<W, A_CONTIG, B_CONTIG, RAGGED, AG>(lds, kt, ta, gs, kt);
+  }
+  if constexpr (AG == 2) {  // for the first half A, which issues step 3
+    gather_s_fetch<W>(gs, 3);
+    gather_s_addr<W>(gs, 3);
+  }
   waitcnt_vm<2 * W::loads>();
   __syncthreads();
   read_frags<W, A_CONTIG, B_CONTIG>(F0, lds, wi, wj, lane, 0);
@@ -279,16 +495,23 @@ __device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta,
         F1.a[i] = read_operand<A_CONTIG>(cur, wi, i, lane, 1);
       else if (i < TM + TN)
         F1.b[i - TM] = read_operand<B_CONTIG>(cur + OP_ELEMS, wj, i - TM, lane, 1);
-      if (i == 1) ra = dma_rsrc(ta.a, k + 3, nk);
+      if (AG == 0 && i == 1) ra = dma_rsrc(ta.a, k + 3, nk);
       if (i == 2) rb = dma_rsrc(ta.b, k + 3, nk);
 #pragma unroll
       for (int u = 0; u < NB; ++u)
-        if (i == (u + 1) * TM * TN / (NB + 1))
-          dma_one<W, A_CONTIG, RAGGED>(ta.a, ra, st, ta.wave_off, k + 3, ta.c_len, u);
+        if (i == (u + 1) * TM * TN / (NB + 1)) {
+          if constexpr (AG == 0)
+            dma_one<W, A_CONTIG, RAGGED>(ta.a, ra, st, ta.wave_off, k + 3, ta.c_len, u);
+          else if constexpr (AG == 1)
+            gather_c_one<W>(ta.gc, st, ta.wave_off, k + 3, ta.c_len, u);
+          else
+            gather_s_one<W>(gs, st, ta.wave_off, u);
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
     waitcnt_vm<W::loads + NB>();
     __syncthreads();
+    if constexpr (AG == 2) gather_s_fetch<W>(gs, k + 4);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < TM * TN; ++i) {  // half B
@@ -304,6 +527,13 @@ __device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta,
         if (i == (u + 1) * TM * TN / (NB + 1))
           dma_one<W, B_CONTIG, RAGGED>(ta.b, rb, st + OP_ELEMS * 2, ta.wave_off, k + 3,
                                        ta.c_len, u);
+      // gathered strided operand: addresses of step k+4 (issued in the next half A) from the
+      // entries fetched after this step's barrier, once this half's fragment reads are out
+      if constexpr (AG == 2) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+          if (i == TM * TN - NB + u) gather_s_addr<W>(gs, k + 4, u);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -603,10 +833,15 @@ __device__ inline void epilogue_bf16(uint16_t *lds, const f32x16 (&acc)[W::TM][W
       }
   __syncthreads();
   constexpr int kRows = BM / W::n;  // rows stored by one wave, two per instruction
+  // the row offsets below depend only on the lane; left alone, the compiler computes them
+  // once per kernel and spills them across the K loop (the empty asm makes it recompute them
+  // per tile, a few instructions)
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
 #pragma unroll
   for (int r = 0; r < kRows / 2; ++r) {
-    const int i = wid * kRows + 2 * r + (lane >> 5);
-    const int c = lane & 31;
+    const int i = wid * kRows + 2 * r + (ln >> 5);
+    const int c = ln & 31;
     const u32x4 v = *(const u32x4 *)(lds + i * 256 + (c ^ (i & 31)) * 8);
     if (i < rows && c * 8 < cols) *(u32x4 *)(o + i * ld + c * 8) = v;
   }
@@ -641,10 +876,12 @@ __device__ inline void epilogue_swiglu(uint16_t *lds, const f32x16 (&acc)[W::TM]
       }
   __syncthreads();
   constexpr int kPass = W::threads / 16;  // rows per pass, 16 chunks each
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // per-tile row offsets, as in epilogue_bf16
 #pragma unroll
   for (int r = 0; r < BM / kPass; ++r) {
-    const int i = (threadIdx.x >> 4) + kPass * r;
-    const int c = threadIdx.x & 15;
+    const int i = (tid >> 4) + kPass * r;
+    const int c = tid & 15;
     const u32x4 v = *(const u32x4 *)(lds + i * 128 + (c ^ (i & 15)) * 8);
     if (i < rows && c * 8 < cols) *(u32x4 *)(o + i * ld + c * 8) = v;
   }
@@ -872,12 +1109,14 @@ __device__ inline void rows_epilogue(uint16_t *lds, const f32x16 (&acc)[W::TM][W
 // one segment x 256 output columns.  FWD: out[m, j] = sum_c a[m, c] W[rho][c, j], c < Kd.
 // DGRAD: out[m, j] = sum_c a[m, c] W[rho][j, c], c < N, j < Kd.  The whole contraction ends
 // in the epilogue; a part of it is stored to `partial` instead.
-template <int OP, bool RAGGED, class W>
+// With GATHER (FWD and the gated FWD only), the rows come from the token rows through gp.
+template <int OP, bool RAGGED, class W, bool GATHER>
 __device__ inline void rows_tile(const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
                                  void *__restrict__ out, void *__restrict__ out2, int G, int Kd,
                                  int N, int n_rt_total, int n_ct, const int *sCu,
                                  const int *sStart, uint16_t *lds, int t, int k0, int k1,
-                                 float *__restrict__ partial, const TileCtx &cx) {
+                                 float *__restrict__ partial, const TileCtx &cx,
+                                 const GatherParams &gp) {
   f32x16 acc[W::TM][W::TN];
   const RowsTile r = rows_tile_at(t, G, n_rt_total, n_ct, sCu, sStart);
   const uint16_t *w = b + (size_t)r.rho * Kd * N;
@@ -899,16 +1138,21 @@ __device__ inline void rows_tile(const uint16_t *__restrict__ a, const uint16_t 
   } else {
     TileArgs ta;
     ta.wave_off = cx.wave_off;
-    dma_init<W, true>(ta.a, a + (size_t)r.m0 * Kd, (long long)r.rows * Kd * 2, Kd, r.rows);
+    if constexpr (GATHER) {
+      gather_c_init<W>(ta.gc, gp, r.m0, r.rows, k0);
+    } else {
+      dma_init<W, true>(ta.a, a + (size_t)r.m0 * Kd, (long long)r.rows * Kd * 2, Kd, r.rows);
+      const long long da = (long long)k0 * ta.a.step;
+      ta.a.base += da;
+      ta.a.bytes -= da;
+    }
     dma_init<W, false>(ta.b, w + r.j0, ((long long)Kd * N - r.j0) * 2, N, N - r.j0);
-    const long long da = (long long)k0 * ta.a.step, db = (long long)k0 * ta.b.step;
-    ta.a.base += da;
-    ta.a.bytes -= da;
+    const long long db = (long long)k0 * ta.b.step;
     ta.b.base += db;
     ta.b.bytes -= db;
     ta.c_len = Kd - k0 * BK;
     ta.nk = k1 - k0;
-    tile_mma<W, true, false, RAGGED>(lds, ta, acc);
+    tile_mma<W, true, false, RAGGED, GATHER ? 1 : 0>(lds, ta, acc);
   }
   if (partial)
     store_partial<W>(partial, acc);
@@ -919,11 +1163,13 @@ __device__ inline void rows_tile(const uint16_t *__restrict__ a, const uint16_t 
 // Output tile t of the weight-gradient GEMM: out[rho][i, j] += sum_m a[m, i] b[m, j] over
 // the rows m of segment rho, i < Kd, j < N; n_it x n_ct tiles per active segment (sStart:
 // index of each segment among the active ones).
-template <class W>
+// With GATHER, row m of the first operand is a token row of gp.
+template <class W, bool GATHER>
 __device__ inline void wgrad_tile(const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
                                   float *__restrict__ out, int G, int Kd, int N, int n_it,
                                   int n_ct, const int *sCu, const int *sStart, const int *sOrd,
-                                  uint16_t *lds, long long t, const TileCtx &cx) {
+                                  uint16_t *lds, long long t, const TileCtx &cx,
+                                  const GatherParams &gp) {
   constexpr int TM = W::TM, TN = W::TN;
   f32x16 acc[TM][TN];
   const int per_seg = n_it * n_ct;
@@ -935,12 +1181,15 @@ __device__ inline void wgrad_tile(const uint16_t *__restrict__ a, const uint16_t
   const int i0 = it * BM, j0 = ct * BN;
   TileArgs ta;
   ta.wave_off = cx.wave_off;
-  dma_init<W, false>(ta.a, a + (size_t)m0 * Kd + i0, ((long long)len * Kd - i0) * 2, Kd,
-                     Kd - i0);
+  if constexpr (GATHER)
+    gather_s_init<W>(ta.gs, gp, m0, len, i0, Kd);
+  else
+    dma_init<W, false>(ta.a, a + (size_t)m0 * Kd + i0, ((long long)len * Kd - i0) * 2, Kd,
+                       Kd - i0);
   dma_init<W, false>(ta.b, b + (size_t)m0 * N + j0, ((long long)len * N - j0) * 2, N, N - j0);
   ta.c_len = len;
   ta.nk = (len + BK - 1) / BK;
-  tile_mma<W, false, false, false>(lds, ta, acc);
+  tile_mma<W, false, false, false, GATHER ? 2 : 0>(lds, ta, acc);
   float *o = out + ((size_t)rho * Kd + i0) * N + j0;
   wgrad_rmw<W>(o, N, Kd - i0, N - j0, acc, lds, cx.wi, cx.wj, cx.lane);
 }
@@ -950,11 +1199,13 @@ __device__ inline void wgrad_tile(const uint16_t *__restrict__ a, const uint16_t
 constexpr int kLdsRing = kStages * STAGE_ELEMS;
 constexpr int kLdsWgrad = kRmwLdsElems > kLdsRing ? kRmwLdsElems : kLdsRing;
 
-template <int OP, bool RAGGED, int WN>
+// GATHER: the row operand (FWD, gated FWD) or the first operand (WGRAD) is read from token
+// rows through gp instead of from `a`.
+template <int OP, bool RAGGED, int WN, bool GATHER = false>
 __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
     const int32_t *__restrict__ cu, void *__restrict__ out, void *__restrict__ out2,
-    float *__restrict__ ws, int G, int M_total, int Kd, int N) {
+    float *__restrict__ ws, int G, int M_total, int Kd, int N, GatherParams gp) {
   using W = Waves<WN>;
   constexpr bool wgrad = OP == MOE_GEMM_WGRAD;
   __shared__ __attribute__((aligned(16))) uint16_t lds[wgrad ? kLdsWgrad : kLdsRing];
@@ -979,7 +1230,8 @@ __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
     for (int r = 0; base < total; ++r, base += grid) {
       const long long t = base + ((r & 1) ? grid - 1 - lb : lb);
       if (t < total)
-        wgrad_tile<W>(a, b, (float *)out, G, Kd, N, n_it, n_ct, sCu, sStart, sOrd, lds, t, cx);
+        wgrad_tile<W, GATHER>(a, b, (float *)out, G, Kd, N, n_it, n_ct, sCu, sStart, sOrd, lds,
+                              t, cx, gp);
     }
   } else {
     constexpr int bk = kStageK<OP>;
@@ -1006,8 +1258,8 @@ __global__ __launch_bounds__(Waves<WN>::threads, 1) void k_ggemm_bf16(
       } else {
         break;
       }
-      rows_tile<OP, RAGGED, W>(a, b, out, out2, G, Kd, N, n_rt_total, n_ct, sCu, sStart, lds,
-                               tile, k0, k1, slot, cx);
+      rows_tile<OP, RAGGED, W, GATHER>(a, b, out, out2, G, Kd, N, n_rt_total, n_ct, sCu, sStart,
+                                       lds, tile, k0, k1, slot, cx, gp);
     }
   }
 }
@@ -1134,21 +1386,27 @@ static size_t sk_workspace_bytes() { return (size_t)device_cu_count() * kTileFlo
 // A row-operand bf16 GEMM: the persistent kernel, then (when a workspace is given and the
 // tiles are long enough that a split could pay) the reduce of the split last round.  The
 // kernel decides on the device whether to split; the reduce returns at once when it did not.
-template <int OP, int WN>
+// With GATHER the row operand is read through gp (a gathered load tests every chunk against
+// the contraction's end itself, so it needs no RAGGED form).
+template <int OP, int WN, bool GATHER = false>
 static void launch_rows(int contraction, const uint16_t *a, const uint16_t *b,
                         const int32_t *cu, void *out, void *out2, void *ws, int G, int M_total,
-                        int Kd, int N, hipStream_t stream) {
+                        int Kd, int N, hipStream_t stream, const GatherParams &gp = {}) {
   const int grid = device_cu_count();
   // a split can pay only when a tile's contraction exceeds what it must save
   float *sk_ws = ws && contraction > kSkGain ? (float *)ws : nullptr;
   // a contiguous operand whose contraction is not a multiple of the K stage needs a per-lane
   // column test in its last stage
-  if (contraction % kStageK<OP>)
+  if constexpr (GATHER)
+    hipLaunchKernelGGL((k_ggemm_bf16<OP, false, WN, true>), dim3(grid),
+                       dim3(Waves<WN>::threads), 0, stream, a, b, cu, out, out2, sk_ws, G,
+                       M_total, Kd, N, gp);
+  else if (contraction % kStageK<OP> != 0)
     hipLaunchKernelGGL((k_ggemm_bf16<OP, true, WN>), dim3(grid), dim3(Waves<WN>::threads), 0,
-                       stream, a, b, cu, out, out2, sk_ws, G, M_total, Kd, N);
+                       stream, a, b, cu, out, out2, sk_ws, G, M_total, Kd, N, gp);
   else
     hipLaunchKernelGGL((k_ggemm_bf16<OP, false, WN>), dim3(grid), dim3(Waves<WN>::threads), 0,
-                       stream, a, b, cu, out, out2, sk_ws, G, M_total, Kd, N);
+                       stream, a, b, cu, out, out2, sk_ws, G, M_total, Kd, N, gp);
   if (sk_ws)
     hipLaunchKernelGGL((k_ggemm_sk_reduce<OP, WN>), dim3(grid * kSkReduceBlocks), dim3(256), 0,
                        stream, cu, out, out2, sk_ws, grid, G, M_total, Kd, N);
@@ -1206,7 +1464,7 @@ extern "C" moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t 
     default:
       hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_WGRAD, false, 4>), dim3(device_cu_count()),
                          dim3(Waves<4>::threads), 0, stream, a16, b16, cu_seqlens, out, nullptr,
-                         nullptr, G, M_total, Kd, N);
+                         nullptr, G, M_total, Kd, N, GatherParams{});
   }
   return launch_status();
 }
@@ -1225,5 +1483,51 @@ extern "C" moe_status_t moe_group_gemm_swiglu(moe_dtype dtype, int32_t G, int32_
   // 8 waves: the gated epilogue needs the registers the 128x128 wave tile would take
   launch_rows<kOpSwiglu, 4>(Kd, (const uint16_t *)a, (const uint16_t *)b, cu_seqlens, z, h, ws,
                             G, M_total, Kd, N, stream);
+  return launch_status();
+}
+
+// floor(e / d) = mulhi(2 e, magic) >> shift = (e * magic) >> (31 + shift) for every
+// 0 <= e < 2^31 and d >= 1: with shift = ceil(log2 d) and magic = floor(2^(31 + shift) / d) + 1
+// (< 2^32), the product's error stays below one unit of the quotient for 31-bit dividends (the
+// round-up method of Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994).  Doubling the dividend keeps the high word's shift non-negative, so
+// d = 1 needs no special case.
+static void div_magic(int32_t d, uint32_t *magic, int *shift) {
+  int l = 0;
+  while ((1LL << l) < d) ++l;
+  *magic = (uint32_t)((1ULL << (31 + l)) / (unsigned long long)d + 1);
+  *shift = l;
+}
+
+extern "C" moe_status_t moe_group_gemm_gather(moe_gemm_op op, moe_dtype dtype, int32_t G,
+                                              int32_t M_total, int32_t Kd, int32_t N,
+                                              const void *x_src, int64_t src_rows,
+                                              const int32_t *gather, int32_t gather_div,
+                                              const void *b, const int32_t *cu_seqlens,
+                                              void *out, void *ws, size_t ws_bytes,
+                                              hipStream_t stream) {
+  if (!x_src || !gather || !b || !cu_seqlens || !out) return MOE_EINVAL;
+  if (dtype != MOE_BF16 || (op != MOE_GEMM_FWD && op != MOE_GEMM_WGRAD)) return MOE_EINVAL;
+  if (G < 1 || G > kMaxG || M_total < 0 || Kd < 8 || N < 8 || Kd % 8 || N % 8) return MOE_EINVAL;
+  if (src_rows < 1 || src_rows >= (1LL << 31) || gather_div < 1) return MOE_EINVAL;
+  if ((long long)M_total * (Kd > N ? Kd : N) >= (1LL << 40)) return MOE_EINVAL;
+  if (op == MOE_GEMM_WGRAD && N > (1 << 20)) return MOE_EINVAL;
+  if (ws && ws_bytes < moe_group_gemm_workspace_bytes(op, dtype)) return MOE_ENOSPACE;
+  if (M_total == 0) return MOE_OK;
+  GatherParams gp;
+  gp.x = (const char *)x_src;
+  gp.ld_bytes = (uint32_t)Kd * 2;
+  gp.idx = gather;
+  gp.n_tok = (int)src_rows;
+  gp.div = gather_div;
+  div_magic(gather_div, &gp.magic, &gp.shift);
+  const uint16_t *b16 = (const uint16_t *)b;
+  if (op == MOE_GEMM_FWD)
+    launch_rows<MOE_GEMM_FWD, 2, true>(Kd, nullptr, b16, cu_seqlens, out, nullptr, ws, G,
+                                       M_total, Kd, N, stream, gp);
+  else
+    hipLaunchKernelGGL((k_ggemm_bf16<MOE_GEMM_WGRAD, false, 4, true>), dim3(device_cu_count()),
+                       dim3(Waves<4>::threads), 0, stream, nullptr, b16, cu_seqlens, out,
+                       nullptr, nullptr, G, M_total, Kd, N, gp);
   return launch_status();
 }

@@ -14,6 +14,10 @@ adjoint for the weights) -> down DGRAD -> down WGRAD -> up DGRAD (into rank
 r's slice of the all-ranks input-gradient buffer) -> up WGRAD -> un-permute
 reduce of the input gradients to the tokens (dispatch's adjoint) -> fold the
 replica rows of both weight gradients into their home experts.
+With ``fused_gather=True`` (identity activation) there is no permute and no
+xp buffer: the up projection's FWD and WGRAD read their row operand straight
+from the token rows through src_flat (moe_group_gemm_gather), the permute
+fused into the expert GEMM.
 The activation between the projections is the identity, or, with
 ``activation="swiglu"``, the gated linear unit: the up projection then has
 2H' columns holding (gate, up) pairs, its GEMM writes both the pre-activation
@@ -26,7 +30,8 @@ import torch
 
 from . import (GEMM_DGRAD, GEMM_FWD, GEMM_WGRAD, dims as _mk_dims, dispatch_layout_workspace_bytes,
                group_gemm_workspace_bytes, moe_combine, moe_combine_weight_grad,
-               moe_dispatch_layout, moe_group_gemm, moe_group_gemm_swiglu, moe_permute, moe_plan,
+               moe_dispatch_layout, moe_group_gemm, moe_group_gemm_gather, moe_group_gemm_swiglu,
+               moe_permute, moe_plan,
                moe_prefetch, moe_replica_grad_fold, moe_swiglu_backward, moe_unpermute_reduce,
                plan_words, plan_workspace_bytes)
 
@@ -52,10 +57,13 @@ class Shape:
 
 class LayerStep:
     def __init__(self, shape: Shape, rank: int = 0, dtype=torch.bfloat16, device="cuda",
-                 backward: bool = True, activation: str = "identity"):
+                 backward: bool = True, activation: str = "identity", fused_gather: bool = False):
         s = shape
         if activation not in ("identity", "swiglu"):
             raise ValueError(f"activation {activation!r}")
+        if fused_gather and (activation != "identity" or dtype != torch.bfloat16):
+            raise ValueError("the gathered (permute-fused) up projection is bf16, identity only")
+        self.fused_gather = fused_gather
         self.s, self.rank, self.dtype, self.device = s, rank, dtype, device
         self.activation = activation
         # gated: the up projection has 2H' columns, (gate, up) pairs interleaved
@@ -81,7 +89,8 @@ class LayerStep:
         self.x_all = torch.zeros((s.R * s.S, s.H), **act)
         self.w_up = torch.zeros((s.G, s.H, self.up_cols), **act)
         self.w_down = torch.zeros((s.G, s.Hp, s.H), **act)
-        self.xp = torch.zeros((s.SK, s.H), **act)
+        # the permuted token rows (not needed when the up projection gathers them itself)
+        self.xp = None if fused_gather else torch.zeros((s.SK, s.H), **act)
         self.z = torch.zeros((s.SK, s.Hp), **act)
         # gated: the pre-activation, kept for the backward
         self.hpre = torch.zeros((s.SK, self.up_cols), **act) if activation == "swiglu" else None
@@ -129,13 +138,17 @@ class LayerStep:
           self.cu, self.dest, self.src, self.ws)
         c(timer, "prefetch", moe_prefetch, self.d, r, self.plan, self.w_up)
         c(timer, "prefetch", moe_prefetch, self.d, r, self.plan, self.w_down)
-        c(timer, "permute", moe_permute, self.d, self.x_all, self.src, self.xp)
-        if self.activation == "swiglu":
-            c(timer, "gemm_fwd_swiglu", moe_group_gemm_swiglu, self.xp, self.w_up, self.cu, self.z,
-              self.hpre, s.H, self.up_cols, self.gemm_ws)
+        if self.fused_gather:   # up projection reading the token rows through src_flat
+            c(timer, "gemm_fwd_gather", moe_group_gemm_gather, GEMM_FWD, self.x_all, self.src,
+              s.K, self.w_up, self.cu, self.z, s.H, s.Hp, self.gemm_ws)
         else:
-            c(timer, "gemm_fwd", moe_group_gemm, GEMM_FWD, self.xp, self.w_up, self.cu, self.z,
-              s.H, s.Hp, self.gemm_ws)
+            c(timer, "permute", moe_permute, self.d, self.x_all, self.src, self.xp)
+            if self.activation == "swiglu":
+                c(timer, "gemm_fwd_swiglu", moe_group_gemm_swiglu, self.xp, self.w_up, self.cu,
+                  self.z, self.hpre, s.H, self.up_cols, self.gemm_ws)
+            else:
+                c(timer, "gemm_fwd", moe_group_gemm, GEMM_FWD, self.xp, self.w_up, self.cu, self.z,
+                  s.H, s.Hp, self.gemm_ws)
         c(timer, "gemm_fwd", moe_group_gemm, GEMM_FWD, self.z, self.w_down, self.cu, self.y, s.Hp,
           s.H, self.gemm_ws)
         c(timer, "combine", moe_combine, self.d, r, self.y_all, self.dest,
@@ -157,8 +170,12 @@ class LayerStep:
             dup = self.dh
         c(timer, "gemm_dgrad", moe_group_gemm, GEMM_DGRAD, dup, self.w_up, self.cu, self.dxp,
           s.H, self.up_cols, self.gemm_ws)
-        c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.xp, dup, self.cu, self.dw_up,
-          s.H, self.up_cols)
+        if self.fused_gather:
+            c(timer, "gemm_wgrad_gather", moe_group_gemm_gather, GEMM_WGRAD, self.x_all, self.src,
+              s.K, dup, self.cu, self.dw_up, s.H, self.up_cols)
+        else:
+            c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.xp, dup, self.cu, self.dw_up,
+              s.H, self.up_cols)
         c(timer, "unpermute_reduce", moe_unpermute_reduce, self.d, r, self.dxp_all, self.dest,
           self.dx)
         c(timer, "fold", moe_replica_grad_fold, self.d, r, self.plan, self.dw_up)

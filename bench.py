@@ -65,6 +65,8 @@ KERNEL_SOURCES = {  # bench kernel name -> (rocprof name prefix, source files th
     "gemm_dgrad": ("moe::k_ggemm_bf16<1", ("group_gemm.hip", "common.hpp")),
     "gemm_wgrad": ("moe::k_ggemm_bf16<2", ("group_gemm.hip", "common.hpp")),
     "gemm_fwd_swiglu": ("moe::k_ggemm_bf16<3", ("group_gemm.hip", "common.hpp")),
+    "gemm_fwd_gather": ("moe::k_ggemm_bf16<0, false, 2, true>", ("group_gemm.hip", "common.hpp")),
+    "gemm_wgrad_gather": ("moe::k_ggemm_bf16<2, false, 4, true>", ("group_gemm.hip", "common.hpp")),
     "permute": ("moe::k_permute<false>", ("rows.hip", "common.hpp")),
     "permute_weighted": ("moe::k_permute<true>", ("rows.hip", "common.hpp")),
     "combine": ("moe::k_combine<true, true>", ("rows.hip", "common.hpp")),
@@ -192,6 +194,8 @@ def algorithmic_work(shape, n_slots_used, gated=False):
         "permute": ("hbm", 2.0 * SK * H * 2 + 4.0 * SK),
         "gemm_fwd": ("mfma", gemm),
         "gemm_fwd_swiglu": ("mfma", 2.0 * gemm),
+        "gemm_fwd_gather": ("mfma", gemm),
+        "gemm_wgrad_gather": ("mfma", gemm),
         "combine": ("hbm", SK * H * 2.0 + S * H * 2.0 + 8.0 * SK),
         "permute_weighted": ("hbm", 2.0 * SK * H * 2 + 8.0 * SK),
         "gemm_dgrad": ("mfma", gemm * both),
@@ -205,7 +209,8 @@ def algorithmic_work(shape, n_slots_used, gated=False):
     }
 
 
-def setup_layer(wl, target, rank, placement="receiver0", layer=None, activation="identity"):
+def setup_layer(wl, target, rank, placement="receiver0", layer=None, activation="identity",
+                fused_gather=False):
     import numpy as np
     import torch
     import synth
@@ -217,7 +222,7 @@ def setup_layer(wl, target, rank, placement="receiver0", layer=None, activation=
     log(f"routing {wl.name} maxvio target {target}: zipf s={zipf:.4f}, {time.time() - t0:.1f}s")
     if layer is None:
         layer = LayerStep(Shape(d.R, d.S, d.K, d.E, d.B, d.H, d.Hp), rank=rank,
-                          activation=activation, backward=wl.backward)
+                          activation=activation, backward=wl.backward, fused_gather=fused_gather)
         seed = wl.base_seed
         synth.fill_normal_(layer.x_all, 1.0, seed * 10 + 1)
         synth.fill_normal_(layer.w_up, 0.02, seed * 10 + 2)
@@ -510,7 +515,8 @@ def scale_sweep(args):
     layer = None
     points = {}
     for t in wl.maxvio_targets:
-        layer, _, _, info = setup_layer(wl, t, args.rank, layer=layer)
+        layer, _, _, info = setup_layer(wl, t, args.rank, layer=layer,
+                                        fused_gather=args.fused_gather)
         n = max(5, args.steps // 2)
         run_steps(layer, 0, 2)
         timer = EventTimer()
@@ -556,6 +562,8 @@ def main():
                          "(keeps a profiler's per-kernel averages to the main step's launches)")
     ap.add_argument("--activation", choices=("identity", "swiglu"), default="identity",
                     help="activation between the projections (swiglu: gated up projection)")
+    ap.add_argument("--fused-gather", action="store_true",
+                    help="the up projection gathers its rows from the token rows (no permute)")
     ap.add_argument("--probe", action="store_true",
                     help="one warm-up step, a 1 GiB calibration copy, one step (for --pmc runs)")
     ap.add_argument("--render-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -581,7 +589,8 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     target = wl.maxvio_targets[-1] if wl.maxvio_targets[-1] is not None else None
-    layer, idx, w, info = setup_layer(wl, target, args.rank, activation=args.activation)
+    layer, idx, w, info = setup_layer(wl, target, args.rank, activation=args.activation,
+                                      fused_gather=args.fused_gather)
     s = layer.s
     if args.probe:
         layer.step()
@@ -687,6 +696,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "R": s.R, "S": s.S, "K": s.K, "E": s.E, "B": s.B,
                    "H": s.H, "H_prime": s.Hp, "activation": args.activation,
+                   "dispatch": "permute fused into the up GEMM" if args.fused_gather
+                   else "permute, then the up GEMM",
                    "rank": args.rank,
                    "step": "forward+backward" if wl.backward else "forward",
                    "maxvio": round(info["maxvio"], 3), "zipf_s": info["zipf_s"],

@@ -14,6 +14,8 @@
  *   moe_prefetch          slot weight rows <- the experts they duplicate
  *   moe_permute           token rows -> expert-grouped rows (bitwise gather)
  *   moe_group_gemm        grouped GEMM over one [E+B, Kd, N] weight tensor
+ *   moe_group_gemm_gather the same, its row operand gathered from the token
+ *                         rows as it is loaded (permute fused into the GEMM)
  *   moe_combine           router-weighted sum of each token's K expert rows
  *   backward: moe_permute (weighted), moe_group_gemm DGRAD/WGRAD,
  *             moe_replica_grad_fold
@@ -229,6 +231,38 @@ moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t G, int32_t 
                             int32_t Kd, int32_t N, const void *a, const void *b,
                             const int32_t *cu_seqlens, void *out, void *ws, size_t ws_bytes,
                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_group_gemm_gather -- moe_group_gemm whose row operand is gathered from
+ * the token rows while the GEMM loads it, so the tokens reach their
+ * expert-grouped GEMM rows with no permute pass: the dispatch's permute fused
+ * into the expert GEMM.  [blog] "What This Does" (tokens go straight to their
+ * final expert-grouped position); [repocard] "Strengths" (permute fused into
+ * dispatch, zero copy).
+ *
+ * Row m of the operand A is token row x_src[gather[m] / gather_div].  With
+ * gather = src_flat of moe_dispatch_layout and gather_div = K, A is the xp
+ * that moe_permute writes, and the result is that of moe_permute followed by
+ * moe_group_gemm, bit for bit (same products, same summation order):
+ *   FWD:   out [M_total, N] = A[seg] @ W[rho],   b = W [G, Kd, N] (the up
+ *          projection's forward);
+ *   WGRAD: out fp32 [G, Kd, N] += A[seg]^T @ b[seg],   b [M_total, N] (the up
+ *          projection's weight gradient, b = its output gradient).
+ *   x_src  [src_rows, Kd] bf16, rows of Kd elements; it may be larger than
+ *          4 GB (the gathered loads take 64-bit addresses).  1 <= src_rows < 2^31.
+ *   gather [M_total] int32, gather_div >= 1.  An entry outside
+ *          [0, src_rows * gather_div) reads row 0 (FWD; that output row is then
+ *          unspecified) or zeros (WGRAD); moe_dispatch_layout writes such entries
+ *          (-1) only for rows past cu_seqlens[G], outside every segment.
+ *   G, M_total, Kd, N, cu_seqlens, out, ws: as moe_group_gemm (FWD may split
+ *   its last round with the workspace).  bf16 only; DGRAD (whose row operand is
+ *   an output gradient, already in expert-grouped order) is MOE_EINVAL.
+ * ------------------------------------------------------------------------- */
+moe_status_t moe_group_gemm_gather(moe_gemm_op op, moe_dtype dtype, int32_t G, int32_t M_total,
+                                   int32_t Kd, int32_t N, const void *x_src, int64_t src_rows,
+                                   const int32_t *gather, int32_t gather_div, const void *b,
+                                   const int32_t *cu_seqlens, void *out, void *ws,
+                                   size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_group_gemm_swiglu -- the FWD grouped GEMM with a gated (SwiGLU) epilogue:

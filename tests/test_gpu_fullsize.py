@@ -75,8 +75,9 @@ def _gpu():
 def test_full_size_step(name, target):
     from balanced_token_dispatch_amd import (GEMM_DGRAD, GEMM_FWD, GEMM_WGRAD, moe_combine,
                                              moe_combine_weight_grad, moe_dispatch_layout,
-                                             moe_group_gemm, moe_permute, moe_plan, moe_prefetch,
-                                             moe_replica_grad_fold, moe_unpermute_reduce)
+                                             moe_group_gemm, moe_group_gemm_gather, moe_permute,
+                                             moe_plan, moe_prefetch, moe_replica_grad_fold,
+                                             moe_unpermute_reduce)
     from balanced_token_dispatch_amd.layer import LayerStep, Shape
     wl = synth.WORKLOADS[name]
     d = wl.dims
@@ -151,6 +152,13 @@ def test_full_size_step(name, target):
     assert (host_rows(L.xp, rows) == x_rows).all(), "permute rows"
     _, z_ref = oracle.group_gemm_rows("fwd", x_rows, Wu, cu_c, np.arange(rows.size))
     check_close(host_rows(L.z, rows), z_ref, "bf16", what="up projection rows")
+    # the permute fused into the up projection: the same bits as permute + GEMM, every row
+    z_g = torch.empty_like(L.z)
+    moe_group_gemm_gather(GEMM_FWD, L.x_all, L.src, K, L.w_up, L.cu, z_g, H, Hp, L.gemm_ws)
+    torch.cuda.synchronize()
+    assert torch.equal(z_g.view(torch.int16), L.z.view(torch.int16)), "gathered up projection"
+    check_close(host_rows(z_g, rows), z_ref, "bf16", what="gathered up projection rows")
+    del z_g
     _, y_ref = oracle.group_gemm_rows("fwd", z_ref, Wd, cu_c, np.arange(rows.size))
     check_close(host_rows(L.y, rows), y_ref, "bf16", what="down projection rows")
     # combine: tokens whose copies landing on rank 0 are all in the sampled segments
@@ -190,7 +198,10 @@ def test_full_size_step(name, target):
     moe_group_gemm(GEMM_WGRAD, L.z, L.dy, L.cu, L.dw_down, Hp, H)
     moe_group_gemm(GEMM_DGRAD, L.dz, L.w_up, L.cu, L.dxp, H, Hp, L.gemm_ws)
     moe_group_gemm(GEMM_WGRAD, L.xp, L.dz, L.cu, L.dw_up, H, Hp)
+    dw_up_g = torch.zeros_like(L.dw_up)
+    moe_group_gemm_gather(GEMM_WGRAD, L.x_all, L.src, K, L.dz, L.cu, dw_up_g, H, Hp)
     torch.cuda.synchronize()
+    assert torch.equal(dw_up_g.view(torch.int32), L.dw_up.view(torch.int32)), "gathered up wgrad"
     g_rows = host_rows(L.dout_all, toks)
     src_l = (np.arange(rows.size) * K + src[rows] % K).astype(np.int32)   # compact copy ids
     rs = np.zeros(rows.size * K, np.float32)
@@ -230,7 +241,11 @@ def test_full_size_step(name, target):
     got2 = L.dw_up[rho][torch.as_tensor(ii2, device="cuda"),
                         torch.as_tensor(jj2, device="cuda")].cpu().numpy()
     assert np.abs(got2 - ent2).max() <= 1e-3 * max(1.0, np.abs(ent2).max()), (got2, ent2)
-    log(f"  wgrad entries of segment {rho} ({n_seg} rows) within tolerance")
+    got3 = dw_up_g[rho][torch.as_tensor(ii2, device="cuda"),
+                        torch.as_tensor(jj2, device="cuda")].cpu().numpy()
+    assert np.abs(got3 - ent2).max() <= 1e-3 * max(1.0, np.abs(ent2).max()), (got3, ent2)
+    del dw_up_g
+    log(f"  wgrad entries of segment {rho} ({n_seg} rows) within tolerance (also gathered)")
     # router-weight gradient and un-permute reduce of the sampled tokens, on the rows the
     # GPU produced (rank 0's expert outputs and input gradients, the peers' staged rows)
     moe_combine_weight_grad(L.d, rank, L.y_all, L.dest, L.dout_all[rank * S:(rank + 1) * S],

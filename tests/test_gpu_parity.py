@@ -581,6 +581,172 @@ def test_group_gemm_wgrad_row_edge_guard(Kd, N):
     assert (got[n_out:] == 0x80000000).all(), "guard after the last weight row untouched"
 
 
+# ------------------------------------------------------------------------------------------
+# fused gather GEMM: the row operand read from the token rows through the gather entries;
+# the definition is the oracle's permute followed by its grouped GEMM
+# ------------------------------------------------------------------------------------------
+
+def _run_gather(op, x, gather, div, b, cu, Kd, N, out_init=None, ws=None):
+    m = mod()
+    opc = {"fwd": m.GEMM_FWD, "wgrad": m.GEMM_WGRAD}[op]
+    if op == "wgrad":
+        out = _dev(out_init.astype(np.float32))
+    else:
+        out = poisoned((gather.size, N), torch.bfloat16)
+    xd = x if torch.is_tensor(x) else from_bits(x)
+    m.moe_group_gemm_gather(opc, xd, _dev(gather), div, from_bits(b), _dev(cu), out, Kd, N, ws)
+    return bits(out) if op != "wgrad" else out.cpu().numpy()
+
+
+def _gather_entries(rng, cu, M, n_tok, div):
+    """Copy ids of random tokens (repeats included) for the rows of every segment, -1 past
+    them, as the dispatch layout writes them."""
+    g = rng.integers(0, n_tok * div, size=M).astype(np.int32)
+    g[cu[-1]:] = -1
+    return g
+
+
+GATHER_SHAPES = [
+    # G, M, Kd, N, token rows, divisor
+    (5, 700, 64, 256, 300, 2),
+    (6, 1000, 136, 392, 97, 6),       # Kd, N not multiples of the tile; ragged contraction
+    (18, 600, 256, 512, 1000, 8),
+    (9, 257, 1408, 2048, 40, 17),
+    (1, 300, 96, 96, 7, 1),
+    (1088, 3000, 64, 128, 500, 3),    # the largest G: ~3 rows per segment, many empty
+]
+
+
+@pytest.mark.parametrize("op", ["fwd", "wgrad"])
+@pytest.mark.parametrize("shape", GATHER_SHAPES)
+def test_group_gemm_gather_integer_exact(op, shape):
+    G, M, Kd, N, n_tok, div = shape
+    rng = np.random.default_rng(G * 13 + M)
+    cu = _segments(rng, G, M - 3)
+    gather = _gather_entries(rng, cu, M, n_tok, div)
+    x = synth.to_bf16_bits(synth.host_ternary(G + M, 1, (n_tok, Kd)))
+    b = synth.to_bf16_bits(synth.host_ternary(G + M, 2, (G, Kd, N) if op == "fwd" else (M, N)))
+    init = synth.host_ternary(G, 9, (G, Kd, N)) if op == "wgrad" else None
+    log(f"gemm gather int op={op} shape={shape}")
+    got = _run_gather(op, x, gather, div, b, cu, Kd, N, init)
+    ref = oracle.group_gemm(op, oracle.permute(x, gather, div), b, cu, "bf16", out=init)
+    if op == "wgrad":
+        assert (got == ref).all()
+    else:
+        rows = cu[-1]
+        assert (got[:rows] == ref[:rows]).all()
+        assert (got[rows:].view(np.uint16) == 0x7F7F).all(), "rows outside segments untouched"
+
+
+def test_group_gemm_gather_wgrad_invalid_entries():
+    """WGRAD reads a gather entry that names no token row (negative, or at least
+    src_rows * divisor) as a zero row, as the permute writes for a negative entry: bit-exact
+    against the oracle's permute (entries past the source mapped to -1 for it) and GEMM."""
+    G, M, Kd, N, n_tok, div = 7, 1500, 264, 520, 300, 4
+    rng = np.random.default_rng(21)
+    cu = _segments(rng, G, M - 3)
+    gather = _gather_entries(rng, cu, M, n_tok, div)
+    bad = rng.choice(int(cu[-1]), size=40, replace=False)
+    gather[bad[:20]] = -1 - rng.integers(0, 1000, 20)
+    gather[bad[20:]] = n_tok * div + rng.integers(0, 1000, 20)
+    x = synth.to_bf16_bits(synth.host_ternary(3, 1, (n_tok, Kd)))
+    b = synth.to_bf16_bits(synth.host_ternary(3, 2, (M, N)))
+    init = synth.host_ternary(3, 9, (G, Kd, N))
+    got = _run_gather("wgrad", x, gather, div, b, cu, Kd, N, init)
+    g_ref = np.where((gather >= 0) & (gather < n_tok * div), gather, -1).astype(np.int32)
+    ref = oracle.group_gemm("wgrad", oracle.permute(x, g_ref, div), b, cu, "bf16", out=init)
+    assert (got == ref).all()
+
+
+@pytest.mark.parametrize("case", [c for c in SPLIT_CASES if c[0] == "fwd"])
+def test_group_gemm_gather_split_round(case):
+    """The gathered FWD with a workspace splits its last round like the plain FWD: bit-exact
+    on ternary inputs."""
+    m = mod()
+    _, G, M, Kd, N = case
+    rng = np.random.default_rng(M + Kd)
+    cu = _segments(rng, G, M - 2, empties=False)
+    n_tok, div = M // 3 + 1, 4
+    gather = _gather_entries(rng, cu, M, n_tok, div)
+    x = synth.to_bf16_bits(synth.host_ternary(M, 1, (n_tok, Kd)))
+    b = synth.to_bf16_bits(synth.host_ternary(M, 2, (G, Kd, N)))
+    ws = _gemm_ws(m, m.GEMM_FWD)
+    log(f"gemm gather split case={case}")
+    got = _run_gather("fwd", x, gather, div, b, cu, Kd, N, ws=ws)
+    torch.cuda.synchronize()
+    assert bool((ws != 0xFF).any()), "split round not taken"
+    ref = oracle.group_gemm("fwd", oracle.permute(x, gather, div), b, cu, "bf16")
+    rows = cu[-1]
+    assert (got[:rows] == ref[:rows]).all()
+
+
+@pytest.mark.parametrize("op", ["fwd", "wgrad"])
+def test_group_gemm_gather_matches_permute_then_gemm(op):
+    """Random bf16 data: the gathered GEMM gives the same bits as moe_permute followed by
+    moe_group_gemm (same products, same order), and is within tolerance of the oracle."""
+    m = mod()
+    G, M, Kd, N, n_tok, K = 12, 4000, 1024, 768, 900, 8
+    rng = np.random.default_rng(77)
+    cu = _segments(rng, G, M - 5)
+    gather = _gather_entries(rng, cu, M, n_tok, K)
+    x = synth.to_bf16_bits(synth.host_normal(5, 1, (n_tok, Kd)))
+    b = synth.to_bf16_bits(synth.host_normal(5, 2, (G, Kd, N) if op == "fwd" else (M, N),
+                                             0.05 if op == "fwd" else 1.0))
+    init = synth.host_normal(5, 9, (G, Kd, N)) if op == "wgrad" else None
+    ws = _gemm_ws(m, m.GEMM_FWD) if op == "fwd" else None
+    got = _run_gather(op, x, gather, K, b, cu, Kd, N, init, ws=ws)
+    # the unfused HIP path: permute into xp, then the grouped GEMM
+    d = m.dims(1, M // K, K, K, 0)      # the permute's S*K rows = the M rows here
+    xp = torch.empty((M, Kd), dtype=torch.bfloat16, device="cuda")
+    m.moe_permute(d, from_bits(x), _dev(gather), xp)
+    two = _run_gemm(op, bits(xp), b, cu, Kd, N, "bf16", init,
+                    ws=_gemm_ws(m, m.GEMM_FWD) if op == "fwd" else None)
+    rows = cu[-1]
+    if op == "wgrad":
+        assert (got.view(np.uint32) == two.view(np.uint32)).all()
+    else:
+        assert (got[:rows] == two[:rows]).all()
+    ref = oracle.group_gemm(op, oracle.permute(x, gather, K), b, cu, "bf16", out=init)
+    if op == "wgrad":
+        assert float(np.abs(got - ref).max() / np.abs(ref).max()) <= 1e-4
+    else:
+        check_close(got[:rows], ref[:rows], "bf16", what=f"gather {op}")
+
+
+@pytest.mark.parametrize("op", ["fwd", "wgrad"])
+def test_group_gemm_gather_source_above_4gb(op):
+    """Token rows more than 4 GB into the source buffer (past any 32-bit offset) are read
+    correctly: a 4.5 GB source, gather entries drawn mostly from its last 0.5 GB."""
+    G, M, Kd, N, K = 3, 600, 2048, 256, 2
+    n_tok = 1_100_000                                   # 1.1e6 rows x 4 KB = 4.5 GB
+    rng = np.random.default_rng(4)
+    cu = np.array([0, 250, 250, 597], np.int32)
+    toks = np.where(rng.random(M) < 0.8, rng.integers(1_050_000, n_tok, M),
+                    rng.integers(0, n_tok, M))
+    toks[0], toks[1] = n_tok - 1, 0                     # the very last and the first row
+    gather = (toks * K + rng.integers(0, K, M)).astype(np.int32)
+    gather[cu[-1]:] = -1
+    uniq = np.unique(toks)
+    rows_h = synth.to_bf16_bits(synth.host_ternary(11, 1, (uniq.size, Kd)))
+    x = torch.zeros((n_tok, Kd), dtype=torch.bfloat16, device="cuda")
+    x[torch.as_tensor(uniq, device="cuda")] = from_bits(rows_h)
+    remap = np.full(n_tok, -1, np.int64)
+    remap[uniq] = np.arange(uniq.size)
+    g_local = np.where(gather >= 0, remap[np.maximum(gather, 0) // K] * K + gather % K, -1)
+    b = synth.to_bf16_bits(synth.host_ternary(11, 2, (G, Kd, N) if op == "fwd" else (M, N)))
+    init = np.zeros((G, Kd, N), np.float32) if op == "wgrad" else None
+    log(f"gemm gather above 4 GB op={op}")
+    got = _run_gather(op, x, gather, K, b, cu, Kd, N, init)
+    ref = oracle.group_gemm(op, oracle.permute(rows_h, g_local.astype(np.int32), K), b, cu,
+                            "bf16", out=init)
+    del x
+    torch.cuda.empty_cache()
+    if op == "wgrad":
+        assert (got == ref).all()
+    else:
+        assert (got[:cu[-1]] == ref[:cu[-1]]).all()
+
+
 @pytest.mark.parametrize("op", ["fwd", "dgrad", "wgrad"])
 def test_group_gemm_f32(op):
     G, M, Kd, N = 18, 256, 256, 512

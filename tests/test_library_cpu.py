@@ -101,6 +101,32 @@ def test_host_validation_rejects_before_launch(mod):
     assert lib.moe_status_string(mod.MOE_ENOSPACE).startswith(b"workspace")
 
 
+def test_group_gemm_gather_host_checks(mod):
+    """moe_group_gemm_gather refuses DGRAD, fp32, an empty source, a zero divisor, null
+    pointers and a short workspace before anything is launched."""
+    lib = mod.library()
+    P = ctypes.c_void_p(16)  # never dereferenced
+    gg = lib.moe_group_gemm_gather
+    ok = (mod.GEMM_FWD, mod.BF16, 18, 256, 64, 64, P, 100, P, 2, P, P, P, None, 0, None)
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return gg(*a)
+    assert call(a0=mod.GEMM_DGRAD) == mod.MOE_EINVAL
+    assert call(a1=mod.F32) == mod.MOE_EINVAL
+    assert call(a7=0) == mod.MOE_EINVAL           # no source rows
+    assert call(a7=1 << 31) == mod.MOE_EINVAL     # source rows >= 2^31
+    assert call(a9=0) == mod.MOE_EINVAL           # gather divisor
+    assert call(a6=None) == mod.MOE_EINVAL
+    assert call(a8=None) == mod.MOE_EINVAL
+    assert call(a4=12) == mod.MOE_EINVAL          # Kd % 8
+    assert call(a2=0) == mod.MOE_EINVAL
+    need = mod.group_gemm_workspace_bytes(mod.GEMM_FWD)
+    assert call(a13=P, a14=need - 1) == mod.MOE_ENOSPACE
+    assert call(a0=mod.GEMM_WGRAD, a5=(1 << 20) + 8) == mod.MOE_EINVAL
+
+
 def test_plan_noalloc_host_checks(mod):
     """moe_plan_noalloc: bad arguments and plans whose scratch exceeds the static array are
     refused before anything touches the GPU; the binding's size constant is the header's."""
