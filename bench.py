@@ -176,6 +176,53 @@ def render_mfma(csv_path):
     print("\n".join(out))
 
 
+def render_stats(stats_csv, title, command):
+    """Markdown table of the library's kernels from a rocprofv3 --kernel-trace --stats run
+    (its kernel_stats.csv): calls, average / min / max duration, share of profiled GPU time."""
+    import csv
+    rows = [r for r in csv.DictReader(open(stats_csv)) if "moe::" in r["Name"]]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = [f"# rocprofv3 kernel stats: {title}", "", "Command (GPU box, `$REPO` = repository root):",
+           "", "```", command, "```", "",
+           "Kernels of the library (torch's input generation and copies are omitted):", "",
+           "| kernel | calls | avg us | min us | max us | % of profiled GPU time |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].split("(")[0].replace("void ", "")
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                   f"{float(r['Percentage']):.2f} |")
+    print("\n".join(out))
+
+
+def render_counters(csv_path, title, command):
+    """Markdown table of per-launch counter values (averaged over the probed step's launches of
+    each library kernel) from a rocprofv3 --pmc run of `bench.py --probe`."""
+    import csv
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(csv_path)):
+        vals[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[r["Dispatch_Id"]] = r["Kernel_Name"].split("(")[0].replace("void ", "")
+    counters = sorted({c for v in vals.values() for c in v})
+    per = collections.defaultdict(list)
+    for d in sorted(vals, key=int):
+        if "moe::" in names[d]:
+            per[names[d]].append(d)
+    out = [f"# rocprofv3 counters per launch: {title}", "", "Command (GPU box, `$REPO` = repository root):",
+           "", "```", command, "```", "",
+           "`--probe` runs one warm-up step, a 1 GiB copy, then one step; the values average each kernel's "
+           "launches in that second step.", "",
+           "| kernel | launches | " + " | ".join(f"`{c}`" for c in counters) + " |",
+           "|---|---|" + "---|" * len(counters)]
+    for n, ds in per.items():
+        ds = ds[len(ds) // 2:]
+        out.append(f"| `{n}` | {len(ds)} | " +
+                   " | ".join(f"{sum(vals[d][c] for d in ds) / len(ds):.0f}" for c in counters) + " |")
+    print("\n".join(out))
+
+
 def algorithmic_work(shape, n_slots_used, gated=False):
     """Minimum bytes (or flops) per launch of each kernel of the step.
 
@@ -518,10 +565,10 @@ def scale_sweep(args):
         layer, _, _, info = setup_layer(wl, t, args.rank, layer=layer,
                                         fused_gather=args.fused_gather)
         n = max(5, args.steps // 2)
-        run_steps(layer, 0, 2)
-        timer = EventTimer()
-        el = run_steps(layer, n, 0, timer)
+        el = run_steps(layer, n, 2)
         ms_t = el * 1000.0 / n
+        timer = EventTimer()
+        run_steps(layer, n, 0, timer)
         kern, _ = kernel_fracs(timer, layer.s, slots_used(layer), n)
         key = f"{info['maxvio']:.2f}"
         points[key] = {"target": t, "ms_per_step": round(ms_t, 4),
@@ -568,12 +615,20 @@ def main():
                     help="one warm-up step, a 1 GiB calibration copy, one step (for --pmc runs)")
     ap.add_argument("--render-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--render-mfma", metavar="COUNTER_CSV")
+    ap.add_argument("--render-stats", nargs=3, metavar=("STATS_CSV", "TITLE", "COMMAND"))
+    ap.add_argument("--render-counters", nargs=3, metavar=("COUNTER_CSV", "TITLE", "COMMAND"))
     args = ap.parse_args()
     if args.render_traffic:
         render_traffic(*args.render_traffic)
         return
     if args.render_mfma:
         render_mfma(args.render_mfma)
+        return
+    if args.render_stats:
+        render_stats(*args.render_stats)
+        return
+    if args.render_counters:
+        render_counters(*args.render_counters)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -589,6 +644,10 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     target = wl.maxvio_targets[-1] if wl.maxvio_targets[-1] is not None else None
+    # a forward-only step runs the permute fused into the up GEMM (measured faster: the
+    # step has no weight gradient, whose gathered form pays for scattered token rows)
+    if not wl.backward and args.activation == "identity":
+        args.fused_gather = True
     layer, idx, w, info = setup_layer(wl, target, args.rank, activation=args.activation,
                                       fused_gather=args.fused_gather)
     s = layer.s
@@ -603,8 +662,12 @@ def main():
         torch.cuda.synchronize()
         log("probe done")
         return
+    # the timed steps run bare; a second pass of as many steps times every launch with HIP
+    # events for the per-kernel figures (the events' own host cost would otherwise stretch
+    # the short launches of the small workloads)
+    elapsed = run_steps(layer, args.steps, args.warmup)
     timer = EventTimer()
-    elapsed = run_steps(layer, args.steps, args.warmup, timer)
+    run_steps(layer, args.steps, 1, timer)
     status = int(layer.status.item())
     if status != 0:
         log(f"WARNING: plan status {status} (bad ids / slot overflow)")
@@ -645,6 +708,24 @@ def main():
             log(f"graph replay: {g_ms:.3f} ms/step")
         except Exception as exc:  # reported, not fatal: the eager figures stand
             graph = {"error": str(exc)[:200]}
+
+    fused = None
+    if not args.main_only and not args.fused_gather and args.activation == "identity":
+        # the same step with the permute fused into the up projection (its forward GEMM and
+        # its weight gradient read the token rows through src_flat)
+        layer.fused_gather = True
+        el_f = run_steps(layer, args.steps, 2)
+        fwd_f = run_steps(layer, args.steps, 2, forward_only=True)
+        t_f = EventTimer()
+        run_steps(layer, args.steps, 1, t_f)
+        layer.fused_gather = False
+        kf, _ = kernel_fracs(t_f, s, n_slots, args.steps)
+        fused = {"ms_per_step": round(el_f * 1000.0 / args.steps, 4),
+                 "tokens_per_s": round(s.S * args.steps / el_f, 1),
+                 "forward_only_ms": round(fwd_f * 1000.0 / args.steps, 4),
+                 "forward_only_tokens_per_s": round(s.S * args.steps / fwd_f, 1),
+                 "kernels": {k: kf[k] for k in kf if k.endswith("_gather")}}
+        log(f"fused gather: {fused['ms_per_step']:.3f} ms/step, forward {fused['forward_only_ms']:.3f} ms")
 
     sweep = {}
     if not args.no_sweep and not args.main_only and wl.name in SWEEPS:
@@ -693,6 +774,7 @@ def main():
         "forward_only": None if fwd_ms is None else {"ms_per_step": round(fwd_ms, 4),
                                                      "tokens_per_s": round(s.S / (fwd_ms * 1e-3), 1)},
         "graph_replay": graph,
+        "fused_gather": fused,
         "data": "synthetic",
         "config": {"workload": wl.name, "R": s.R, "S": s.S, "K": s.K, "E": s.E, "B": s.B,
                    "H": s.H, "H_prime": s.Hp, "activation": args.activation,
