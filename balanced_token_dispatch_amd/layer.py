@@ -14,6 +14,8 @@ adjoint for the weights) -> down DGRAD -> down WGRAD -> up DGRAD (into rank
 r's slice of the all-ranks input-gradient buffer) -> up WGRAD -> un-permute
 reduce of the input gradients to the tokens (dispatch's adjoint) -> fold the
 replica rows of both weight gradients into their home experts.
+With ``plan_noalloc=True`` the plan runs on the library's static scratch
+(moe_plan_noalloc) instead of the workspace.
 With ``fused_gather=True`` (identity activation) there is no permute and no
 xp buffer: the up projection's FWD and WGRAD read their row operand straight
 from the token rows through src_flat (moe_group_gemm_gather), the permute
@@ -31,7 +33,7 @@ import torch
 from . import (GEMM_DGRAD, GEMM_FWD, GEMM_WGRAD, dims as _mk_dims, dispatch_layout_workspace_bytes,
                group_gemm_workspace_bytes, moe_combine, moe_combine_weight_grad,
                moe_dispatch_layout, moe_group_gemm, moe_group_gemm_gather, moe_group_gemm_swiglu,
-               moe_permute, moe_plan,
+               moe_permute, moe_plan, moe_plan_noalloc,
                moe_prefetch, moe_replica_grad_fold, moe_swiglu_backward, moe_unpermute_reduce,
                plan_words, plan_workspace_bytes)
 
@@ -57,13 +59,16 @@ class Shape:
 
 class LayerStep:
     def __init__(self, shape: Shape, rank: int = 0, dtype=torch.bfloat16, device="cuda",
-                 backward: bool = True, activation: str = "identity", fused_gather: bool = False):
+                 backward: bool = True, activation: str = "identity", fused_gather: bool = False,
+                 plan_noalloc: bool = False):
         s = shape
         if activation not in ("identity", "swiglu"):
             raise ValueError(f"activation {activation!r}")
         if fused_gather and (activation != "identity" or dtype != torch.bfloat16):
             raise ValueError("the gathered (permute-fused) up projection is bf16, identity only")
         self.fused_gather = fused_gather
+        # plan with the library's static scratch (moe_plan_noalloc) instead of the workspace
+        self.plan_noalloc = plan_noalloc
         self.s, self.rank, self.dtype, self.device = s, rank, dtype, device
         self.activation = activation
         # gated: the up projection has 2H' columns, (gate, up) pairs interleaved
@@ -132,8 +137,12 @@ class LayerStep:
 
     def forward(self, timer=None):
         s, r, c = self.s, self.rank, self._call
-        c(timer, "plan", moe_plan, self.d, self.topk_idx, self.counts, self.plan, self.status,
-          self.ws)
+        if self.plan_noalloc:
+            c(timer, "plan", moe_plan_noalloc, self.d, self.topk_idx, self.counts, self.plan,
+              self.status)
+        else:
+            c(timer, "plan", moe_plan, self.d, self.topk_idx, self.counts, self.plan,
+              self.status, self.ws)
         c(timer, "dispatch_layout", moe_dispatch_layout, self.d, r, self.topk_idx, self.plan,
           self.cu, self.dest, self.src, self.ws)
         c(timer, "prefetch", moe_prefetch, self.d, r, self.plan, self.w_up)

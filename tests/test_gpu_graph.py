@@ -3,9 +3,11 @@ step bit for bit.
 
 The library makes no allocation, memset, host synchronisation or host read inside its entry
 points, so a whole forward + backward step (plan, layout, prefetch, permute, grouped GEMMs,
-combine, the backward kernels and the fold) can be captured once and replayed.  The test
-replays the graph several times with eager steps and eager work in between and compares every
-output of every replay with the eager step's.
+combine, the backward kernels and the fold) can be captured once and replayed; also with the
+permute fused into the up GEMM and the plan on the library's static scratch (moe_plan_noalloc,
+whose device address is looked up before capture, on the eager step).  The test replays the
+graph several times with eager steps and eager work in between and compares every output of
+every replay with the eager step's.
 """
 import numpy as np
 import pytest
@@ -29,15 +31,20 @@ def _outputs(L):
          "dtopk_w": L.dtopk_w, "dw_up": L.dw_up, "dw_down": L.dw_down, "w_up": L.w_up}
     if L.activation == "swiglu":
         t["h"], t["dh"] = L.hpre, L.dh
-    return {k: v.clone() for k, v in t.items()}
+    return {k: v.clone() for k, v in t.items() if v is not None}
 
 
-@pytest.mark.parametrize("activation", ["identity", "swiglu"])
-def test_layer_step_graph_replay(activation):
+# (activation, permute fused into the up GEMM, plan on the library's static scratch)
+CASES = [("identity", False, False), ("swiglu", False, False), ("identity", True, True)]
+
+
+@pytest.mark.parametrize("activation,fused,noalloc", CASES)
+def test_layer_step_graph_replay(activation, fused, noalloc):
     from balanced_token_dispatch_amd.layer import LayerStep, Shape
     d = synth.Dims(R=8, S=512, K=4, E=32, B=4, H=256, Hp=192)
     idx, w = synth.routing(d, 1.0, 21)
-    L = LayerStep(Shape(d.R, d.S, d.K, d.E, d.B, d.H, d.Hp), rank=1, activation=activation)
+    L = LayerStep(Shape(d.R, d.S, d.K, d.E, d.B, d.H, d.Hp), rank=1, activation=activation,
+                  fused_gather=fused, plan_noalloc=noalloc)
     synth.fill_normal_(L.x_all, 1.0, 211)
     synth.fill_normal_(L.w_up, 0.05, 212)
     synth.fill_normal_(L.w_down, 0.05, 213)
@@ -84,4 +91,5 @@ def test_layer_step_graph_replay(activation):
         got = _outputs(L)
         for k in ref:
             assert torch.equal(got[k], ref[k]), f"eager after replay {rep}: {k} differs"
-        log(f"graph replay {rep} ({activation}) identical to the eager step")
+        log(f"graph replay {rep} ({activation}, fused={fused}, noalloc={noalloc}) identical "
+            f"to the eager step")
