@@ -43,6 +43,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int kMaxDim = 1 << 22;  // largest Kd and N (per-lane load offsets stay in 32 bits)
 constexpr int kMaxG = 1088;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
@@ -126,11 +127,46 @@ __device__ inline void dma_init(DmaOp &d, const uint16_t *base, long long bytes,
   }
 }
 
+// Byte count of an operand's buffer resource at K step kt: the bytes left from the step's
+// base, clamped to [0, kOOB], and 0 past the last step.  Worked out once per tile so that a K
+// step costs a few 32-bit scalar operations (the step's instructions share one wave's issue
+// slots with its MFMAs): the first `ksat` steps have more than kOOB bytes left; from then on
+// the count fits 31 bits and equals the low word of the byte count minus kt steps, in 32-bit
+// arithmetic (it never falls below -2^31: a tile ends within a step of its operand's end).
+struct DmaCount {
+  uint32_t lo;  // low 32 bits of the byte count at step 0
+  int ksat;     // steps whose count saturates at kOOB
+};
+
+__device__ inline DmaCount dma_count(long long bytes, long long step) {
+  DmaCount c;
+  c.lo = (uint32_t)bytes;
+  c.ksat = 0;
+  if (bytes >= kOOB) {
+    // operands over 2 GB only; the empty asm keeps the division's set-up from being hoisted
+    // out of the tile loop (where its registers would stay live for nothing)
+    asm volatile("" : "+s"(step));
+    c.ksat = (int)((bytes - kOOB) / step) + 1;
+  }
+  // the division may run on the vector unit; the count is wave-uniform and must stay in
+  // scalar registers (it becomes part of a buffer resource)
+  c.ksat = __builtin_amdgcn_readfirstlane(c.ksat);
+  return c;
+}
+
+__device__ inline int dma_bytes_at(const DmaCount &c, int step, int kt, int nk) {
+  int n = (int)(c.lo - (uint32_t)kt * (uint32_t)step);
+  n = n < 0 ? 0 : n;
+  n = kt < c.ksat ? kOOB : n;
+  return kt < nk ? n : 0;
+}
+
 // Buffer resource of K step kt of an operand (a zero-byte resource past the last step).
-__device__ inline __amdgpu_buffer_rsrc_t dma_rsrc(const DmaOp &d, int kt, int nk) {
-  const long long c0b = (long long)kt * d.step;
-  const long long rem = d.bytes - c0b;
-  return make_rsrc(d.base + c0b, (kt < nk && rem > 0) ? rem : 0);
+__device__ inline __amdgpu_buffer_rsrc_t dma_rsrc(const DmaOp &d, const DmaCount &c, int kt,
+                                                  int nk) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(d.base + (long long)kt * d.step),
+                                           (short)0, dma_bytes_at(c, (int)d.step, kt, nk),
+                                           0x00020000);
 }
 
 // This wave's load u of K step kt into the operand's LDS region at byte address `lds_op`
@@ -400,6 +436,7 @@ __device__ inline void read_frags(Frags<W> &f, const uint16_t *stage, int wi, in
 
 struct TileArgs {
   DmaOp a, b;
+  DmaCount ca, cb;    // byte counts of a and b (tile_mma works them out)
   int c_len, nk;
   uint32_t wave_off;  // this wave's 1-KB block offset within an operand tile (wave-uniform)
   GatherC gc;         // the row-side operand gathered from token rows (AG == 1)
@@ -414,9 +451,9 @@ template <class W, bool A_CONTIG, bool B_CONTIG, bool RAGGED, int AG>
 __device__ inline void dma_step(const uint16_t *lds, int stage, const TileArgs &ta,
                                 const GatherS &gs, int kt) {
   const uint32_t st = (uint32_t)(uintptr_t)(lds_vptr)(lds + stage * STAGE_ELEMS);
-  const __amdgpu_buffer_rsrc_t rb = dma_rsrc(ta.b, kt, ta.nk);
+  const __amdgpu_buffer_rsrc_t rb = dma_rsrc(ta.b, ta.cb, kt, ta.nk);
   if constexpr (AG == 0) {
-    const __amdgpu_buffer_rsrc_t ra = dma_rsrc(ta.a, kt, ta.nk);
+    const __amdgpu_buffer_rsrc_t ra = dma_rsrc(ta.a, ta.ca, kt, ta.nk);
 #pragma unroll
     for (int u = 0; u < W::blk; ++u)
       dma_one<W, A_CONTIG, RAGGED>(ta.a, ra, st, ta.wave_off, kt, ta.c_len, u);
@@ -450,13 +487,88 @@ __device__ inline void dma_step(const uint16_t *lds, int stage, const TileArgs &
 // the middle of step k follows every wave's wait for step k+1, which half B then reads.
 // The prologue issues steps 0-2 and waits for step 0.  Loads of steps past the last have
 // every offset out of range and write zeros into stages no later read uses.
-template <class W, bool A_CONTIG, bool B_CONTIG, bool RAGGED, int AG = 0>
-__device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta,
-                                f32x16 (&acc)[W::TM][W::TN]) {
+//
+// A wave issues at most one instruction per issue cycle of its SIMD, and an MFMA of this shape
+// keeps the matrix unit busy for 8 of them, so the scalar and address work between two MFMAs
+// stalls the unit once it exceeds 7 instructions.  The per-step work is therefore kept small
+// (byte counts in 32 bits, see DmaCount), and the 8-wave form, which has registers to spare,
+// runs the loop unrolled over the ring's four stages so that every LDS address of a step is a
+// constant offset (kstep with S >= 0); in the 4-wave form that unrolling runs out of registers,
+// so it computes the stage from k.
+template <class W, bool A_CONTIG, bool B_CONTIG, bool RAGGED, int AG, int S>
+__device__ __attribute__((always_inline)) inline void kstep(uint16_t *lds, const TileArgs &ta,
+                                                            f32x16 (&acc)[W::TM][W::TN],
+                                                            Frags<W> &F0, Frags<W> &F1,
+                                                            GatherS &gs, int k, int wi, int wj,
+                                                            int lane) {
   constexpr int TM = W::TM, TN = W::TN, NB = W::blk;
+  const int nk = ta.nk;
+  const int s0 = S >= 0 ? S : (k & 3);
+  const uint16_t *cur = lds + s0 * STAGE_ELEMS;
+  const uint16_t *nxt = lds + ((s0 + 1) & 3) * STAGE_ELEMS;
+  const uint32_t st = (uint32_t)(uintptr_t)(lds_vptr)(lds + ((s0 + 3) & 3) * STAGE_ELEMS);
+  __amdgpu_buffer_rsrc_t ra, rb;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < TM * TN; ++i) {  // half A
+    const int tm = i / TN, tn = i % TN;
+    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F0.b[tn], F0.a[tm], acc[tm][tn], 0,
+                                                          0, 0);
+    if (i < TM)
+      F1.a[i] = read_operand<A_CONTIG>(cur, wi, i, lane, 1);
+    else if (i < TM + TN)
+      F1.b[i - TM] = read_operand<B_CONTIG>(cur + OP_ELEMS, wj, i - TM, lane, 1);
+    if (AG == 0 && i == 1) ra = dma_rsrc(ta.a, ta.ca, k + 3, nk);
+    if (i == 2) rb = dma_rsrc(ta.b, ta.cb, k + 3, nk);
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (i == (u + 1) * TM * TN / (NB + 1)) {
+        if constexpr (AG == 0)
+          dma_one<W, A_CONTIG, RAGGED>(ta.a, ra, st, ta.wave_off, k + 3, ta.c_len, u);
+        else if constexpr (AG == 1)
+          gather_c_one<W>(ta.gc, st, ta.wave_off, k + 3, ta.c_len, u);
+        else
+          gather_s_one<W>(gs, st, ta.wave_off, u);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  waitcnt_vm<W::loads + NB>();
+  __syncthreads();
+  if constexpr (AG == 2) gather_s_fetch<W>(gs, k + 4);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < TM * TN; ++i) {  // half B
+    const int tm = i / TN, tn = i % TN;
+    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F1.b[tn], F1.a[tm], acc[tm][tn], 0,
+                                                          0, 0);
+    if (i < TM)
+      F0.a[i] = read_operand<A_CONTIG>(nxt, wi, i, lane, 0);
+    else if (i < TM + TN)
+      F0.b[i - TM] = read_operand<B_CONTIG>(nxt + OP_ELEMS, wj, i - TM, lane, 0);
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (i == (u + 1) * TM * TN / (NB + 1))
+        dma_one<W, B_CONTIG, RAGGED>(ta.b, rb, st + OP_ELEMS * 2, ta.wave_off, k + 3,
+                                     ta.c_len, u);
+    // gathered strided operand: addresses of step k+4 (issued in the next half A) from the
+    // entries fetched after this step's barrier, once this half's fragment reads are out
+    if constexpr (AG == 2) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (i == TM * TN - NB + u) gather_s_addr<W>(gs, k + 4, u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <class W, bool A_CONTIG, bool B_CONTIG, bool RAGGED, int AG = 0>
+__device__ inline void tile_mma(uint16_t *lds, TileArgs &ta, f32x16 (&acc)[W::TM][W::TN]) {
+  constexpr int TM = W::TM, TN = W::TN;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wi = (wid / W::N) * (32 * TM), wj = (wid % W::N) * (32 * TN);
   const int nk = ta.nk;
+  if constexpr (AG == 0) ta.ca = dma_count(ta.a.bytes, ta.a.step);
+  ta.cb = dma_count(ta.b.bytes, ta.b.step);
 #pragma unroll
   for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -480,61 +592,26 @@ __device__ inline void tile_mma(uint16_t *lds, const TileArgs &ta,
   waitcnt_vm<2 * W::loads>();
   __syncthreads();
   read_frags<W, A_CONTIG, B_CONTIG>(F0, lds, wi, wj, lane, 0);
-  for (int k = 0; k < nk; ++k) {
-    const uint16_t *cur = lds + (k & 3) * STAGE_ELEMS;
-    const uint16_t *nxt = lds + ((k + 1) & 3) * STAGE_ELEMS;
-    const uint32_t st = (uint32_t)(uintptr_t)(lds_vptr)(lds + ((k + 3) & 3) * STAGE_ELEMS);
-    __amdgpu_buffer_rsrc_t ra, rb;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < TM * TN; ++i) {  // half A
-      const int tm = i / TN, tn = i % TN;
-      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F0.b[tn], F0.a[tm], acc[tm][tn], 0,
-                                                            0, 0);
-      if (i < TM)
-        F1.a[i] = read_operand<A_CONTIG>(cur, wi, i, lane, 1);
-      else if (i < TM + TN)
-        F1.b[i - TM] = read_operand<B_CONTIG>(cur + OP_ELEMS, wj, i - TM, lane, 1);
-      if (AG == 0 && i == 1) ra = dma_rsrc(ta.a, k + 3, nk);
-      if (i == 2) rb = dma_rsrc(ta.b, k + 3, nk);
-#pragma unroll
-      for (int u = 0; u < NB; ++u)
-        if (i == (u + 1) * TM * TN / (NB + 1)) {
-          if constexpr (AG == 0)
-            dma_one<W, A_CONTIG, RAGGED>(ta.a, ra, st, ta.wave_off, k + 3, ta.c_len, u);
-          else if constexpr (AG == 1)
-            gather_c_one<W>(ta.gc, st, ta.wave_off, k + 3, ta.c_len, u);
-          else
-            gather_s_one<W>(gs, st, ta.wave_off, u);
-        }
-      __builtin_amdgcn_sched_barrier(0);
+  if constexpr (W::n == 4) {
+    for (int k = 0; k < nk; ++k)
+      kstep<W, A_CONTIG, B_CONTIG, RAGGED, AG, -1>(lds, ta, acc, F0, F1, gs, k, wi, wj, lane);
+  } else {
+    int k = 0;
+    for (; k + 4 <= nk; k += 4) {
+      kstep<W, A_CONTIG, B_CONTIG, RAGGED, AG, 0>(lds, ta, acc, F0, F1, gs, k, wi, wj, lane);
+      kstep<W, A_CONTIG, B_CONTIG, RAGGED, AG, 1>(lds, ta, acc, F0, F1, gs, k + 1, wi, wj, lane);
+      kstep<W, A_CONTIG, B_CONTIG, RAGGED, AG, 2>(lds, ta, acc, F0, F1, gs, k + 2, wi, wj, lane);
+      kstep<W, A_CONTIG, B_CONTIG, RAGGED, AG, 3>(lds, ta, acc, F0, F1, gs, k + 3, wi, wj, lane);
     }
-    waitcnt_vm<W::loads + NB>();
-    __syncthreads();
-    if constexpr (AG == 2) gather_s_fetch<W>(gs, k + 4);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < TM * TN; ++i) {  // half B
-      const int tm = i / TN, tn = i % TN;
-      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F1.b[tn], F1.a[tm], acc[tm][tn], 0,
-                                                            0, 0);
-      if (i < TM)
-        F0.a[i] = read_operand<A_CONTIG>(nxt, wi, i, lane, 0);
-      else if (i < TM + TN)
-        F0.b[i - TM] = read_operand<B_CONTIG>(nxt + OP_ELEMS, wj, i - TM, lane, 0);
-#pragma unroll
-      for (int u = 0; u < NB; ++u)
-        if (i == (u + 1) * TM * TN / (NB + 1))
-          dma_one<W, B_CONTIG, RAGGED>(ta.b, rb, st + OP_ELEMS * 2, ta.wave_off, k + 3,
-                                       ta.c_len, u);
-      // gathered strided operand: addresses of step k+4 (issued in the next half A) from the
-      // entries fetched after this step's barrier, once this half's fragment reads are out
-      if constexpr (AG == 2) {
-#pragma unroll
-        for (int u = 0; u < NB; ++u)
-          if (i == TM * TN - NB + u) gather_s_addr<W>(gs, k + 4, u);
+    if (k < nk) {  // the last nk % 4 steps, from stage 0
+      kstep<W, A_CONTIG, B_CONTIG, RAGGED, AG, 0>(lds, ta, acc, F0, F1, gs, k, wi, wj, lane);
+      if (k + 1 < nk) {
+        kstep<W, A_CONTIG, B_CONTIG, RAGGED, AG, 1>(lds, ta, acc, F0, F1, gs, k + 1, wi, wj,
+                                                    lane);
+        if (k + 2 < nk)
+          kstep<W, A_CONTIG, B_CONTIG, RAGGED, AG, 2>(lds, ta, acc, F0, F1, gs, k + 2, wi, wj,
+                                                      lane);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
   waitcnt_vm<0>();  // the trailing out-of-range loads land before the stages are reused
@@ -581,11 +658,13 @@ __device__ inline void dma_init64(DmaOp64 &d, const uint16_t *base, long long by
   }
 }
 
-// Buffer resource of stage kt (a zero-byte resource past the last stage).
-__device__ inline __amdgpu_buffer_rsrc_t dma_rsrc64(const DmaOp64 &d, int kt, int nk) {
-  const long long c0b = (long long)kt * BK64 * 2;
-  const long long rem = d.bytes - c0b;
-  return make_rsrc(d.base + c0b, (kt < nk && rem > 0) ? rem : 0);
+// Buffer resource of stage kt (a zero-byte resource past the last stage); c from
+// dma_count(d.bytes, BK64 * 2).
+__device__ inline __amdgpu_buffer_rsrc_t dma_rsrc64(const DmaOp64 &d, const DmaCount &c, int kt,
+                                                    int nk) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(d.base + (long long)kt * BK64 * 2),
+                                           (short)0, dma_bytes_at(c, BK64 * 2, kt, nk),
+                                           0x00020000);
 }
 
 template <class W, bool RAGGED>
@@ -639,9 +718,11 @@ __device__ inline void tile_mma64(uint16_t *lds, const TileArgs64 &ta,
   auto stage_addr = [&](int s) {
     return (uint32_t)(uintptr_t)(lds_vptr)(lds + (s & 1) * STAGE64_ELEMS);
   };
+  const DmaCount ca = dma_count(ta.a.bytes, BK64 * 2), cb = dma_count(ta.b.bytes, BK64 * 2);
   {
-    const __amdgpu_buffer_rsrc_t ra0 = dma_rsrc64(ta.a, 0, nk), rb0 = dma_rsrc64(ta.b, 0, nk);
-    const __amdgpu_buffer_rsrc_t ra1 = dma_rsrc64(ta.a, 1, nk);
+    const __amdgpu_buffer_rsrc_t ra0 = dma_rsrc64(ta.a, ca, 0, nk);
+    const __amdgpu_buffer_rsrc_t rb0 = dma_rsrc64(ta.b, cb, 0, nk);
+    const __amdgpu_buffer_rsrc_t ra1 = dma_rsrc64(ta.a, ca, 1, nk);
 #pragma unroll
     for (int u = 0; u < NB; ++u)
       dma_one64<W, RAGGED>(ta.a, ra0, stage_addr(0), ta.wave_off, 0, ta.c_len, u);
@@ -679,7 +760,7 @@ __device__ inline void tile_mma64(uint16_t *lds, const TileArgs64 &ta,
         else if (i < TM + TN)
           Fn.b[i - TM] = read_operand64(cur + OP64_ELEMS, wj, i - TM, lane, ks + 1);
         if (ks == 0) {
-          if (i == 1) rb = dma_rsrc64(ta.b, s + 1, nk);
+          if (i == 1) rb = dma_rsrc64(ta.b, cb, s + 1, nk);
 #pragma unroll
           for (int u = 0; u < NB; ++u)
             if (i == (u + 1) * TM * TN / (NB + 1))
@@ -701,7 +782,7 @@ __device__ inline void tile_mma64(uint16_t *lds, const TileArgs64 &ta,
         F0.a[i] = read_operand64(nxt, wi, i, lane, 0);
       else if (i < TM + TN)
         F0.b[i - TM] = read_operand64(nxt + OP64_ELEMS, wj, i - TM, lane, 0);
-      if (i == 1) ra = dma_rsrc64(ta.a, s + 2, nk);
+      if (i == 1) ra = dma_rsrc64(ta.a, ca, s + 2, nk);
 #pragma unroll
       for (int u = 0; u < NB; ++u)
         if (i == (u + 1) * TM * TN / (NB + 1))
@@ -1425,6 +1506,8 @@ extern "C" moe_status_t moe_group_gemm(moe_gemm_op op, moe_dtype dtype, int32_t 
   if (op != MOE_GEMM_FWD && op != MOE_GEMM_DGRAD && op != MOE_GEMM_WGRAD) return MOE_EINVAL;
   if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_EINVAL;
   if ((long long)M_total * (Kd > N ? Kd : N) >= (1LL << 40)) return MOE_EINVAL;
+  // the operand loads address a 256-row tile of either operand with 32-bit byte offsets
+  if (Kd > kMaxDim || N > kMaxDim) return MOE_EINVAL;
   // WGRAD's epilogue addresses a tile's fp32 rows with 32-bit buffer offsets (row * N * 4
   // plus an out-of-range marker for masked chunks), which must not wrap
   if (op == MOE_GEMM_WGRAD && N > (1 << 20)) return MOE_EINVAL;
@@ -1478,6 +1561,7 @@ extern "C" moe_status_t moe_group_gemm_swiglu(moe_dtype dtype, int32_t G, int32_
   if (dtype != MOE_BF16) return MOE_EINVAL;
   if (G < 1 || G > kMaxG || M_total < 0 || Kd < 8 || N < 16 || Kd % 8 || N % 16) return MOE_EINVAL;
   if ((long long)M_total * (Kd > N ? Kd : N) >= (1LL << 40)) return MOE_EINVAL;
+  if (Kd > kMaxDim || N > kMaxDim) return MOE_EINVAL;
   if (ws && ws_bytes < moe_group_gemm_workspace_bytes(MOE_GEMM_FWD, dtype)) return MOE_ENOSPACE;
   if (M_total == 0) return MOE_OK;
   // 8 waves: the gated epilogue needs the registers the 128x128 wave tile would take
@@ -1511,6 +1595,7 @@ extern "C" moe_status_t moe_group_gemm_gather(moe_gemm_op op, moe_dtype dtype, i
   if (G < 1 || G > kMaxG || M_total < 0 || Kd < 8 || N < 8 || Kd % 8 || N % 8) return MOE_EINVAL;
   if (src_rows < 1 || src_rows >= (1LL << 31) || gather_div < 1) return MOE_EINVAL;
   if ((long long)M_total * (Kd > N ? Kd : N) >= (1LL << 40)) return MOE_EINVAL;
+  if (Kd > kMaxDim || N > kMaxDim) return MOE_EINVAL;
   if (op == MOE_GEMM_WGRAD && N > (1 << 20)) return MOE_EINVAL;
   if (ws && ws_bytes < moe_group_gemm_workspace_bytes(op, dtype)) return MOE_ENOSPACE;
   if (M_total == 0) return MOE_OK;

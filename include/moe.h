@@ -217,7 +217,8 @@ moe_status_t moe_permute(const moe_dims *dims, moe_dtype dtype, int64_t width,
  *   DGRAD: a [M_total, N],  b = W [G, Kd, N]        -> out [M_total, Kd]
  *   WGRAD: a [M_total, Kd], b [M_total, N]          -> out fp32 [G, Kd, N], +=
  *   cu_seqlens [G+1] int32, non-decreasing, cu_seqlens[G] <= M_total.
- *   Kd % 8 == 0, N % 8 == 0; WGRAD: N <= 2^20 (else MOE_EINVAL).
+ *   Kd % 8 == 0, N % 8 == 0, Kd <= 2^22, N <= 2^22; WGRAD: N <= 2^20 (else
+ *   MOE_EINVAL).
  *   ws: optional device scratch (NULL: none) of at least
  *   moe_group_gemm_workspace_bytes(op, dtype) bytes, else MOE_ENOSPACE.  With
  *   it, bf16 FWD and DGRAD may split the contraction of the output tiles of

@@ -748,6 +748,78 @@ def test_group_gemm_gather_source_above_4gb(op):
 
 
 @pytest.mark.parametrize("op", ["fwd", "dgrad", "wgrad"])
+def test_group_gemm_operand_above_2gb(op):
+    """An operand that extends more than 2 GB past a tile's start: its buffer resources count
+    more bytes than a resource holds for the first K steps (the count saturates), then the
+    exact remainder, down to the zero fill past the contraction's end.  The 2 GB operand is
+    zero except for chosen rows (the first steps, the middle, the end), so the oracle needs
+    only those; ternary values keep every sum exact.
+      FWD:   W [1, 32768, 32776] (2.15 GB), nonzero contraction rows;
+      DGRAD: W [1, 16384, 65544] (2.15 GB), nonzero output rows (columns of the result);
+      WGRAD: a [262508, 4096] (2.15 GB), a 262444-row segment then a 64-row one, nonzero
+             rows at the long segment's start and end and all of the short one (an over-read
+             past the first segment's end would pick them up)."""
+    m = mod()
+    M = 300
+    rng = np.random.default_rng(21)
+    log(f"gemm operand above 2 GB op={op}")
+    if op == "fwd":
+        Kd, N = 32768, 32776
+        nz = np.unique(np.concatenate([np.arange(0, 40), np.arange(16370, 16410),
+                                       np.arange(Kd - 40, Kd), rng.integers(0, Kd, 100)]))
+        a = synth.to_bf16_bits(synth.host_ternary(21, 1, (M, Kd)))
+        w_nz = synth.to_bf16_bits(synth.host_ternary(21, 2, (nz.size, N)))
+        W = torch.zeros((1, Kd, N), dtype=torch.bfloat16, device="cuda")
+        W[0, torch.as_tensor(nz, device="cuda")] = from_bits(w_nz)
+        cu = np.array([0, M], np.int32)
+        out = poisoned((M, N), torch.bfloat16)
+        m.moe_group_gemm(m.GEMM_FWD, from_bits(a), W, _dev(cu), out, Kd, N)
+        got = bits(out)
+        del W
+        ref = oracle.group_gemm("fwd", np.ascontiguousarray(a[:, nz]), w_nz[None], cu, "bf16")
+        assert (got == ref).all()
+    elif op == "dgrad":
+        Kd, N = 16384, 65544
+        nz = np.unique(np.concatenate([np.arange(0, 64), np.arange(8000, 8064),
+                                       np.arange(Kd - 64, Kd), rng.integers(0, Kd, 64)]))
+        a = synth.to_bf16_bits(synth.host_ternary(21, 3, (M, N)))
+        w_nz = synth.to_bf16_bits(synth.host_ternary(21, 4, (nz.size, N)))
+        W = torch.zeros((1, Kd, N), dtype=torch.bfloat16, device="cuda")
+        W[0, torch.as_tensor(nz, device="cuda")] = from_bits(w_nz)
+        cu = np.array([0, M], np.int32)
+        out = poisoned((M, Kd), torch.bfloat16)
+        m.moe_group_gemm(m.GEMM_DGRAD, from_bits(a), W, _dev(cu), out, Kd, N)
+        got = bits(out)
+        del W
+        ref = oracle.group_gemm("dgrad", a, w_nz[None], cu, "bf16")
+        assert (got[:, nz] == ref).all()
+        rest = np.setdiff1d(np.arange(Kd), nz)
+        assert ((got[:, rest] & 0x7FFF) == 0).all(), "columns of zero weight rows are zero"
+    else:
+        Kd, N = 4096, 256
+        L0, L1 = 262444, 64
+        Mw = L0 + L1
+        nz0 = np.unique(np.concatenate([np.arange(0, 400), np.arange(L0 - 44, L0),
+                                        rng.integers(0, L0, 100)]))
+        rows = np.concatenate([nz0, np.arange(L0, Mw)])
+        a_nz = synth.to_bf16_bits(synth.host_ternary(21, 5, (rows.size, Kd)))
+        A = torch.zeros((Mw, Kd), dtype=torch.bfloat16, device="cuda")
+        A[torch.as_tensor(rows, device="cuda")] = from_bits(a_nz)
+        b = synth.to_bf16_bits(synth.host_ternary(21, 6, (Mw, N)))
+        cu = np.array([0, L0, Mw], np.int32)
+        init = synth.host_ternary(21, 7, (2, Kd, N))
+        out = _dev(init.astype(np.float32))
+        m.moe_group_gemm(m.GEMM_WGRAD, A, from_bits(b), _dev(cu), out, Kd, N)
+        got = out.cpu().numpy()
+        del A
+        cu_c = np.array([0, nz0.size, rows.size], np.int32)
+        ref = oracle.group_gemm("wgrad", a_nz, np.ascontiguousarray(b[rows]), cu_c, "bf16",
+                                out=init)
+        assert (got == ref).all()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("op", ["fwd", "dgrad", "wgrad"])
 def test_group_gemm_f32(op):
     G, M, Kd, N = 18, 256, 256, 512
     rng = np.random.default_rng(4)
