@@ -319,13 +319,17 @@ __device__ inline void gather_c_one(const GatherC &g, uint32_t lds_op, uint32_t 
 // the contraction runs over the segment's rows): each block of a K step covers two
 // contraction rows (lanes 0-31 and 32-63), so the rows, and their tokens, change every step.
 // Their gather entries are read with scalar loads (gather_s_fetch) right after a mid-step
-// barrier and turned into per-lane addresses (gather_s_addr) in the last two MFMA slots of
-// the same half step.  Scalar loads share the LDS reads' counter and return out of order, so
-// any wait while one is outstanding must wait for everything: issued where the counter has
-// just been drained and consumed after the half step's last fragment read, they cost neither
-// an early wait for the fragments nor arithmetic ahead of a step's first MFMA.
+// barrier; each lane then works out its own row's token and address with vector arithmetic
+// (gather_s_addr_part, two parts pinned to two MFMA slots): block 0's in the last two slots
+// of the same half step, block 1's in the next half step's first slots, ahead of its load.
+// Scalar loads share the LDS reads' counter and return out of order, so any wait while one is
+// outstanding must wait for everything: issued where the counter has just been drained and
+// consumed after the half step's last fragment read, they cost neither an early wait for the
+// fragments nor arithmetic ahead of a step's first MFMA.
 struct GatherS {
   GatherParams gp;
+  const int32_t *idx_seg;  // gather entries of the segment's rows (wave-uniform)
+  int row_w;         // 2 * wave index: this wave's first row of a K step's block
   int m0, len;       // first operand row and row count of the segment (wave-uniform)
   uint32_t e_lim;    // gather entries in [0, e_lim) name a token row
   const char *xcol;  // x + this lane's column byte offset
@@ -333,6 +337,7 @@ struct GatherS {
   int half;          // which of a block's two contraction rows this lane loads
   int e[kMaxBlk][2];          // gather entries of the rows of the next step to be issued
   const char *addr[kMaxBlk];  // this lane's load addresses for the step being issued
+  int tok[kMaxBlk], ok[kMaxBlk];  // between the two parts of gather_s_addr_part
 };
 
 // Block blk = u n + wid of a strided [BK][256] operand tile covers contraction rows 2 blk and
@@ -349,6 +354,8 @@ __device__ inline void gather_s_init(GatherS &g, const GatherParams &gp, int m0,
   g.gp = gp;
   g.m0 = __builtin_amdgcn_readfirstlane(m0);
   g.len = __builtin_amdgcn_readfirstlane(len);
+  g.idx_seg = gp.idx + g.m0;
+  g.row_w = __builtin_amdgcn_readfirstlane(2 * wid);
   const unsigned long long lim = (unsigned long long)gp.n_tok * gp.div;
   g.e_lim = lim < 0x80000000ull ? (uint32_t)lim : 0x80000000u;
   g.xcol = gp.x + (long long)col * 2;
@@ -358,8 +365,8 @@ __device__ inline void gather_s_init(GatherS &g, const GatherParams &gp, int m0,
 
 // First segment row of block u's pair of contraction rows in K step kt (wave-uniform).
 template <class W>
-__device__ inline int gather_s_row(int kt, int u) {
-  return kt * BK + 2 * (u * W::n + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+__device__ inline int gather_s_row(const GatherS &g, int kt, int u) {
+  return kt * BK + 2 * u * W::n + g.row_w;
 }
 
 // Scalar loads of the gather entries of K step kt's rows (rows past the segment read its
@@ -370,33 +377,40 @@ __device__ inline void gather_s_fetch(GatherS &g, int kt) {
   for (int u = 0; u < W::blk; ++u)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      g.e[u][h] = load_uniform(g.gp.idx + g.m0 + min(gather_s_row<W>(kt, u) + h, g.len - 1));
+      g.e[u][h] = load_uniform((const int32_t *)((const char *)g.idx_seg +
+                                                 (uint32_t)min(gather_s_row<W>(g, kt, u) + h,
+                                                               g.len - 1) * 4u));
 }
 
-// Byte offset from x of a contraction row's token (wave-uniform), or the offset that lands on
-// g_zeros for a row past the segment or one whose gather entry names no token row (zeros,
-// as the permute writes for such rows).  The empty asms keep the arithmetic in scalar
-// registers and free of branches: left alone, the compiler turns the choice into a branch
-// around the multiply, or selects the token per lane and multiplies in vector registers.
-__device__ inline long long gather_s_off(const GatherS &g, int e, bool in_seg) {
-  long long prod = (long long)((unsigned long long)(uint32_t)gather_div(e, g.gp) * g.gp.ld_bytes);
-  asm volatile("" : "+s"(prod));
-  long long o = ((uint32_t)e < g.e_lim && in_seg) ? prod : g.ozero;
-  asm volatile("" : "+s"(o));
-  return o;
+// This lane's address for load u of K step kt, from the entries gather_s_fetch(kt) read, in
+// two parts so that each fits beside one MFMA: the lane's token and whether its row is real
+// (part 0: a row past the segment, or an entry that names no token row, reads g_zeros, as
+// the permute writes zeros for such rows), then the address (part 1).  The empty asms pin
+// each part's arithmetic to its call site: left alone, the compiler gathers it ahead of a
+// step's first MFMAs.
+template <class W>
+__device__ inline void gather_s_addr_part(GatherS &g, int kt, int u, int part) {
+  if (part == 0) {
+    int e0 = g.e[u][0], e1 = g.e[u][1];
+    asm volatile("" : "+s"(e0), "+s"(e1));
+    const int e = g.half ? e1 : e0;
+    int tok = (int)(__umulhi((uint32_t)e << 1, g.gp.magic) >> g.gp.shift);
+    int ok = (uint32_t)e < g.e_lim && gather_s_row<W>(g, kt, u) + g.half < g.len;
+    asm volatile("" : "+v"(tok), "+v"(ok));
+    g.tok[u] = tok;
+    g.ok[u] = ok;
+  } else {
+    int tok = g.tok[u], ok = g.ok[u];
+    asm volatile("" : "+v"(tok), "+v"(ok));
+    const char *p = g.xcol + (unsigned long long)(uint32_t)tok * g.gp.ld_bytes;
+    g.addr[u] = ok ? p : g.xcol + g.ozero;
+  }
 }
 
-// Address of this lane's load u of K step kt from the entries gather_s_fetch(kt) read.  The
-// entries pass through an empty asm first, so none of the arithmetic can be scheduled ahead
-// of the call's place.
 template <class W>
 __device__ inline void gather_s_addr(GatherS &g, int kt, int u) {
-  int e0 = g.e[u][0], e1 = g.e[u][1];
-  asm volatile("" : "+s"(e0), "+s"(e1));
-  const int c0 = gather_s_row<W>(kt, u);
-  const long long o0 = gather_s_off(g, e0, c0 < g.len);
-  const long long o1 = gather_s_off(g, e1, c0 + 1 < g.len);
-  g.addr[u] = g.xcol + (g.half ? o1 : o0);
+  gather_s_addr_part<W>(g, kt, u, 0);
+  gather_s_addr_part<W>(g, kt, u, 1);
 }
 
 template <class W>
@@ -518,6 +532,13 @@ __device__ __attribute__((always_inline)) inline void kstep(uint16_t *lds, const
       F1.a[i] = read_operand<A_CONTIG>(cur, wi, i, lane, 1);
     else if (i < TM + TN)
       F1.b[i - TM] = read_operand<B_CONTIG>(cur + OP_ELEMS, wj, i - TM, lane, 1);
+    // gathered strided operand: the other blocks' addresses of step k+3 (block 0's were
+    // formed at the end of the previous step), ahead of their loads
+    if constexpr (AG == 2) {
+      static_assert(AG != 2 || NB == 2, "the gathered strided operand has two blocks per wave");
+      if (i == 1) gather_s_addr_part<W>(gs, k + 3, 1, 0);
+      if (i == 3) gather_s_addr_part<W>(gs, k + 3, 1, 1);
+    }
     if (AG == 0 && i == 1) ra = dma_rsrc(ta.a, ta.ca, k + 3, nk);
     if (i == 2) rb = dma_rsrc(ta.b, ta.cb, k + 3, nk);
 #pragma unroll
@@ -553,9 +574,8 @@ __device__ __attribute__((always_inline)) inline void kstep(uint16_t *lds, const
     // gathered strided operand: addresses of step k+4 (issued in the next half A) from the
     // entries fetched after this step's barrier, once this half's fragment reads are out
     if constexpr (AG == 2) {
-#pragma unroll
-      for (int u = 0; u < NB; ++u)
-        if (i == TM * TN - NB + u) gather_s_addr<W>(gs, k + 4, u);
+      if (i == TM * TN - 2) gather_s_addr_part<W>(gs, k + 4, 0, 0);
+      if (i == TM * TN - 1) gather_s_addr_part<W>(gs, k + 4, 0, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
