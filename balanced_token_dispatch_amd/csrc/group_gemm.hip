@@ -723,7 +723,9 @@ struct TileArgs64 {
 // everywhere (the barrier waits for this wave's LDS reads); sub-step 3 reads stage s+1's first
 // fragments and issues the row-side loads of stage s+2 into stage s's buffer.  The prologue
 // issues stage 0 and the row side of stage 1 and waits for stage 0.  Loads of stages past the
-// last write zeros into buffers no later read uses.
+// last write zeros into buffers no later read uses.  The buffer resources of stage s+2 are
+// built in sub-steps 1 (row side) and 2 (column side, after stage s's last column-side load),
+// whose MFMA slots have room for them (see tile_mma on issue slots).
 template <class W, bool RAGGED>
 __device__ inline void tile_mma64(uint16_t *lds, const TileArgs64 &ta,
                                   f32x16 (&acc)[W::TM][W::TN]) {
@@ -761,10 +763,11 @@ __device__ inline void tile_mma64(uint16_t *lds, const TileArgs64 &ta,
   for (int t = 0; t < TM; ++t) F0.a[t] = read_operand64(lds, wi, t, lane, 0);
 #pragma unroll
   for (int t = 0; t < TN; ++t) F0.b[t] = read_operand64(lds + OP64_ELEMS, wj, t, lane, 0);
+  __amdgpu_buffer_rsrc_t rb = dma_rsrc64(ta.b, cb, 1, nk);
   for (int s = 0; s < nk; ++s) {
     const uint16_t *cur = lds + (s & 1) * STAGE64_ELEMS;
     const uint16_t *nxt = lds + ((s + 1) & 1) * STAGE64_ELEMS;
-    __amdgpu_buffer_rsrc_t rb, ra;
+    __amdgpu_buffer_rsrc_t ra;
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {  // sub-steps 0..2
       Frags<W> &Fc = (ks & 1) ? F1 : F0;
@@ -779,8 +782,21 @@ __device__ inline void tile_mma64(uint16_t *lds, const TileArgs64 &ta,
           Fn.a[i] = read_operand64(cur, wi, i, lane, ks + 1);
         else if (i < TM + TN)
           Fn.b[i - TM] = read_operand64(cur + OP64_ELEMS, wj, i - TM, lane, ks + 1);
+        // the resources of the next loads, in slots with room (empty asms pin them there:
+        // left alone, the compiler moves the arithmetic ahead of the stage's first MFMAs)
+        if (ks == 1 && i == TM * TN - 4) {
+          int kk = s + 2;
+          asm volatile("" : "+s"(kk));
+          ra = dma_rsrc64(ta.a, ca, kk, nk);
+          asm volatile("" : "+s"(ra));
+        }
+        if (ks == 2 && i == TM * TN - 4) {  // after this stage's last column-side load
+          int kk = s + 2;
+          asm volatile("" : "+s"(kk));
+          rb = dma_rsrc64(ta.b, cb, kk, nk);
+          asm volatile("" : "+s"(rb));
+        }
         if (ks == 0) {
-          if (i == 1) rb = dma_rsrc64(ta.b, cb, s + 1, nk);
 #pragma unroll
           for (int u = 0; u < NB; ++u)
             if (i == (u + 1) * TM * TN / (NB + 1))
@@ -802,11 +818,11 @@ __device__ inline void tile_mma64(uint16_t *lds, const TileArgs64 &ta,
         F0.a[i] = read_operand64(nxt, wi, i, lane, 0);
       else if (i < TM + TN)
         F0.b[i - TM] = read_operand64(nxt + OP64_ELEMS, wj, i - TM, lane, 0);
-      if (i == 1) ra = dma_rsrc64(ta.a, ca, s + 2, nk);
 #pragma unroll
       for (int u = 0; u < NB; ++u)
         if (i == (u + 1) * TM * TN / (NB + 1))
           dma_one64<W, RAGGED>(ta.a, ra, stage_addr(s + 2), ta.wave_off, s + 2, ta.c_len, u);
+
       __builtin_amdgcn_sched_barrier(0);
     }
   }
