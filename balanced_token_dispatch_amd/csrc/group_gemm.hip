@@ -21,7 +21,9 @@
 //     strided (the weight in FWD, both operands in WGRAD) with the
 //     transposing ds_read_b64_tr_b16;
 //   * interleaved K loop: each wave issues one fragment read or load behind
-//     each MFMA (see tile_mma);
+//     each MFMA, and the per-step scalar work is kept small enough to fit the
+//     issue cycles an MFMA leaves (see tile_mma; the 8-wave loop runs
+//     unrolled over the ring's stages);
 //   * the MFMA is issued as (column-side x row-side) so each lane ends with
 //     4 consecutive output columns; output tiles leave through LDS so that
 //     global memory sees whole rows (bf16 stores; WGRAD's fp32
