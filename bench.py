@@ -81,11 +81,17 @@ COPY_BYTES = 1 << 30          # calibration copy: reads and writes exactly this 
 
 
 def source_hash(kernel):
+    """sha256 of the kernel's source files with comments and blank space removed, so that a
+    change to the comments alone keeps the recorded counters valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel][1]:
-        with open(os.path.join(ROOT, "balanced_token_dispatch_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "balanced_token_dispatch_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
