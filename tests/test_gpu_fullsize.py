@@ -44,6 +44,19 @@ class HostWeights:
         return self.cache[rho]
 
 
+def sum_abs_products(y, dest, dout, rank, S, K, tokens):
+    """[tokens, K]: sum_h |dout[s, h] * y[row of copy (rank, s, k), h]| of bf16 rows."""
+    out = np.zeros((len(tokens), K))
+    dp = np.asarray(dest).reshape(-1)
+    for t, s_ in enumerate(tokens):
+        g = np.abs(oracle.bf16_bits_to_f64(dout[int(s_)]))
+        for k in range(K):
+            dd = int(dp[(rank * S + int(s_)) * K + k])
+            if dd >= 0:
+                out[t, k] = float(np.dot(g, np.abs(oracle.bf16_bits_to_f64(y[dd]))))
+    return out
+
+
 def compact_cu(seg, G):
     counts = np.bincount(np.asarray(seg, np.int64), minlength=G)
     return np.concatenate([[0], np.cumsum(counts)])
@@ -188,7 +201,20 @@ def test_full_size_step(name, target):
     dest_l[copies] = np.arange(copies.size)          # need[i] is the row of copies[i]
     out_ref = oracle.combine(y_tab, dest_l, w, rank, S, K, "bf16", tokens=tok_s)
     check_close(host_rows(L.out, tok_s), out_ref, "bf16", what="combine tokens")
-    log("  forward sampled rows within tolerance")
+    # and up to 128 tokens none of whose copies lands on rank 0: every row they gather is a
+    # peer's staged row (a generated input)
+    dest3 = dest.reshape(d.R, S, K)[rank]
+    far = np.flatnonzero(((dest3 >= rank * SK) & (dest3 < (rank + 1) * SK)).sum(axis=1) == 0)
+    tok_z = np.sort(rng.permutation(far)[:128]).tolist()
+    need_z = dest3[tok_z].reshape(-1)
+    copies_z = ((rank * S + np.array(tok_z, np.int64))[:, None] * K
+                + np.arange(K)[None, :]).reshape(-1)
+    dest_z = np.full(dest.size, -1, np.int64)
+    dest_z[copies_z] = np.where(need_z >= 0, np.arange(copies_z.size), -1)
+    yz = host_rows(L.y_all, np.maximum(need_z, 0))
+    out_z = oracle.combine(yz, dest_z, w, rank, S, K, "bf16", tokens=tok_z)
+    check_close(host_rows(L.out, tok_z), out_z, "bf16", what="combine, tokens gathering staged rows")
+    log(f"  forward sampled rows within tolerance; combine of {len(tok_s)} + {len(tok_z)} tokens")
 
     # --- backward: weighted permute, down dgrad/wgrad, up dgrad/wgrad, fold
     moe_permute(L.d, L.dout_all, L.src, L.dy, L.topk_w.view(-1))
@@ -246,24 +272,57 @@ def test_full_size_step(name, target):
     assert np.abs(got3 - ent2).max() <= 1e-3 * max(1.0, np.abs(ent2).max()), (got3, ent2)
     del dw_up_g
     log(f"  wgrad entries of segment {rho} ({n_seg} rows) within tolerance (also gathered)")
-    # router-weight gradient and un-permute reduce of the sampled tokens, on the rows the
-    # GPU produced (rank 0's expert outputs and input gradients, the peers' staged rows)
+    # router-weight gradient and un-permute reduce.  Tokens none of whose copies lands on rank
+    # 0 read only the peers' staged rows (generated inputs): the oracle takes those rows and the
+    # GPU must match it within the summation bound.  The sampled tokens with copies on rank 0
+    # read rank 0's expert outputs and input gradients, which the oracle recomputes by its own
+    # chain (x -> z -> y above; dOut -> dy -> dz -> dxp here); the GPU's chain rounds those rows
+    # on its own, so there the check is normwise.
     moe_combine_weight_grad(L.d, rank, L.y_all, L.dest, L.dout_all[rank * S:(rank + 1) * S],
                             L.dtopk_w)
     moe_unpermute_reduce(L.d, rank, L.dxp_all, L.dest, L.dx)
     torch.cuda.synchronize()
-    y_gpu = host_rows(L.y_all, need)
+    dw_all = L.dtopk_w.view(S, K)
+    # (a) staged rows only
+    gz = np.zeros((S, H), np.uint16)
+    gz[tok_z] = host_rows(L.dout_all, rank * S + np.array(tok_z))
+    dwz_ref = oracle.combine_weight_grad(yz, dest_z, gz, rank, S, K, "bf16", tokens=tok_z)
+    dwz_got = dw_all[torch.as_tensor(tok_z, device="cuda")].cpu().numpy()
+    bound = router_grad_bound(yz, dest_z, gz, rank, S, K, "bf16", H, tokens=tok_z)
+    err = np.abs(dwz_got.astype(np.float64) - dwz_ref.astype(np.float64))
+    assert (err <= bound + np.abs(dwz_ref) * 2.0 ** -24).all(), "router-weight gradient, staged rows"
+    dxz_ref = oracle.unpermute_reduce(host_rows(L.dxp_all, np.maximum(need_z, 0)), dest_z, rank,
+                                      S, K, "bf16", tokens=tok_z)
+    check_close(host_rows(L.dx, tok_z), dxz_ref, "bf16", what="un-permute reduce, staged rows")
+    # (b) tokens with copies on rank 0, rank 0's rows from the oracle's chain
+    dxp_tab = host_rows(L.dxp_all, need)       # staged rows of other ranks: generated inputs
+    for k_, dd in enumerate(need):
+        if rank * SK <= dd < (rank + 1) * SK:
+            r_ = dd - rank * SK
+            rho = int(np.searchsorted(cu, r_, side="right") - 1)
+            gr = host_rows(L.dout_all, [src[r_] // K])
+            dyr = oracle.permute(gr, np.array([src[r_] % K], np.int32), K,
+                                 row_scale=np.where(np.arange(K) == src[r_] % K,
+                                                    w_flat[src[r_]], 0).astype(np.float32))
+            cu1 = compact_cu([rho], G)
+            _, dzr = oracle.group_gemm_rows("dgrad", dyr, Wd, cu1, [0])
+            _, dxr = oracle.group_gemm_rows("dgrad", dzr, Wu, cu1, [0])
+            dxp_tab[k_] = dxr[0]
     g_full = np.zeros((S, H), np.uint16)
     g_full[tok_s] = host_rows(L.dout_all, rank * S + np.array(tok_s))
-    dw_ref = oracle.combine_weight_grad(y_gpu, dest_l, g_full, rank, S, K, "bf16", tokens=tok_s)
-    dw_got = L.dtopk_w.view(S, K)[torch.as_tensor(tok_s, device="cuda")].cpu().numpy()
-    bound = router_grad_bound(y_gpu, dest_l, g_full, rank, S, K, "bf16", H, tokens=tok_s)
+    dw_ref = oracle.combine_weight_grad(y_tab, dest_l, g_full, rank, S, K, "bf16", tokens=tok_s)
+    dw_got = dw_all[torch.as_tensor(tok_s, device="cuda")].cpu().numpy()
+    # the GPU's y rows on rank 0 may differ from the oracle's by one bf16 unit (at most 2^-7
+    # of the value) in any element
+    gy = sum_abs_products(y_tab, dest_l, g_full, rank, S, K, tok_s)
+    bound = router_grad_bound(y_tab, dest_l, g_full, rank, S, K, "bf16", H, tokens=tok_s)
     err = np.abs(dw_got.astype(np.float64) - dw_ref.astype(np.float64))
-    assert (err <= bound + np.abs(dw_ref) * 2.0 ** -24).all(), (dw_got, dw_ref)
-    dx_ref = oracle.unpermute_reduce(host_rows(L.dxp_all, need), dest_l, rank, S, K, "bf16",
-                                     tokens=tok_s)
-    check_close(host_rows(L.dx, tok_s), dx_ref, "bf16", what="un-permute reduce tokens")
-    log(f"  router-weight gradient and un-permute reduce of {len(tok_s)} tokens within tolerance")
+    assert (err <= bound + gy * 2.0 ** -7).all(), (dw_got, dw_ref)
+    dx_ref = oracle.unpermute_reduce(dxp_tab, dest_l, rank, S, K, "bf16", tokens=tok_s)
+    check_close(host_rows(L.dx, tok_s), dx_ref, "bf16", min_identical=0.0,
+                what="un-permute reduce tokens")
+    log(f"  router-weight gradient and un-permute reduce of {len(tok_z)} + {len(tok_s)} tokens "
+        f"within tolerance")
     # fold: home rows gain the slot rows, slot rows end zero (bitwise, on a sampled column block)
     cols = slice(0, 4096)
     before = {int(e): (L.dw_up[e].view(-1)[cols].cpu().numpy(),
