@@ -951,8 +951,11 @@ def test_swiglu_backward(dtype):
 
 
 def test_gated_layer_step_against_oracle():
-    """Tiny gated layer on rank 0: dispatch, gated up, down, combine, and the backward through
-    the gated unit (down DGRAD, swiglu backward, up DGRAD, both WGRADs), stage by stage."""
+    """Tiny gated layer on rank 0: dispatch, gated up, down, and the backward through the gated
+    unit (down DGRAD, swiglu backward, up DGRAD, up WGRAD), each stage against the oracle's own
+    chain from the generated inputs (no GPU output is fed to the oracle).  The chained stages
+    carry the earlier stages' bf16 roundings, so they are checked normwise (2e-2) without a
+    floor on bit-identical elements."""
     R, S, K, E, B, H, Hp = 4, 96, 2, 16, 2, 64, 48
     idx, pl = _plan_for(R, S, K, E, B, 33)
     m = mod()
@@ -983,9 +986,8 @@ def test_gated_layer_step_against_oracle():
     z_r, h_r = oracle.group_gemm_swiglu(xp_r, Wu_r, cu, "bf16")
     check_close(bits(hpre), h_r, "bf16", what="gated layer pre-activation")
     check_close(bits(z), z_r, "bf16", min_identical=0.95, what="gated layer z")
-    # downstream stages take the GPU's own z so each comparison tests one kernel
-    y_r = oracle.group_gemm("fwd", bits(z), Wd_r, cu, "bf16")
-    check_close(bits(y), y_r, "bf16", what="gated layer down projection")
+    y_r = oracle.group_gemm("fwd", z_r, Wd_r, cu, "bf16")
+    check_close(bits(y), y_r, "bf16", min_identical=0.0, what="gated layer down projection")
     dy = poisoned((SK, H), torch.bfloat16)
     m.moe_permute(d, from_bits(dout), _dev(src), dy, row_scale=_dev(w))
     dz = poisoned((SK, Hp), torch.bfloat16)
@@ -1000,10 +1002,12 @@ def test_gated_layer_step_against_oracle():
     assert (bits(dy) == dy_r).all()
     dz_r = oracle.group_gemm("dgrad", dy_r, Wd_r, cu, "bf16")
     check_close(bits(dz), dz_r, "bf16", what="gated layer down dgrad")
-    dh_r = oracle.swiglu_backward(bits(dz), bits(hpre), "bf16")
-    check_close(bits(dh), dh_r, "bf16", min_identical=0.95, what="gated layer swiglu backward")
-    dxp_r = oracle.group_gemm("dgrad", bits(dh), Wu_r, cu, "bf16")
-    check_close(bits(dxp), dxp_r, "bf16", what="gated layer up dgrad")
-    dWu_r = oracle.group_gemm("wgrad", xp_r, bits(dh), cu, "bf16",
+    dh_r = oracle.swiglu_backward(dz_r, h_r, "bf16")
+    check_close(bits(dh), dh_r, "bf16", min_identical=0.0, what="gated layer swiglu backward")
+    dxp_r = oracle.group_gemm("dgrad", dh_r, Wu_r, cu, "bf16")
+    check_close(bits(dxp), dxp_r, "bf16", min_identical=0.0, what="gated layer up dgrad")
+    dWu_r = oracle.group_gemm("wgrad", xp_r, dh_r, cu, "bf16",
                               out=np.zeros((G, H, 2 * Hp), np.float32))
-    check_close(dWu.cpu().numpy(), dWu_r, "f32", tol=1e-4, what="gated layer up wgrad")
+    # fp32 output, but its row operand dh went through the bf16 chain: the bf16 tolerance
+    check_close(dWu.cpu().numpy(), dWu_r, "f32", tol=2e-2, min_identical=0.0,
+                what="gated layer up wgrad")
