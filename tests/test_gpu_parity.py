@@ -121,6 +121,51 @@ def test_plan_layout_relay(case):
         check_plan_layout(gp, idx, r, pl)
 
 
+def test_plan_layout_relay_seeded_overflows():
+    """Every walk overflow of the oracle's seeded medium-routing set (4-8 ranks, 1-4 experts
+    per rank, B = 1..3; the set the CPU test pins against mixed-integer feasibility), solved or
+    not, and of 300 more routings of 6-16 ranks: the GPU plan and layout match the oracle bit for
+    bit (first and last rank of the first set, rank 0 of the second)."""
+    from test_oracle_plan import random_routing
+    n = 0
+    for seed in range(60):
+        rng = np.random.default_rng(10_000 + seed)
+        R = int(rng.integers(4, 9))
+        E_loc = int(rng.choice([1, 2, 4]))
+        E = R * E_loc
+        K = int(rng.integers(1, min(E, 4) + 1))
+        S = int(rng.integers(2, 32))
+        idx = random_routing(rng, R, S, K, E, skew=float(rng.choice([0.5, 1.0, 2.0, 5.0])))
+        for B in (1, 2, 3):
+            pl = oracle.plan(idx, E, B)
+            if pl.max_needed <= B:
+                continue
+            n += 1
+            gp = GpuPlan(R, S, K, E, B)
+            for r in (0, R - 1):
+                gp.run(_dev(idx), r)
+                check_plan_layout(gp, idx, r, pl)
+    # and 300 routings of 6-16 ranks with stronger skew
+    for seed in range(300):
+        rng = np.random.default_rng(50_000 + seed)
+        R = int(rng.integers(6, 17))
+        E_loc = int(rng.choice([1, 2, 4]))
+        E = R * E_loc
+        K = int(rng.integers(1, min(E, 6) + 1))
+        S = int(rng.integers(2, 40))
+        idx = random_routing(rng, R, S, K, E, skew=float(rng.choice([1.0, 2.0, 5.0, 10.0])))
+        for B in (1, 2):
+            pl = oracle.plan(idx, E, B)
+            if pl.max_needed <= B:
+                continue
+            n += 1
+            gp = GpuPlan(R, S, K, E, B)
+            gp.run(_dev(idx), 0)
+            check_plan_layout(gp, idx, 0, pl)
+    log(f"relay: {n} seeded overflows bit-exact")
+    assert n >= 400
+
+
 @pytest.mark.parametrize("B", [1, 2])
 def test_plan_layout_relay_chain(B):
     """Five donors with excess 1 and one receiver with deficit 5: chains of relays (B=2) and
