@@ -182,6 +182,72 @@ def render_mfma(csv_path):
     print("\n".join(out))
 
 
+def render_stalls(*csv_paths):
+    """Summarise rocprofv3 --pmc runs of `bench.py --probe` on the GEMM launches of the probed
+    step: wave states, the vector-memory pipeline (TA, TD, TCP, L2 requests) and LDS.  Each
+    figure is computed from whichever run holds its counters.  SQ, TA, TD and TCP values arrive
+    summed over the chip's shader engines or CUs; the SQ wave counters are in units of 4 clocks
+    per wave; clocks per launch are GRBM_GUI_ACTIVE of one XCD (the run's sum over 8)."""
+    import csv
+    import collections
+
+    def load(path):
+        vals = collections.defaultdict(lambda: collections.defaultdict(float))
+        names = {}
+        for r in csv.DictReader(open(path)):
+            vals[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        return vals, names
+
+    cus = 256
+    clk = lambda v: v["GRBM_GUI_ACTIVE"] / 8
+    figures = [  # (column, counters needed, value per launch, format)
+        ("waves per CU", ("SQ_WAVE_CYCLES",), lambda v: 4 * v["SQ_WAVE_CYCLES"] / clk(v) / cus, "{:.2f}"),
+        ("dependency wait, % of wave time", ("SQ_WAIT_ANY",),
+         lambda v: 100 * v["SQ_WAIT_ANY"] / v["SQ_WAVE_CYCLES"], "{:.1f}"),
+        ("issue wait, %", ("SQ_WAIT_INST_ANY",),
+         lambda v: 100 * v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"], "{:.1f}"),
+        ("of it LDS, %", ("SQ_WAIT_INST_LDS",),
+         lambda v: 100 * v["SQ_WAIT_INST_LDS"] / v["SQ_WAVE_CYCLES"], "{:.1f}"),
+        ("VMEM instruction latency, clk", ("VmemLatency",), lambda v: v["VmemLatency"], "{:.0f}"),
+        ("L2 read latency at the TCP, clk", ("TCP_TCC_READ_REQ_LATENCY_sum",),
+         lambda v: v["TCP_TCC_READ_REQ_LATENCY_sum"] / v["TCP_TCC_READ_REQ_sum"], "{:.0f}"),
+        ("L2 read requests, M", ("TCP_TCC_READ_REQ_sum",),
+         lambda v: v["TCP_TCC_READ_REQ_sum"] / 1e6, "{:.1f}"),
+        ("TA busy, % of CU clocks", ("TA_TA_BUSY_sum",),
+         lambda v: 100 * v["TA_TA_BUSY_sum"] / clk(v) / cus, "{:.1f}"),
+        ("TA address FIFO full, %", ("SQ_VMEM_TA_ADDR_FIFO_FULL",),
+         lambda v: 100 * v["SQ_VMEM_TA_ADDR_FIFO_FULL"] / clk(v) / cus, "{:.1f}"),
+        ("TD busy, %", ("TD_TD_BUSY_sum",), lambda v: 100 * v["TD_TD_BUSY_sum"] / clk(v) / cus, "{:.1f}"),
+        ("TCP waiting on L2 data, %", ("TCP_PENDING_STALL_CYCLES_sum",),
+         lambda v: 100 * v["TCP_PENDING_STALL_CYCLES_sum"] / clk(v) / cus, "{:.1f}"),
+        ("LDS busy, %", ("SQ_LDS_IDX_ACTIVE",),
+         lambda v: 100 * v["SQ_LDS_IDX_ACTIVE"] / clk(v) / cus, "{:.1f}"),
+        ("LDS instruction latency, clk", ("LdsLatency",), lambda v: v["LdsLatency"], "{:.0f}"),
+        ("LDS address conflict clocks", ("SQ_LDS_ADDR_CONFLICT",), lambda v: v["SQ_LDS_ADDR_CONFLICT"], "{:.0f}"),
+    ]
+    runs = [load(p) for p in csv_paths]
+    cols = [f for f in figures if any(all(c in v for c in f[1]) for vals, _ in runs for v in vals.values())]
+    out = ["| kernel | launches | " + " | ".join(f[0] for f in cols) + " |",
+           "|---|---|" + "---|" * len(cols)]
+    for k in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad"):
+        prefix = KERNEL_SOURCES[k][0]
+        row, n = [], 0
+        for name, need, fn, fmt in cols:
+            cell = "–"
+            for vals, names in runs:
+                ds = [d for d, m in names.items() if m.startswith(prefix) or m.startswith("void " + prefix)]
+                ds = sorted(ds, key=int)[len(ds) // 2:]  # the probed step's launches
+                if ds and all(c in vals[ds[0]] for c in need):
+                    cell = fmt.format(sum(fn(vals[d]) for d in ds) / len(ds))
+                    n = len(ds)
+                    break
+            row.append(cell)
+        if n:
+            out.append(f"| `{k}` | {n} | " + " | ".join(row) + " |")
+    print("\n".join(out))
+
+
 def render_stats(stats_csv, title, command):
     """Markdown table of the library's kernels from a rocprofv3 --kernel-trace --stats run
     (its kernel_stats.csv): calls, average / min / max duration, share of profiled GPU time."""
@@ -621,6 +687,7 @@ def main():
                     help="one warm-up step, a 1 GiB calibration copy, one step (for --pmc runs)")
     ap.add_argument("--render-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--render-mfma", metavar="COUNTER_CSV")
+    ap.add_argument("--render-stalls", nargs="+", metavar="COUNTER_CSV")
     ap.add_argument("--render-stats", nargs=3, metavar=("STATS_CSV", "TITLE", "COMMAND"))
     ap.add_argument("--render-counters", nargs=3, metavar=("COUNTER_CSV", "TITLE", "COMMAND"))
     args = ap.parse_args()
@@ -632,6 +699,9 @@ def main():
         return
     if args.render_stats:
         render_stats(*args.render_stats)
+        return
+    if args.render_stalls:
+        render_stalls(*args.render_stalls)
         return
     if args.render_counters:
         render_counters(*args.render_counters)
