@@ -111,6 +111,7 @@ class Plan:
     rep_first: np.ndarray = field(default=None)
     rep_n: np.ndarray = field(default=None)
     n_relayed: int = 0          # walk replicas placed by the relay fallback
+    n_search: int = 0           # steps of the bounded search (0: not run)
 
     @property
     def E_loc(self):
@@ -156,7 +157,7 @@ class Plan:
         """int32 words: header, T, keep, rep_first, rep_n, replica list, slot tables.
 
         header = [status, n_replicas, max_needed, n_donors, n_receivers,
-        n_pieces, n_relayed, 0]; the replica list holds E+R entries of each of
+        n_pieces, n_relayed, n_search]; the replica list holds E+R entries of each of
         (expert, rank, slot, start, count), unused entries (-1, -1, -1, 0, 0);
         the slot tables are [R*B] each of (expert, start, count).
         """
@@ -168,7 +169,7 @@ class Plan:
             re[i], rq[i], rs[i], rst[i], rc[i] = m.expert, m.rank, m.slot, m.start, m.count
         se, ss, sc = self.slot_table()
         hdr = np.array([self.status, len(self.replicas), self.max_needed, self.n_donors,
-                        self.n_receivers, self.n_pieces, self.n_relayed, 0], np.int64)
+                        self.n_receivers, self.n_pieces, self.n_relayed, self.n_search], np.int64)
         blob = np.concatenate([hdr, self.T, self.keep, self.rep_first, self.rep_n,
                                re, rq, rs, rst, rc, se.ravel(), ss.ravel(), sc.ravel()])
         assert blob.size == plan_words(R, E, B)
@@ -204,8 +205,11 @@ def plan(topk_idx: np.ndarray, E: int, B: int) -> Plan:
          emitted); whichever runs out advances
       6. replicas on a receiver take slots 0, 1, ... in emission order; when
          a receiver would need more than B slots the relay fallback
-         (``relay_fallback``) re-places the walk's replicas; a replica it
-         cannot place is dropped and STATUS_SLOT_OVERFLOW is set
+         (``relay_fallback``) re-places the walk's replicas; if it cannot
+         place one, a bounded search (``relay_search``) looks for a plan
+         with at most one replica per rank; if that fails too, the relay
+         fallback's plan stands, its unplaced replicas dropped, and
+         STATUS_SLOT_OVERFLOW is set
     """
     R, S, K = topk_idx.shape
     SK = S * K
@@ -262,9 +266,15 @@ def plan(topk_idx: np.ndarray, E: int, B: int) -> Plan:
         m.slot = hosted[m.rank] if hosted[m.rank] < B else -1
         hosted[m.rank] += 1
     max_needed = max(hosted) if R else 0
-    n_relayed = 0
+    n_relayed = n_search = 0
     if max_needed > B:
         replicas, keep, n_relayed, dropped = relay_fallback(replicas, keep, E_loc, R, B)
+        if dropped and B >= 1:
+            found, keep_s, n_search = relay_search(T, E_loc, R, SK)
+            if found is not None:
+                replicas = _gather_tile([Replica(expert=f, rank=q, start=0, count=x, slot=0)
+                                         for f, q, x in found], keep_s)
+                keep, dropped = keep_s, 0
         if dropped:
             status |= STATUS_SLOT_OVERFLOW
 
@@ -278,7 +288,7 @@ def plan(topk_idx: np.ndarray, E: int, B: int) -> Plan:
     return Plan(R=R, S=S, K=K, E=E, B=B, status=status, counts=C, T=T, keep=keep,
                 replicas=replicas, n_donors=len(donors), n_receivers=len(receivers),
                 n_pieces=len(pieces), max_needed=max_needed, rep_first=rep_first, rep_n=rep_n,
-                n_relayed=n_relayed)
+                n_relayed=n_relayed, n_search=n_search)
 
 
 def relay_fallback(walk, keep, E_loc: int, R: int, B: int):
@@ -377,17 +387,116 @@ def relay_fallback(walk, keep, E_loc: int, R: int, B: int):
             out.append(Replica(expert=f, rank=q, start=0, count=x, slot=-1))
             dropped += 1
 
-    # gather each expert's entries, then tile its copies: home first, entries in order
+    return _gather_tile(out, keep), keep, relayed, dropped
+
+
+def _gather_tile(entries, keep):
+    """Gather each expert's entries together (experts in the order of their
+    first entry, an expert's entries in list order), then tile the expert's
+    copies home first: an entry starts at keep_e + the counts of the
+    expert's earlier entries."""
     first = {}
-    for i, r in enumerate(out):
+    for i, r in enumerate(entries):
         first.setdefault(r.expert, i)
-    order = sorted(range(len(out)), key=lambda i: (first[out[i].expert], i))
-    grouped = [out[i] for i in order]
+    order = sorted(range(len(entries)), key=lambda i: (first[entries[i].expert], i))
+    grouped = [entries[i] for i in order]
     pos = {}
     for r in grouped:
         r.start = int(keep[r.expert]) + pos.get(r.expert, 0)
         pos[r.expert] = pos.get(r.expert, 0) + r.count
-    return grouped, keep, relayed, dropped
+    return grouped
+
+
+SEARCH_BUDGET = 4096
+
+
+def relay_search(T, E_loc: int, R: int, SK: int, budget: int = SEARCH_BUDGET):
+    """Bounded search for a plan with at most one replica per rank, run when
+    the relay fallback leaves a replica unplaced.
+
+    [ainovat] invariant paragraph: every rank gets exactly S*K copies
+    whatever the skew.  READING (the pages give no algorithm).  With one
+    replica per rank a rank takes all the copies it lacks from a single
+    expert of another rank, and that rank may in turn send out more than its
+    own excess and make up the difference the same way (the moves the
+    one-hop fallback cannot express).  The search builds such a plan in
+    generations:
+
+      generation 0: the receivers (d_r < 0), each needing -d_r copies;
+      each rank of a generation, taken by (need desc, r asc), takes its whole
+      need from one expert f whose home g has not taken copies (and is not in
+      this generation) and has cap_f >= need left, where cap starts at T;
+      experts are tried in a fixed order (homes by (d desc, r asc), a home's
+      experts by (T desc, e asc)), first those whose home still has that much
+      excess left (d_g - out_g >= need), then the others, so that a home
+      overshoots only when nothing fits;
+      when a generation is placed, every rank that has not taken copies and
+      has sent out more than its excess (out_r > d_r) forms the next
+      generation, needing out_r - d_r; when none is left the plan is
+      complete if every such rank sent out exactly its excess.
+
+    Depth first, undoing a choice when what follows fails; at most `budget`
+    placements are tried (the search then gives up).  Each rank takes copies
+    at most once, so each hosts at most one replica, and a complete plan
+    keeps every rank at exactly SK copies.
+    Returns (entries [(expert, rank, count)] in placement order, keep = cap,
+    placements tried) or (None, None, placements tried).
+    """
+    E = R * E_loc
+    T = [int(t) for t in T]
+    d = [sum(T[r * E_loc:(r + 1) * E_loc]) - SK for r in range(R)]
+    homes = sorted(range(R), key=lambda r: (-d[r], r))
+    cand = [e for r in homes
+            for e in sorted(range(r * E_loc, (r + 1) * E_loc), key=lambda e: (-T[e], e))]
+    cap = list(T)
+    out = [0] * R
+    got = [False] * R
+    entries = []
+    steps = 0
+
+    def place(pend, i):
+        # True: complete; False: no plan below this point; None: budget spent
+        nonlocal steps
+        if i == len(pend):
+            nxt = sorted(((r, out[r] - d[r]) for r in range(R) if not got[r] and out[r] > d[r]),
+                         key=lambda t: (-t[1], t[0]))
+            if not nxt:
+                return all(got[r] or out[r] == d[r] for r in range(R))
+            for r, _ in nxt:
+                got[r] = True
+            res = place(nxt, 0)
+            if not res:
+                for r, _ in nxt:
+                    got[r] = False
+            return res
+        n, need = pend[i]
+        for fitting in (True, False):
+            for f in cand:
+                g = f // E_loc
+                if got[g] or cap[f] < need or (d[g] - out[g] >= need) != fitting:
+                    continue
+                if steps == budget:
+                    return None
+                steps += 1
+                cap[f] -= need
+                out[g] += need
+                entries.append((f, n, need))
+                res = place(pend, i + 1)
+                if res:
+                    return True
+                cap[f] += need
+                out[g] -= need
+                entries.pop()
+                if res is None:
+                    return None
+        return False
+
+    pend = sorted(((r, -d[r]) for r in range(R) if d[r] < 0), key=lambda t: (-t[1], t[0]))
+    for r, _ in pend:
+        got[r] = True
+    if place(pend, 0):
+        return entries, np.array(cap, np.int64), steps
+    return None, None, steps
 
 
 # --------------------------------------------------------------------------------------------

@@ -287,12 +287,11 @@ def _feasible_within_b(T, R, E, SK, B):
 
 
 def test_relay_fallback_medium_routings():
-    """4-8 ranks, 1-4 experts per rank, B in 1..3, skewed routings: the fallback resolves every
-    overflow with B >= 2 that has any placement within B, and at least 90% of those with B = 1
-    (seeded sample: the fallback is a heuristic, the exact problem is a mixed-integer program;
-    with one slot per rank a receiver's whole deficit must come from one expert, the
-    partition-like case the relay and switch moves do not always reach), and every plan it
-    returns is valid."""
+    """4-8 ranks, 1-4 experts per rank, B in 1..3, skewed routings: every overflow that has any
+    placement within B (a mixed-integer feasibility check) gets a complete plan, from the
+    one-hop fallback or, where that drops a replica (only seen with B = 1: a receiver's whole
+    deficit must then come from one expert, a partition-like condition), from the bounded
+    search; and every plan returned is valid."""
     feas = {1: 0, 2: 0, 3: 0}
     solved = {1: 0, 2: 0, 3: 0}
     for seed in range(60):
@@ -313,8 +312,68 @@ def test_relay_fallback_medium_routings():
                 solved[B] += pl.status == 0
             else:
                 assert pl.status & oracle.STATUS_SLOT_OVERFLOW
-    assert feas[1] >= 30 and solved[1] >= 0.9 * feas[1], (feas, solved)
-    assert feas[2] + feas[3] >= 10 and solved[2] == feas[2] and solved[3] == feas[3], (feas, solved)
+    assert feas[1] >= 30 and feas[2] + feas[3] >= 10, feas
+    assert solved == feas, (feas, solved)
+
+
+def _routing_6_16(seed):
+    rng = np.random.default_rng(50_000 + seed)
+    R = int(rng.integers(6, 17))
+    E_loc = int(rng.choice([1, 2, 4]))
+    E = R * E_loc
+    K = int(rng.integers(1, min(E, 6) + 1))
+    S = int(rng.integers(2, 40))
+    return random_routing(rng, R, S, K, E, skew=float(rng.choice([1.0, 2.0, 5.0, 10.0]))), E
+
+
+def test_relay_search_closes_b1_overflows():
+    """6-16 ranks, B = 1, skew up to 10: every overflow with a placement of one replica per
+    rank (mixed-integer feasibility) gets a complete plan; the search runs only where the
+    one-hop fallback drops a replica, and stays within its step budget."""
+    solved = searched = 0
+    for seed in range(120):
+        idx, E = _routing_6_16(seed)
+        R, S, K = idx.shape
+        pl = oracle.plan(idx, E, 1)
+        check_plan_invariants(idx, pl, 1)
+        assert pl.n_search <= oracle.moe_ref.SEARCH_BUDGET
+        if pl.max_needed <= 1:
+            assert pl.n_search == 0
+            continue
+        searched += pl.n_search > 0
+        if pl.status == 0:
+            solved += 1  # a complete plan (checked above) proves the overflow feasible
+        else:
+            assert pl.status & oracle.STATUS_SLOT_OVERFLOW
+            assert not _feasible_within_b(pl.T, R, E, S * K, 1), seed
+    assert solved >= 80 and searched >= 5, (solved, searched)
+
+
+def test_relay_search_hand_worked():
+    """R5 E_loc4 S*K=48 (seeded routing 10003), B = 1: T by rank [[2,4,4,4], [1,11,5,3],
+    [3,5,7,21], [20,5,21,55], [9,5,19,36]], excess [-34,-28,-12,53,21].  Worked by hand: the
+    walk needs two slots on rank 1 and the one-hop fallback cannot place expert 19's 9 copies
+    there.  The search: rank 0 (34) takes expert 15 (rank 3 has 53 to give); rank 1 (28) finds
+    no home with 28 left, so it takes expert 19 (cap 36) and rank 4 overshoots its 21 by 7;
+    rank 2 (12) takes expert 15; generation 1: rank 4 needs 7 and takes them from expert 15,
+    which leaves rank 3 at exactly its 53.  Keep: expert 15 2, expert 19 8."""
+    rng = np.random.default_rng(10_000 + 3)
+    R = int(rng.integers(4, 9))
+    E_loc = int(rng.choice([1, 2, 4]))
+    E = R * E_loc
+    K = int(rng.integers(1, min(E, 4) + 1))
+    S = int(rng.integers(2, 32))
+    idx = random_routing(rng, R, S, K, E, skew=float(rng.choice([0.5, 1.0, 2.0, 5.0])))
+    pl = oracle.plan(idx, E, 1)
+    assert (R, E_loc, S * K) == (5, 4, 48)
+    assert pl.T.reshape(R, E_loc).tolist() == [[2, 4, 4, 4], [1, 11, 5, 3], [3, 5, 7, 21],
+                                                [20, 5, 21, 55], [9, 5, 19, 36]]
+    assert pl.status == 0 and pl.max_needed == 2 and pl.n_search == 4
+    got = [(m.expert, m.rank, m.start, m.count, m.slot) for m in pl.replicas]
+    assert got == [(15, 0, 2, 34, 0), (15, 2, 36, 12, 0), (15, 4, 48, 7, 0), (19, 1, 8, 28, 0)]
+    assert pl.keep[15] == 2 and pl.keep[19] == 8
+    check_plan_invariants(idx, pl, 1)
+    check_layout(idx, pl)
 
 
 # ------------------------------------------------------------------------------------------
