@@ -19,6 +19,7 @@
 //                  need more than B slots, one thread then re-places the
 //                  walk's replicas with the relay fallback (relay_pass) and
 //                  the block regroups the list by expert.
+#include <climits>
 #include <mutex>
 
 #include "common.hpp"
@@ -185,6 +186,171 @@ __device__ int relay_pass(RelayState &st, int nWalk, int *dropped) {
   return relayed;
 }
 
+// Second fallback, run only when relay_pass drops a replica and B >= 1: a bounded depth-first
+// search for a plan with at most one replica per rank, in generations.  Generation 0 is the
+// receivers, each needing -d_r copies; each rank of a generation, by (need desc, r asc), takes
+// its whole need from one expert f whose home g has taken no copies and is not in the
+// generation, with cap_f >= need (cap starts at T); experts are tried in a fixed order (homes
+// by (d desc, r asc), a home's experts by (T desc, e asc)), first those whose home has that
+// much excess left (d_g - out_g >= need), then the others.  When a generation is placed, the
+// ranks that took no copies and sent out more than their excess form the next one, each
+// needing out_r - d_r; with none left the plan is complete if every such rank sent out exactly
+// its excess.  A failed continuation undoes the last choice and tries the next candidate; at
+// most kSearchBudget placements are tried.  One wavefront runs it: its 64 lanes test 64
+// candidates at a time and the first that fits is taken, so the order is the serial one.
+// The state is in LDS, written by lane 0 and read by all lanes of the same wavefront, whose
+// LDS accesses take effect in program order; the pointers to what changes are volatile so
+// that every access is made where the code makes it.
+constexpr int kSearchBudget = 512;
+constexpr int kTaken = INT_MIN;  // avail[] of a rank that takes copies
+
+struct SearchState {
+  const int *cand;      // [E] experts in trial order
+  const int *cand_g;    // [E] their homes
+  volatile int *cap;    // [E] copies of e not yet placed elsewhere
+  volatile int *out;    // [R] copies rank r has sent out
+  volatile int *avail;  // [R] d_r - out_r, or kTaken if r takes copies
+  volatile int *pn;     // [R] ranks of the generations, in order
+  volatile int *pneed;  // [R] their needs
+  volatile int *gs;     // [R+1] first position of each generation, and the end
+  volatile int *ci;     // [R] candidate taken at each position
+  const int *D;         // excess per rank
+  int E, R;
+};
+
+// First candidate position c >= c0 that a rank needing `need` copies can take: c < E is
+// cand[c] with a home that has that much excess left, E <= c < 2E is cand[c - E] with a home
+// that has not.  2E if none.  One sweep over the candidates answers both passes (each
+// candidate is in exactly one of them), stopping at the first fitting candidate at or past c0.
+// Wave-uniform.
+__device__ int search_scan(const SearchState &s, int c0, int need, int lane) {
+  const int k0 = c0 < s.E ? c0 : c0 - s.E;  // first candidate of the pass c0 is in
+  int other = 2 * s.E;
+  for (int base = 0; base < s.E; base += 64) {
+    const int k = base + lane;
+    bool fit = false, oth = false;
+    if (k < s.E) {
+      const int a = s.avail[s.cand_g[k]];
+      if (a != kTaken && s.cap[s.cand[k]] >= need) {
+        fit = a >= need && c0 < s.E && k >= k0;
+        oth = a < need && (c0 < s.E || k >= k0);
+      }
+    }
+    const unsigned long long mf = __ballot(fit);
+    if (mf) return base + __ffsll((unsigned long long)mf) - 1;
+    const unsigned long long mo = __ballot(oth);
+    if (mo && other == 2 * s.E) other = s.E + base + __ffsll((unsigned long long)mo) - 1;
+  }
+  return other;
+}
+
+// One wavefront (all 64 lanes).  s.pn/pneed[0, n0) hold generation 0, marked taken in avail,
+// and s.gs[0..1] = 0, n0.  Returns the number of placements of a complete plan (positions
+// 0..n-1 of pn, pneed, ci), or -1; *steps = placements tried.
+__device__ int relay_search(const SearchState &s, int n0, int lane, int *steps) {
+  int i = 0, g = 0, gend = n0, c0 = 0;
+  *steps = 0;
+  for (;;) {
+    bool back = false;
+    if (i == gend) {
+      // the next generation: ranks that take no copies and sent out more than their excess,
+      // gathered in rank order, then put in (need desc, r asc) order
+      int cnt = 0;
+      bool balanced = true;
+      for (int r0 = 0; r0 < s.R; r0 += 64) {
+        const int r = r0 + lane;
+        const int a = r < s.R ? s.avail[r] : kTaken;
+        const bool over = a != kTaken && a < 0;
+        const unsigned long long m = __ballot(over);
+        if (over) {
+          const int j = cnt + (int)__builtin_amdgcn_mbcnt_hi(
+                                  (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+          s.pn[gend + j] = r;
+          s.pneed[gend + j] = -a;
+        }
+        cnt += __popcll(m);
+        balanced = balanced && __ballot(a != kTaken && a != 0) == 0;
+      }
+      if (cnt == 0) {
+        if (balanced) return gend;
+        back = true;
+      } else {
+        // every entry's place among the cnt entries, all read before any is moved
+        constexpr int kPer = kMaxR / 64;
+        int rr[kPer], nn[kPer], pp[kPer];
+#pragma unroll
+        for (int b = 0; b < kPer; ++b) {
+          const int t = lane + 64 * b;
+          rr[b] = t < cnt ? s.pn[gend + t] : 0;
+          nn[b] = t < cnt ? s.pneed[gend + t] : 0;
+        }
+#pragma unroll
+        for (int b = 0; b < kPer; ++b) {
+          int pos = 0;
+          if (lane + 64 * b < cnt)
+            for (int u = 0; u < cnt; ++u) {
+              const int nu = s.pneed[gend + u], ru = s.pn[gend + u];
+              pos += nu > nn[b] || (nu == nn[b] && ru < rr[b]);
+            }
+          pp[b] = pos;
+        }
+#pragma unroll
+        for (int b = 0; b < kPer; ++b)
+          if (lane + 64 * b < cnt) {
+            s.pn[gend + pp[b]] = rr[b];
+            s.pneed[gend + pp[b]] = nn[b];
+            s.avail[rr[b]] = kTaken;
+          }
+        ++g;
+        gend += cnt;
+        if (lane == 0) s.gs[g + 1] = gend;
+        c0 = 0;
+        continue;
+      }
+    }
+    if (!back) {
+      const int need = s.pneed[i];
+      const int c = search_scan(s, c0, need, lane);
+      if (c < 2 * s.E) {
+        if (*steps == kSearchBudget) return -1;
+        ++*steps;
+        const int k = c < s.E ? c : c - s.E;
+        const int f = s.cand[k], h = s.cand_g[k];
+        if (lane == 0) {
+          s.cap[f] = s.cap[f] - need;
+          s.out[h] = s.out[h] + need;
+          s.avail[h] = s.D[h] - s.out[h];
+          s.ci[i] = c;
+        }
+        ++i;
+        c0 = 0;
+        continue;
+      }
+    }
+    // no (further) candidate here: undo the previous placement and try its next candidate,
+    // first dropping the current generation if this is its first position
+    if (g > 0 && i == s.gs[g]) {
+      for (int p = s.gs[g] + lane; p < gend; p += 64) {
+        const int r = s.pn[p];
+        s.avail[r] = s.D[r] - s.out[r];
+      }
+      --g;
+      gend = s.gs[g + 1];
+    }
+    if (i == 0) return -1;
+    --i;
+    const int c = s.ci[i], need = s.pneed[i];
+    const int k = c < s.E ? c : c - s.E;
+    const int f = s.cand[k], h = s.cand_g[k];
+    if (lane == 0) {
+      s.cap[f] = s.cap[f] + need;
+      s.out[h] = s.out[h] - need;
+      s.avail[h] = s.D[h] - s.out[h];
+    }
+    c0 = c + 1;
+  }
+}
+
 __global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__restrict__ counts,
                                                               const int32_t *__restrict__ bad,
                                                               int32_t *__restrict__ plan,
@@ -205,7 +371,11 @@ __global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__r
   __shared__ int sHosted[kMaxR], sChainFirst[kMaxR], sChainLast[kMaxR], sChainNext[kMaxL];
   __shared__ int tExp[kMaxL], tRank[kMaxL], tCount[kMaxL], tSlot[kMaxL];
   __shared__ int sTmp[32];
+  // bounded search: candidate order, copies left, per-rank out/took, generations, choices
+  __shared__ int sCand[kMaxE], sCandG[kMaxE], sCap[kMaxE];
+  __shared__ int sOut[kMaxR], sAvail[kMaxR], sPn[kMaxR], sPneed[kMaxR], sGs[kMaxR + 1], sCi[kMaxR];
   __shared__ int sNDonor, sNRecv, sMaxNeeded, sOverflow, sBad, sNOut, sRelayed, sDropped;
+  __shared__ int sSteps, sFound;
 
   const int tid = threadIdx.x, nt = blockDim.x;
   const int E_loc = E / R;
@@ -220,6 +390,8 @@ __global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__r
     sBad = 0;
     sRelayed = 0;
     sDropped = 0;
+    sSteps = 0;
+    sFound = 0;
   }
   __syncthreads();
   // T_e and the bad-id flag
@@ -408,6 +580,63 @@ __global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__r
       sDropped = nd;
       sNOut = st.w;
     }
+    __syncthreads();
+    if (sDropped && B >= 1) {  // uniform: the bounded search
+      // candidate order (homes by (d desc, r asc), experts by (T desc, e asc) = sSrank),
+      // copies left, and generation 0 (the receivers in their walk order)
+      for (int e = tid; e < E; e += nt) {
+        const int r = e / E_loc, d = sD[r];
+        int pos = 0;
+        for (int q = 0; q < R; ++q) {
+          const int dq = sD[q];
+          pos += (dq > d) || (dq == d && q < r);
+        }
+        sCand[pos * E_loc + sSrank[e]] = e;
+        sCandG[pos * E_loc + sSrank[e]] = r;
+        sCap[e] = sT[e];
+      }
+      for (int r = tid; r < R; r += nt) {
+        sOut[r] = 0;
+        sAvail[r] = sD[r] < 0 ? kTaken : sD[r];
+      }
+      for (int j = tid; j < nRecv; j += nt) {
+        sPn[j] = sRecvAt[j];
+        sPneed[j] = -sD[sRecvAt[j]];
+      }
+      if (tid == 0) {
+        sGs[0] = 0;
+        sGs[1] = nRecv;
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const SearchState ss{sCand, sCandG, sCap, sOut, sAvail, sPn, sPneed, sGs, sCi, sD, E, R};
+        int steps = 0;
+        const int n = relay_search(ss, nRecv, tid, &steps);
+        if (tid == 0) {
+          sSteps = steps;
+          sFound = n >= 0;
+          if (n >= 0) {
+            sNOut = n;
+            sDropped = 0;
+          }
+        }
+      }
+      __syncthreads();
+      if (sFound) {  // uniform: the search's plan replaces the relay pass's
+        for (int m = tid; m < sNOut; m += nt) {
+          const int c = sCi[m];
+          sRexp[m] = sCand[c < E ? c : c - E];
+          sRrank[m] = sPn[m];
+          sRcount[m] = sPneed[m];
+          sRslot[m] = 0;
+        }
+        for (int e = tid; e < E; e += nt) sKeep[e] = sCap[e];
+        for (int r = tid; r < R; r += nt) sHosted[r] = 0;
+        __syncthreads();
+        for (int m = tid; m < sNOut; m += nt) sHosted[sPn[m]] = 1;
+      }
+      __syncthreads();
+    }
     // sSrank (per expert) is free now: first list index of each expert
     for (int e = tid; e < E; e += nt) {
       sSrank[e] = 0x7fffffff;
@@ -466,7 +695,7 @@ __global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__r
     plan[4] = nRecv;
     plan[5] = nPieces;
     plan[6] = sRelayed;
-    plan[7] = 0;
+    plan[7] = sSteps;
     if (dev_status) *dev_status = (uint32_t)status;
   }
   for (int e = tid; e < E; e += nt) {

@@ -103,12 +103,20 @@ const char *moe_status_string(moe_status_t s);
  * of its replicas switches to the new expert while the new expert's home
  * takes the switched-out copies (first fit over the receiver's slots; a
  * "place" goes to the home's keep, an existing replica, or a free slot).
- * A replica neither can place is dropped with MOE_DEV_SLOT_OVERFLOW.  The
- * list is then gathered by expert (experts by first entry, entries in pass
- * order) and each expert's copies are tiled home first, then its entries.
- * Plans the walk fits are the walk's.  Afterwards every rank processes
- * exactly S*K copies (absent overflow and bad ids).  The fallback is one
- * thread's loop (fast when few replicas need it; it runs only on overflow).
+ * If it cannot place a replica and B >= 1, a bounded search looks for a plan
+ * with at most one replica per rank: the receivers, by (deficit desc, r asc),
+ * each take their whole deficit from one expert of a rank that takes no
+ * copies (homes by (d desc, r asc), experts by (T desc, e asc); homes with
+ * that much excess left first, then the others); a home that so sends out
+ * more than its excess takes the difference the same way, in the next
+ * generation; depth first, at most 512 placements.  If it finds none, the
+ * relay fallback's plan stands and each replica it could not place is dropped
+ * with MOE_DEV_SLOT_OVERFLOW.  The list is then gathered by expert (experts
+ * by first entry, entries in pass order) and each expert's copies are tiled
+ * home first, then its entries.  Plans the walk fits are the walk's.
+ * Afterwards every rank processes exactly S*K copies (absent overflow and bad
+ * ids).  The relay fallback is one thread's loop and the search one
+ * wavefront's (64 candidates tested at a time); both run only on overflow.
  *
  *   topk_idx   [R*S*K] int32, router top-K expert ids of every rank.
  *   counts     [R*E] int32 out, C[p][e] (ids outside [0,E) not counted).
@@ -116,7 +124,8 @@ const char *moe_status_string(moe_status_t s);
  *                [0] status bits  [1] replicas in the list  [2] most
  *                replicas the walk asked of one rank  [3] donors
  *                [4] receivers  [5] pieces  [6] replicas relayed or
- *                switched by the fallback  [7] 0
+ *                switched by the fallback  [7] placements tried by
+ *                the bounded search (0: it did not run)
  *                T[E]  keep[E] (copies of e staying home)
  *                rep_first[E] rep_n[E] (e's replicas in the list; 0,0 if none)
  *                replica list, E+R entries each of expert[] rank[] slot[]

@@ -407,7 +407,7 @@ def _gather_tile(entries, keep):
     return grouped
 
 
-SEARCH_BUDGET = 4096
+SEARCH_BUDGET = 512
 
 
 def relay_search(T, E_loc: int, R: int, SK: int, budget: int = SEARCH_BUDGET):

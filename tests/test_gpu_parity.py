@@ -98,7 +98,7 @@ RELAY_CASES = [
     (4, 64, 2, 8, 1, 0.3),           # one relay
     (8, 200, 2, 16, 1, 0.3),
     (8, 50, 1, 8, 1, 0.5),
-    (16, 100, 4, 32, 1, 0.2),        # relays, and some replicas still dropped
+    (16, 100, 4, 32, 1, 0.2),        # relays drop replicas; the bounded search plans it
     (32, 256, 8, 256, 1, 0.1),       # the same at 32 ranks
     (64, 64, 4, 128, 1, 0.1),        # 13 relays over 64 ranks
 ]
@@ -125,9 +125,10 @@ def test_plan_layout_relay_seeded_overflows():
     """Every walk overflow of the oracle's seeded medium-routing set (4-8 ranks, 1-4 experts
     per rank, B = 1..3; the set the CPU test pins against mixed-integer feasibility), solved or
     not, and of 300 more routings of 6-16 ranks: the GPU plan and layout match the oracle bit for
-    bit (first and last rank of the first set, rank 0 of the second)."""
+    bit (first and last rank of the first set, rank 0 of the second), among them the plans the
+    bounded search finds where the relay fallback drops a replica."""
     from test_oracle_plan import random_routing
-    n = 0
+    n = searched = 0
     for seed in range(60):
         rng = np.random.default_rng(10_000 + seed)
         R = int(rng.integers(4, 9))
@@ -141,6 +142,7 @@ def test_plan_layout_relay_seeded_overflows():
             if pl.max_needed <= B:
                 continue
             n += 1
+            searched += pl.n_search > 0 and pl.status == 0
             gp = GpuPlan(R, S, K, E, B)
             for r in (0, R - 1):
                 gp.run(_dev(idx), r)
@@ -159,11 +161,53 @@ def test_plan_layout_relay_seeded_overflows():
             if pl.max_needed <= B:
                 continue
             n += 1
+            searched += pl.n_search > 0 and pl.status == 0
             gp = GpuPlan(R, S, K, E, B)
             gp.run(_dev(idx), 0)
             check_plan_layout(gp, idx, 0, pl)
-    log(f"relay: {n} seeded overflows bit-exact")
-    assert n >= 400
+    log(f"relay: {n} seeded overflows bit-exact, {searched} of them planned by the search")
+    assert n >= 400 and searched >= 20
+
+
+@pytest.mark.parametrize("seed", [0, 11, 13])
+def test_plan_layout_search_gives_up(seed):
+    """32-64 ranks, B = 1, skew up to 20: routings where the relay fallback drops replicas and
+    the bounded search finds no plan, at once (seeds 0, 13: some receiver's deficit exceeds
+    every expert it could take from) or after its 4096 placements (seed 11).  The relay
+    fallback's plan stands, with MOE_DEV_SLOT_OVERFLOW, bit for bit as in the oracle."""
+    from test_oracle_plan import random_routing
+    rng = np.random.default_rng(90_000 + seed)
+    R = int(rng.choice([32, 64]))
+    E_loc = int(rng.choice([2, 4, 8]))
+    E = R * E_loc
+    K = int(rng.choice([4, 8]))
+    S = int(rng.integers(16, 128))
+    idx = random_routing(rng, R, S, K, E, skew=float(rng.choice([2.0, 5.0, 10.0, 20.0])))
+    pl = oracle.plan(idx, E, 1)
+    assert pl.status & oracle.STATUS_SLOT_OVERFLOW
+    assert pl.n_search == (oracle.moe_ref.SEARCH_BUDGET if seed == 11 else 0)
+    gp = GpuPlan(R, S, K, E, 1)
+    for r in (0, R - 1):
+        log(f"search gives up seed={seed} R={R} E={E} rank={r} steps={pl.n_search}")
+        gp.run(_dev(idx), r)
+        check_plan_layout(gp, idx, r, pl)
+
+
+def test_plan_layout_search_gives_up_max_shape():
+    """R = 512, E = 1024 (the largest the library takes), B = 1, skew 20: the search spends its
+    whole budget and the relay fallback's plan stands, bit for bit as in the oracle."""
+    from test_oracle_plan import random_routing
+    rng = np.random.default_rng(77_000)
+    R, E, K = 512, 1024, 4
+    S = int(rng.integers(8, 32))
+    idx = random_routing(rng, R, S, K, E, skew=float(rng.choice([5.0, 10.0, 20.0])))
+    pl = oracle.plan(idx, E, 1)
+    assert pl.status & oracle.STATUS_SLOT_OVERFLOW and pl.n_search == oracle.moe_ref.SEARCH_BUDGET
+    gp = GpuPlan(R, S, K, E, 1)
+    for r in (0, R - 1):
+        log(f"search gives up at R={R} E={E} rank={r}")
+        gp.run(_dev(idx), r)
+        check_plan_layout(gp, idx, r, pl)
 
 
 @pytest.mark.parametrize("B", [1, 2])

@@ -460,3 +460,24 @@ def test_plan_blob_size_and_header():
     assert blob.dtype == np.int32 and blob.size == oracle.plan_words(4, 16, 3)
     assert blob[0] == pl.status and blob[1] == len(pl.replicas)
     assert (blob[8:8 + 16] == pl.T).all()
+
+
+def test_relay_search_gives_up_within_budget():
+    """32-64 ranks, B = 1, skew up to 20 (seeded): where the search finds no plan it stops at
+    once when some receiver's deficit exceeds every expert it could take from (nothing to try),
+    else after exactly its budget of placements; the relay fallback's plan then stands with
+    STATUS_SLOT_OVERFLOW and stays valid."""
+    for seed, steps in ((0, 0), (11, oracle.moe_ref.SEARCH_BUDGET), (13, 0)):
+        rng = np.random.default_rng(90_000 + seed)
+        R = int(rng.choice([32, 64]))
+        E_loc = int(rng.choice([2, 4, 8]))
+        E = R * E_loc
+        K = int(rng.choice([4, 8]))
+        S = int(rng.integers(16, 128))
+        idx = random_routing(rng, R, S, K, E, skew=float(rng.choice([2.0, 5.0, 10.0, 20.0])))
+        pl = oracle.plan(idx, E, 1)
+        assert pl.status & oracle.STATUS_SLOT_OVERFLOW and pl.n_search == steps, (seed, pl.n_search)
+        check_plan_invariants(idx, pl, 1)
+        if steps == 0:
+            d = pl.T.reshape(R, E_loc).sum(axis=1) - S * K
+            assert -d.min() > pl.T.max()  # the largest deficit fits no expert
