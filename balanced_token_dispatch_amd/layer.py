@@ -20,6 +20,13 @@ With ``fused_gather=True`` (identity activation) there is no permute and no
 xp buffer: the up projection's FWD and WGRAD read their row operand straight
 from the token rows through src_flat (moe_group_gemm_gather), the permute
 fused into the expert GEMM.
+With ``overlap=True`` (the default) the backward puts the kernels whose
+results no later kernel of the step reads on a second stream, each under a
+GEMM of the four-wave form (one workgroup per CU that leaves room on every
+CU for a row kernel's waves): the router-weight gradient runs beside the
+down DGRAD, and both folds beside the up DGRAD, which then comes after the
+up WGRAD.  Events order them after what they read; the main stream waits for
+the second one before the step ends.
 The activation between the projections is the identity, or, with
 ``activation="swiglu"``, the gated linear unit: the up projection then has
 2H' columns holding (gate, up) pairs, its GEMM writes both the pre-activation
@@ -60,7 +67,7 @@ class Shape:
 class LayerStep:
     def __init__(self, shape: Shape, rank: int = 0, dtype=torch.bfloat16, device="cuda",
                  backward: bool = True, activation: str = "identity", fused_gather: bool = False,
-                 plan_noalloc: bool = False):
+                 plan_noalloc: bool = False, overlap: bool = True):
         s = shape
         if activation not in ("identity", "swiglu"):
             raise ValueError(f"activation {activation!r}")
@@ -102,6 +109,11 @@ class LayerStep:
         self.y_all = torch.zeros((s.R * s.SK, s.H), **act)
         self.out = torch.zeros((s.S, s.H), **act)
         self.backward_enabled = backward
+        # the backward's side stream (default priority) and its fork/join events
+        self.overlap = overlap
+        if overlap:
+            self.side = torch.cuda.Stream(device=device)
+            self.ev_fork, self.ev_wgrad, self.ev_join = (torch.cuda.Event() for _ in range(3))
         if backward:
             self.dout_all = torch.zeros((s.R * s.S, s.H), **act)
             self.dy = torch.zeros((s.SK, s.H), **act)
@@ -167,28 +179,52 @@ class LayerStep:
         s, r, c = self.s, self.rank, self._call
         c(timer, "permute_weighted", moe_permute, self.d, self.dout_all, self.src, self.dy,
           self.topk_w.view(-1))
-        c(timer, "combine_wgrad", moe_combine_weight_grad, self.d, r, self.y_all, self.dest,
-          self.dout_all[r * s.S:(r + 1) * s.S], self.dtopk_w)
+        cwgrad = (timer, "combine_wgrad", moe_combine_weight_grad, self.d, r, self.y_all,
+                  self.dest, self.dout_all[r * s.S:(r + 1) * s.S], self.dtopk_w)
+        if self.overlap:
+            main = torch.cuda.current_stream()
+            self.ev_fork.record(main)
+        else:
+            c(*cwgrad)
         c(timer, "gemm_dgrad", moe_group_gemm, GEMM_DGRAD, self.dy, self.w_down, self.cu, self.dz,
           s.Hp, s.H, self.gemm_ws)
+        if self.overlap:  # beside the down DGRAD: it reads only forward results and dout
+            self.side.wait_event(self.ev_fork)
+            with torch.cuda.stream(self.side):
+                c(*cwgrad)
         c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.z, self.dy, self.cu, self.dw_down,
           s.Hp, s.H)
         dup = self.dz
         if self.activation == "swiglu":
             c(timer, "swiglu_bwd", moe_swiglu_backward, self.hpre, self.dz, self.dh)
             dup = self.dh
-        c(timer, "gemm_dgrad", moe_group_gemm, GEMM_DGRAD, dup, self.w_up, self.cu, self.dxp,
-          s.H, self.up_cols, self.gemm_ws)
+        up_dgrad = (timer, "gemm_dgrad", moe_group_gemm, GEMM_DGRAD, dup, self.w_up, self.cu,
+                    self.dxp, s.H, self.up_cols, self.gemm_ws)
+        if not self.overlap:
+            c(*up_dgrad)
         if self.fused_gather:
             c(timer, "gemm_wgrad_gather", moe_group_gemm_gather, GEMM_WGRAD, self.x_all, self.src,
               s.K, dup, self.cu, self.dw_up, s.H, self.up_cols)
         else:
             c(timer, "gemm_wgrad", moe_group_gemm, GEMM_WGRAD, self.xp, dup, self.cu, self.dw_up,
               s.H, self.up_cols)
+        folds = ((timer, "fold", moe_replica_grad_fold, self.d, r, self.plan, self.dw_up),
+                 (timer, "fold", moe_replica_grad_fold, self.d, r, self.plan, self.dw_down))
+        if self.overlap:  # both folds beside the up DGRAD, after both WGRADs
+            self.ev_wgrad.record(main)
+            c(*up_dgrad)
+            self.side.wait_event(self.ev_wgrad)
+            with torch.cuda.stream(self.side):
+                for f in folds:
+                    c(*f)
+            self.ev_join.record(self.side)
         c(timer, "unpermute_reduce", moe_unpermute_reduce, self.d, r, self.dxp_all, self.dest,
           self.dx)
-        c(timer, "fold", moe_replica_grad_fold, self.d, r, self.plan, self.dw_up)
-        c(timer, "fold", moe_replica_grad_fold, self.d, r, self.plan, self.dw_down)
+        if self.overlap:
+            main.wait_event(self.ev_join)
+        else:
+            for f in folds:
+                c(*f)
 
     def step(self, timer=None):
         self.forward(timer)
