@@ -640,7 +640,9 @@ def scale_sweep(args):
         el = run_steps(layer, n, 2)
         ms_t = el * 1000.0 / n
         timer = EventTimer()
+        ov, layer.overlap = layer.overlap, False  # each kernel's own event time (see main)
         run_steps(layer, n, 0, timer)
+        layer.overlap = ov
         kern, _ = kernel_fracs(timer, layer.s, slots_used(layer), n)
         key = f"{info['maxvio']:.2f}"
         points[key] = {"target": t, "ms_per_step": round(ms_t, 4),
