@@ -7,7 +7,9 @@ combine, the backward kernels and the fold) can be captured once and replayed; a
 permute fused into the up GEMM and the plan on the library's static scratch (moe_plan_noalloc,
 whose device address is looked up before capture, on the eager step).  The test replays the
 graph several times with eager steps and eager work in between and compares every output of
-every replay with the eager step's.
+every replay with the eager step's.  The step's second stream (on by default) is captured with
+its event fork and join; a second test checks that the step with it matches the step in one
+stream bit for bit.
 """
 import numpy as np
 import pytest
@@ -93,3 +95,40 @@ def test_layer_step_graph_replay(activation, fused, noalloc):
             assert torch.equal(got[k], ref[k]), f"eager after replay {rep}: {k} differs"
         log(f"graph replay {rep} ({activation}, fused={fused}, noalloc={noalloc}) identical "
             f"to the eager step")
+
+
+@pytest.mark.parametrize("activation,fused,noalloc", CASES)
+def test_layer_step_second_stream_matches_one_stream(activation, fused, noalloc):
+    """The step with its second stream (slot-row prefetches beside the dispatch layout, the
+    router-weight gradient and the folds beside the DGRAD GEMMs, joined by events) gives every
+    output bit for bit as the step in one stream, over several steps in a row."""
+    from balanced_token_dispatch_amd.layer import LayerStep, Shape
+    d = synth.Dims(R=8, S=512, K=4, E=32, B=4, H=256, Hp=192)
+    idx, w = synth.routing(d, 1.0, 22)
+    L = LayerStep(Shape(d.R, d.S, d.K, d.E, d.B, d.H, d.Hp), rank=2, activation=activation,
+                  fused_gather=fused, plan_noalloc=noalloc)
+    assert L.overlap
+    for t, sd in ((L.x_all, 221), (L.y_all, 224), (L.dout_all, 225), (L.dxp_all, 226)):
+        synth.fill_normal_(t, 1.0, sd)
+    synth.fill_normal_(L.w_up, 0.05, 222)
+    synth.fill_normal_(L.w_down, 0.05, 223)
+    L.topk_idx.copy_(torch.from_numpy(idx))
+    L.topk_w.copy_(torch.from_numpy(w))
+
+    def step(overlap):
+        L.overlap = overlap
+        L.dw_up.zero_()
+        L.dw_down.zero_()
+        L.step()
+        torch.cuda.synchronize()
+        return _outputs(L)
+
+    ref = step(False)
+    assert int(L.status.item()) == 0
+    for rep in range(3):
+        got = step(True)
+        for k, v in ref.items():
+            same = torch.equal(got[k].view(torch.uint8), v.view(torch.uint8))
+            log(f"second stream {activation} fused={fused} rep={rep} {k}: "
+                f"{'identical' if same else 'DIFFERENT'}")
+            assert same, k
