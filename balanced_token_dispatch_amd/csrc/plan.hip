@@ -198,9 +198,9 @@ __device__ int relay_pass(RelayState &st, int nWalk, int *dropped) {
 // its excess.  A failed continuation undoes the last choice and tries the next candidate; at
 // most kSearchBudget placements are tried.  One wavefront runs it: its 64 lanes test 64
 // candidates at a time and the first that fits is taken, so the order is the serial one.
-// The state is in LDS, written by lane 0 and read by all lanes of the same wavefront, whose
-// LDS accesses take effect in program order; the pointers to what changes are volatile so
-// that every access is made where the code makes it.
+// The state is in LDS, each word written by one lane and read by any lane of the same
+// wavefront, whose LDS accesses take effect in program order; the pointers to what changes
+// are volatile so that every access is made where the code makes it.
 constexpr int kSearchBudget = 512;
 constexpr int kTaken = INT_MIN;  // avail[] of a rank that takes copies
 
