@@ -2,9 +2,11 @@
 
 Buffers are allocated once (static shapes: every rank receives exactly S*K
 rows, so nothing here depends on the routing).  ``forward`` and
-``backward`` only enqueue C-ABI calls on torch's current stream; every
-number is computed by the HIP kernels.
+``backward`` only enqueue C-ABI calls on torch's current stream (and, with
+``overlap``, on a second stream joined back into it); every number is
+computed by the HIP kernels.
 
+In one stream (``overlap=False``):
 Forward (rank r):  plan -> dispatch layout -> prefetch slot rows of both
 projections -> permute -> up GEMM -> down GEMM (written into rank r's
 slice of the all-ranks expert-output buffer) -> combine.
