@@ -116,7 +116,9 @@ const char *moe_status_string(moe_status_t s);
  * home first, then its entries.  Plans the walk fits are the walk's.
  * Afterwards every rank processes exactly S*K copies (absent overflow and bad
  * ids).  The relay fallback is one thread's loop and the search one
- * wavefront's (64 candidates tested at a time); both run only on overflow.
+ * wavefront's (64 candidates tested at a time); both run only on overflow.  A
+ * search that spends its budget adds a few milliseconds to the plan (2.2 ms at
+ * R=32 E=256, 3.4 ms at R=512 E=1024 on MI355X).
  *
  *   topk_idx   [R*S*K] int32, router top-K expert ids of every rank.
  *   counts     [R*E] int32 out, C[p][e] (ids outside [0,E) not counted).
