@@ -3,8 +3,8 @@
 Buffers are allocated once (static shapes: every rank receives exactly S*K
 rows, so nothing here depends on the routing).  ``forward`` and
 ``backward`` only enqueue C-ABI calls on torch's current stream (and, with
-``overlap``, on a second stream joined back into it); every number is
-computed by the HIP kernels.
+``overlap``, the backward on a second stream joined back into it); every
+number is computed by the HIP kernels.
 
 In one stream (``overlap=False``):
 Forward (rank r):  plan -> dispatch layout -> prefetch slot rows of both
@@ -22,15 +22,15 @@ With ``fused_gather=True`` (identity activation) there is no permute and no
 xp buffer: the up projection's FWD and WGRAD read their row operand straight
 from the token rows through src_flat (moe_group_gemm_gather), the permute
 fused into the expert GEMM.
-With ``overlap=True`` (the default) a second stream takes kernels that can
-run beside others: in the forward the two slot-row prefetches, beside the
-latency-bound dispatch layout (and the permute), joined before the up GEMM;
-in the backward the kernels whose results no later kernel of the step reads,
-each under a GEMM of the four-wave form (one workgroup per CU that leaves
-room on every CU for a row kernel's waves): the router-weight gradient
-beside the down DGRAD, and both folds beside the up DGRAD, which then comes
-after the up WGRAD.  Events order them after what they read; the main stream
-waits for the second one before the step ends.
+With ``overlap=True`` the backward puts the kernels whose results no later
+kernel of the step reads on a second stream, each under a GEMM of the
+four-wave form (one workgroup per CU that leaves room on every CU for a row
+kernel's waves): the router-weight gradient beside the down DGRAD, and both
+folds beside the up DGRAD, which then comes after the up WGRAD.  Events order
+them after what they read; the main stream waits for the second one before
+the step ends.  The default (``overlap=None``) turns it on for steps with
+S*K*H*H' >= kOverlapMinWork, where the GEMMs are long enough to hide the
+kernels beside them.
 The activation between the projections is the identity, or, with
 ``activation="swiglu"``, the gated linear unit: the up projection then has
 2H' columns holding (gate, up) pairs, its GEMM writes both the pre-activation
@@ -47,6 +47,11 @@ from . import (GEMM_DGRAD, GEMM_FWD, GEMM_WGRAD, dims as _mk_dims, dispatch_layo
                moe_permute, moe_plan, moe_plan_noalloc,
                moe_prefetch, moe_replica_grad_fold, moe_swiglu_backward, moe_unpermute_reduce,
                plan_words, plan_workspace_bytes)
+
+
+# S*K*H*H' from which the backward uses its second stream by default (the R32 S4096 K8 H7168
+# H'2048 step has 4.8e11; its DGRADs take ~0.8 ms each)
+kOverlapMinWork = 1e11
 
 
 @dataclass
@@ -71,7 +76,7 @@ class Shape:
 class LayerStep:
     def __init__(self, shape: Shape, rank: int = 0, dtype=torch.bfloat16, device="cuda",
                  backward: bool = True, activation: str = "identity", fused_gather: bool = False,
-                 plan_noalloc: bool = False, overlap: bool = True):
+                 plan_noalloc: bool = False, overlap=None):
         s = shape
         if activation not in ("identity", "swiglu"):
             raise ValueError(f"activation {activation!r}")
@@ -113,12 +118,14 @@ class LayerStep:
         self.y_all = torch.zeros((s.R * s.SK, s.H), **act)
         self.out = torch.zeros((s.S, s.H), **act)
         self.backward_enabled = backward
-        # the backward's side stream (default priority) and its fork/join events
-        self.overlap = overlap
-        if overlap:
-            self.side = torch.cuda.Stream(device=device)
-            self.ev_fork, self.ev_wgrad, self.ev_join, self.ev_plan, self.ev_prefetch = (
-                torch.cuda.Event() for _ in range(5))
+        # the backward's side stream (default priority) and its fork/join events; by default
+        # only where the GEMMs are long enough for the kernels beside them to gain more than
+        # the cross-stream waits cost (~tens of microseconds on short steps)
+        if overlap is None:
+            overlap = s.S * s.K * s.H * s.Hp >= kOverlapMinWork
+        self.overlap = bool(overlap)
+        self.side = torch.cuda.Stream(device=device)
+        self.ev_fork, self.ev_wgrad, self.ev_join = (torch.cuda.Event() for _ in range(3))
         if backward:
             self.dout_all = torch.zeros((s.R * s.S, s.H), **act)
             self.dy = torch.zeros((s.SK, s.H), **act)
@@ -160,30 +167,15 @@ class LayerStep:
         else:
             c(timer, "plan", moe_plan, self.d, self.topk_idx, self.counts, self.plan,
               self.status, self.ws)
-        prefetch = ((timer, "prefetch", moe_prefetch, self.d, r, self.plan, self.w_up),
-                    (timer, "prefetch", moe_prefetch, self.d, r, self.plan, self.w_down))
-        if self.overlap:  # the slot rows' copies beside the (latency-bound) dispatch layout
-            main = torch.cuda.current_stream()
-            self.ev_plan.record(main)
-            self.side.wait_event(self.ev_plan)
-            with torch.cuda.stream(self.side):
-                for f in prefetch:
-                    c(*f)
-            self.ev_prefetch.record(self.side)
         c(timer, "dispatch_layout", moe_dispatch_layout, self.d, r, self.topk_idx, self.plan,
           self.cu, self.dest, self.src, self.ws)
-        if not self.overlap:
-            for f in prefetch:
-                c(*f)
+        c(timer, "prefetch", moe_prefetch, self.d, r, self.plan, self.w_up)
+        c(timer, "prefetch", moe_prefetch, self.d, r, self.plan, self.w_down)
         if self.fused_gather:   # up projection reading the token rows through src_flat
-            if self.overlap:
-                main.wait_event(self.ev_prefetch)
             c(timer, "gemm_fwd_gather", moe_group_gemm_gather, GEMM_FWD, self.x_all, self.src,
               s.K, self.w_up, self.cu, self.z, s.H, s.Hp, self.gemm_ws)
         else:
             c(timer, "permute", moe_permute, self.d, self.x_all, self.src, self.xp)
-            if self.overlap:
-                main.wait_event(self.ev_prefetch)
             if self.activation == "swiglu":
                 c(timer, "gemm_fwd_swiglu", moe_group_gemm_swiglu, self.xp, self.w_up, self.cu,
                   self.z, self.hpre, s.H, self.up_cols, self.gemm_ws)

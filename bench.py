@@ -860,8 +860,8 @@ def main():
         "kernel_ms_per_step": round(kern_ms, 4),
         "overlap": None if seq_ms is None else {
             "one_stream_ms_per_step": round(seq_ms, 4), "saved_ms": round(seq_ms - ms_step, 4),
-            "second_stream": "slot-row prefetches beside the dispatch layout; router-weight "
-                             "gradient beside the down DGRAD; both folds beside the up DGRAD"},
+            "second_stream": "router-weight gradient beside the down DGRAD; both folds beside "
+                             "the up DGRAD"},
         "forward_only": None if fwd_ms is None else {"ms_per_step": round(fwd_ms, 4),
                                                      "tokens_per_s": round(s.S / (fwd_ms * 1e-3), 1)},
         "graph_replay": graph,

@@ -7,9 +7,8 @@ combine, the backward kernels and the fold) can be captured once and replayed; a
 permute fused into the up GEMM and the plan on the library's static scratch (moe_plan_noalloc,
 whose device address is looked up before capture, on the eager step).  The test replays the
 graph several times with eager steps and eager work in between and compares every output of
-every replay with the eager step's.  The step's second stream (on by default) is captured with
-its event fork and join; a second test checks that the step with it matches the step in one
-stream bit for bit.
+every replay with the eager step's.  A second test checks that the step with its backward's
+second stream (event fork and join) matches the step in one stream bit for bit.
 """
 import numpy as np
 import pytest
@@ -99,15 +98,15 @@ def test_layer_step_graph_replay(activation, fused, noalloc):
 
 @pytest.mark.parametrize("activation,fused,noalloc", CASES)
 def test_layer_step_second_stream_matches_one_stream(activation, fused, noalloc):
-    """The step with its second stream (slot-row prefetches beside the dispatch layout, the
-    router-weight gradient and the folds beside the DGRAD GEMMs, joined by events) gives every
-    output bit for bit as the step in one stream, over several steps in a row."""
+    """The step with its backward's second stream (the router-weight gradient and the folds
+    beside the DGRAD GEMMs, joined by events; on by default only for large steps, forced on
+    here) gives every output bit for bit as the step in one stream, over several steps in a
+    row."""
     from balanced_token_dispatch_amd.layer import LayerStep, Shape
     d = synth.Dims(R=8, S=512, K=4, E=32, B=4, H=256, Hp=192)
     idx, w = synth.routing(d, 1.0, 22)
     L = LayerStep(Shape(d.R, d.S, d.K, d.E, d.B, d.H, d.Hp), rank=2, activation=activation,
-                  fused_gather=fused, plan_noalloc=noalloc)
-    assert L.overlap
+                  fused_gather=fused, plan_noalloc=noalloc, overlap=True)
     for t, sd in ((L.x_all, 221), (L.y_all, 224), (L.dout_all, 225), (L.dxp_all, 226)):
         synth.fill_normal_(t, 1.0, sd)
     synth.fill_normal_(L.w_up, 0.05, 222)
