@@ -42,10 +42,17 @@ __global__ __launch_bounds__(kLayThreads) void k_lay_hist(const int32_t *__restr
   __syncthreads();
   const int lo = c * kLayChunk, hi = min(SK, lo + kLayChunk);
   const int32_t *ids = topk + (size_t)p * SK;
-  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
-    const int e = ids[i];
-    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  // all of a thread's ids are loaded before the first is counted, so the loads overlap
+  constexpr int kPer = kLayChunk / kLayThreads;
+  int ev[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = lo + u * kLayThreads + threadIdx.x;
+    ev[u] = i < hi ? ids[i] : -1;
   }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (ev[u] >= 0 && ev[u] < E) atomicAdd(&hist[ev[u]], 1);
   __syncthreads();
   const int col = p * nchunk + c;
   for (int e = threadIdx.x; e < E; e += blockDim.x) part[(size_t)e * npc + col] = hist[e];
@@ -103,6 +110,7 @@ __global__ __launch_bounds__(kLayThreads) void k_lay_scan(
   for (int e = tid; e < E; e += kLayThreads) {
     const int r0 = (e / E_loc) * E_loc;
     int s = 0;
+#pragma unroll 8
     for (int f = r0; f < e; ++f) s += plan[L.off_keep + f];
     hs[e] = s;
   }

@@ -44,8 +44,19 @@ __global__ __launch_bounds__(kHistThreads) void k_plan_hist(const int32_t *__res
   const int lo = c * kPlanChunk;
   const int hi = min(SK, lo + kPlanChunk);
   const int32_t *ids = topk + (size_t)p * SK;
-  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
-    const int e = ids[i];
+  // all of a thread's ids are loaded before the first is counted (kPlanChunk / kHistThreads
+  // per thread), so the loads overlap instead of each waiting for the one before
+  constexpr int kPer = kPlanChunk / kHistThreads;
+  int ev[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = lo + u * blockDim.x + threadIdx.x;
+    ev[u] = i < hi ? ids[i] : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    if (lo + u * (int)blockDim.x + (int)threadIdx.x >= hi) continue;
+    const int e = ev[u];
     const int key = (e >= 0 && e < E) ? e : E;
     atomicAdd(&hist[key], 1);
   }
@@ -62,6 +73,7 @@ __global__ __launch_bounds__(kHistThreads) void k_plan_reduce(const int32_t *__r
   const int p = blockIdx.x;
   for (int e = threadIdx.x; e <= E; e += blockDim.x) {
     int s = 0;
+#pragma unroll 8
     for (int c = 0; c < nchunk; ++c) s += partial[(size_t)(p * nchunk + c) * (E + 1) + e];
     if (e < E)
       counts[(size_t)p * E + e] = s;
@@ -397,6 +409,7 @@ __global__ __launch_bounds__(kSolveThreads) void k_plan_solve(const int32_t *__r
   // T_e and the bad-id flag
   for (int e = tid; e < E; e += nt) {
     int s = 0;
+#pragma unroll 8
     for (int p = 0; p < R; ++p) s += counts[(size_t)p * E + e];
     sT[e] = s;
     sRepFirst[e] = 0;
