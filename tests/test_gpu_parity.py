@@ -501,6 +501,7 @@ GEMM_SHAPES = [
     (9, 257, 1408, 2048),
     (1, 300, 96, 96),         # one segment, one partial tile
     (1088, 3000, 64, 128),    # the largest G: ~3 rows per segment, many empty
+    (2, 500, 32, 320),        # a one-step contraction
 ]
 
 
