@@ -254,7 +254,7 @@ def render_stats(stats_csv, title, command):
     import csv
     rows = [r for r in csv.DictReader(open(stats_csv)) if "moe::" in r["Name"]]
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    out = [f"# rocprofv3 kernel stats: {title}", "", "Command (GPU box, `$REPO` = repository root):",
+    out = [f"# rocprofv3 kernel stats: {title}", "", "Command (on the MI355X host, `$REPO` = repository root):",
            "", "```", command, "```", "",
            "Kernels of the library (torch's input generation and copies are omitted):", "",
            "| kernel | calls | avg us | min us | max us | % of profiled GPU time |",
@@ -282,7 +282,7 @@ def render_counters(csv_path, title, command):
     for d in sorted(vals, key=int):
         if "moe::" in names[d]:
             per[names[d]].append(d)
-    out = [f"# rocprofv3 counters per launch: {title}", "", "Command (GPU box, `$REPO` = repository root):",
+    out = [f"# rocprofv3 counters per launch: {title}", "", "Command (on the MI355X host, `$REPO` = repository root):",
            "", "```", command, "```", "",
            "`--probe` runs one warm-up step, a 1 GiB copy, then one step; the values average each kernel's "
            "launches in that second step.", "",
@@ -711,7 +711,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures the one-GPU share of one rank; --gpus {args.gpus} "
-              f"(WORLD_SIZE {world}) is not supported: this build has no multi-GPU path.",
+              f"(WORLD_SIZE {world}) is not supported: the benchmark has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
 
